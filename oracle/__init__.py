@@ -1,0 +1,22 @@
+"""CPU oracle for the Block KV decode path: test infrastructure only.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package. It shares no code with the HIP library.
+"""
+
+from .kvslot_oracle import (  # noqa: F401
+    NULL_BLOCK_ID,
+    P_MAX,
+    PAD_SLOT_ID,
+    OracleError,
+    compute_slot_mapping,
+    kv_cache_tensor_bytes,
+    map_to_kernel_blocks,
+    paged_decode_attention,
+    remap_null_block_to_sentinel,
+    reshape_and_cache,
+    select_ctx_bucket,
+    smallest_bucket_at_least,
+    validate_buckets,
+    widen,
+)
