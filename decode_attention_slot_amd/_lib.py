@@ -1,0 +1,230 @@
+"""ctypes binding of libkvslot.so: argument marshalling only.
+
+Every function has the name of the C entry point it wraps (include/kvslot.h)
+and runs no arithmetic of its own: tensors become device pointers, the
+current torch stream becomes the hipStream_t, and a non-zero status becomes
+KvslotError. PyTorch provides device memory and streams, nothing else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvslot.so")
+
+KVS_OK = 0
+KVS_F32, KVS_BF16 = 0, 1
+KVS_WALK_TABLE = 0x1
+STATUS = {
+    0: "KVS_OK", -1: "KVS_EINVAL", -2: "KVS_EUNSUPPORTED", -3: "KVS_EBUCKET",
+    -4: "KVS_ERANGE", -5: "KVS_ENOSPACE", -6: "KVS_EHIP",
+}
+
+# Every symbol include/kvslot.h declares.
+EXPORTS = (
+    "kvs_status_string",
+    "kv_slot_mapping",
+    "kv_cache_write",
+    "select_ctx_bucket",
+    "kv_map_to_kernel_blocks",
+    "paged_decode_attention_workspace_bytes",
+    "paged_decode_attention",
+)
+
+
+class KvslotError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{where}: {self.name} ({_lib().kvs_status_string(status).decode()})")
+
+
+_LIB = None
+
+
+def _lib():
+    """Load libkvslot.so once; fail loudly if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m decode_attention_slot_amd.build` "
+                "(there is no fallback path)"
+            )
+        lib = ctypes.CDLL(LIB_PATH)
+        i32, i64, u32, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.kvs_status_string.argtypes = [ctypes.c_int]
+        lib.kvs_status_string.restype = ctypes.c_char_p
+        lib.kv_slot_mapping.argtypes = [vp, vp, i64, i64, vp, i32, i32, i32, vp, vp]
+        lib.kv_cache_write.argtypes = [vp, vp, vp, i64, vp, vp, i64, i32, i32, i32, ctypes.c_int, vp]
+        lib.select_ctx_bucket.argtypes = [i64, i32, vp, i32, i32, i32, vp, vp]
+        lib.kv_map_to_kernel_blocks.argtypes = [vp, i32, i32, i32, i32, vp, i32]
+        lib.paged_decode_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.paged_decode_attention_workspace_bytes.restype = sz
+        lib.paged_decode_attention.argtypes = [
+            vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32, i64, f32,
+            ctypes.c_int, u32, vp, sz, vp, vp,
+        ]
+        for name in ("kv_slot_mapping", "kv_cache_write", "select_ctx_bucket",
+                     "kv_map_to_kernel_blocks", "paged_decode_attention"):
+            getattr(lib, name).restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def load():
+    """Load the library and return the ctypes handle."""
+    return _lib()
+
+
+def _check(status: int, where: str):
+    if status != KVS_OK:
+        raise KvslotError(status, where)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream)
+
+
+def _kvs_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KVS_F32
+    if t.dtype == torch.bfloat16:
+        return KVS_BF16
+    raise TypeError(f"unsupported cache dtype {t.dtype}")
+
+
+def kv_slot_mapping(req_indices: torch.Tensor, positions: torch.Tensor, block_table: torch.Tensor,
+                    block_size: int, slot_mapping: Optional[torch.Tensor] = None,
+                    max_num_tokens: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Slots of the tokens (int64 [max_num_tokens]); see kv_slot_mapping in kvslot.h."""
+    T = int(req_indices.numel())
+    if slot_mapping is None:
+        n = T if max_num_tokens is None else int(max_num_tokens)
+        slot_mapping = torch.empty(n, dtype=torch.int64, device=block_table.device)
+    rows, stride = block_table.shape
+    st = _lib().kv_slot_mapping(
+        _dev(req_indices, "req_indices", torch.int32, 1), _dev(positions, "positions", torch.int64, 1),
+        T, int(slot_mapping.numel()), _dev(block_table, "block_table", torch.int32, 2),
+        int(rows), int(stride), int(block_size), _dev(slot_mapping, "slot_mapping", torch.int64, 1),
+        _stream(block_table, stream))
+    _check(st, "kv_slot_mapping")
+    return slot_mapping
+
+
+def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Scatter k_new / v_new [T, Hkv, D] into the caches in place; see kvslot.h."""
+    nb, bs, hkv, d = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_new.shape[1:] != (hkv, d) \
+            or v_new.shape != k_new.shape or k_new.dtype != k_cache.dtype \
+            or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise ValueError("kv_cache_write: shape or dtype mismatch")
+    T = int(k_new.shape[0])
+    if slot_mapping.numel() < T:
+        raise ValueError("kv_cache_write: slot_mapping shorter than k_new")
+    st = _lib().kv_cache_write(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping", torch.int64),
+        T, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), int(nb), int(bs), int(hkv), int(d),
+        _kvs_dtype(k_cache), _stream(k_cache, stream))
+    _check(st, "kv_cache_write")
+
+
+def select_ctx_bucket(max_num_computed_tokens: int, num_speculative_tokens: int,
+                      buckets: Optional[Sequence[int]], max_model_len: int, block_size: int):
+    """(bucket_len, walk_blocks) for this step; host only. See kvslot.h."""
+    out_b, out_w = ctypes.c_int32(), ctypes.c_int32()
+    if buckets is None:
+        ptr, n, keep = None, 0, None
+    else:
+        keep = (ctypes.c_int32 * max(len(buckets), 1))(*[int(b) for b in buckets])
+        ptr, n = ctypes.cast(keep, ctypes.c_void_p), len(buckets)
+    st = _lib().select_ctx_bucket(int(max_num_computed_tokens), int(num_speculative_tokens), ptr, n,
+                                  int(max_model_len), int(block_size), ctypes.byref(out_b),
+                                  ctypes.byref(out_w))
+    _check(st, "select_ctx_bucket")
+    return out_b.value, out_w.value
+
+
+def kv_map_to_kernel_blocks(block_table: np.ndarray, manager_block_size: int,
+                            kernel_block_size: int) -> np.ndarray:
+    """Expand a host block table from manager to kernel blocks; see kvslot.h."""
+    src = np.ascontiguousarray(block_table, dtype=np.int32)
+    rows, width = src.shape
+    k = max(int(manager_block_size) // max(int(kernel_block_size), 1), 1)
+    dst = np.empty((rows, width * k), dtype=np.int32)
+    st = _lib().kv_map_to_kernel_blocks(src.ctypes.data, int(rows), int(width),
+                                        int(manager_block_size), int(kernel_block_size),
+                                        dst.ctypes.data, int(width * k))
+    _check(st, "kv_map_to_kernel_blocks")
+    return dst
+
+
+def paged_decode_attention_workspace_bytes(num_seqs: int, q_len: int, num_q_heads: int,
+                                           num_kv_heads: int, head_dim: int) -> int:
+    return int(_lib().paged_decode_attention_workspace_bytes(
+        int(num_seqs), int(q_len), int(num_q_heads), int(num_kv_heads), int(head_dim)))
+
+
+def make_workspace(num_seqs: int, q_len: int, num_q_heads: int, num_kv_heads: int,
+                   head_dim: int, device) -> torch.Tensor:
+    """A zero-filled workspace of the required size (zero before first use)."""
+    n = paged_decode_attention_workspace_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim)
+    if n == 0:
+        raise ValueError("invalid sizes for the decode workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                           walk_blocks: Optional[int] = None, flags: int = 0,
+                           workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention; q [B, S_q, Hq, D] in the cache dtype -> fp32 out.
+
+    walk_blocks defaults to the table width. See paged_decode_attention in
+    kvslot.h for the semantics and the workspace contract.
+    """
+    B, Sq, Hq, D = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != D or q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype \
+            or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("paged_decode_attention: shape or dtype mismatch")
+    if block_table.shape[0] < B or seq_lens.numel() < B:
+        raise ValueError("paged_decode_attention: block_table / seq_lens have too few rows")
+    stride = int(block_table.shape[1])
+    walk = stride if walk_blocks is None else int(walk_blocks)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(B, Sq, Hq, hkv, D, q.device)
+    st = _lib().paged_decode_attention(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table", torch.int32, 2), stride, walk,
+        _dev(seq_lens, "seq_lens", torch.int32), int(B), int(Sq), int(Hq), int(hkv), int(D),
+        int(bs), int(nb), float(scale), _kvs_dtype(k_cache), int(flags),
+        _dev(workspace, "workspace", torch.uint8), int(workspace.numel()),
+        _dev(out, "out", torch.float32), _stream(q, stream))
+    _check(st, "paged_decode_attention")
+    return out

@@ -1,0 +1,207 @@
+// C ABI of the Block KV decode path: argument checks, the host-only entry
+// points, and launches of the HIP kernels on the caller's stream.
+// The contract of every function is documented in include/kvslot.h.
+#include <limits.h>
+#include <math.h>
+
+#include "kvslot.h"
+#include "kvslot_internal.h"
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP; }
+
+int elem_bytes(kvs_dtype d) {
+  switch (d) {
+    case KVS_F32: return 4;
+    case KVS_BF16: return 2;
+  }
+  return 0;
+}
+
+constexpr int kMaxRows = 16;        // (Hq / Hkv) * q_len: one MFMA column tile
+constexpr int kMaxSeqs = 8192;
+
+}  // namespace
+
+extern "C" {
+
+const char* kvs_status_string(int status) {
+  switch (status) {
+    case KVS_OK: return "ok";
+    case KVS_EINVAL: return "invalid argument";
+    case KVS_EUNSUPPORTED: return "unsupported dtype, head_dim, block_size or shape";
+    case KVS_EBUCKET: return "decode context-length bucket list fails validation";
+    case KVS_ERANGE: return "needed_seq exceeds max_model_len";
+    case KVS_ENOSPACE: return "workspace too small";
+    case KVS_EHIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int kv_slot_mapping(const int32_t* req_indices, const int64_t* positions, int64_t num_tokens,
+                    int64_t max_num_tokens, const int32_t* block_table, int32_t table_rows,
+                    int32_t table_stride, int32_t block_size, int64_t* slot_mapping,
+                    void* stream) {
+  if (num_tokens < 0 || max_num_tokens < num_tokens || table_rows < 0 || table_stride < 1 ||
+      block_size < 1)
+    return KVS_EINVAL;
+  if (max_num_tokens > 0 && !slot_mapping) return KVS_EINVAL;
+  if (num_tokens > 0 && (!req_indices || !positions)) return KVS_EINVAL;
+  if (table_rows > 0 && !block_table) return KVS_EINVAL;
+  return launch_status(kvs::launch_slot_mapping(req_indices, positions, num_tokens,
+                                                max_num_tokens, block_table, table_rows,
+                                                table_stride, block_size, slot_mapping,
+                                                (hipStream_t)stream));
+}
+
+int kv_cache_write(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                   int64_t num_tokens, void* k_cache, void* v_cache, int64_t total_blocks,
+                   int32_t block_size, int32_t num_kv_heads, int32_t head_dim, kvs_dtype dtype,
+                   void* stream) {
+  if (num_tokens < 0 || total_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1)
+    return KVS_EINVAL;
+  const int es = elem_bytes(dtype);
+  if (!es) return KVS_EUNSUPPORTED;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * es;
+  if (row_bytes % 16 != 0 || row_bytes > INT_MAX) return KVS_EUNSUPPORTED;
+  if (total_blocks > INT64_MAX / block_size) return KVS_EINVAL;
+  if (num_tokens == 0) return KVS_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return KVS_EINVAL;
+  return launch_status(kvs::launch_cache_write(k_new, v_new, slot_mapping, num_tokens, k_cache,
+                                               v_cache, total_blocks * block_size,
+                                               (int32_t)row_bytes, (hipStream_t)stream));
+}
+
+int select_ctx_bucket(int64_t max_num_computed_tokens, int32_t num_speculative_tokens,
+                      const int32_t* buckets, int32_t num_buckets, int32_t max_model_len,
+                      int32_t block_size, int32_t* bucket_len_out, int32_t* walk_blocks_out) {
+  if (!bucket_len_out || !walk_blocks_out || num_buckets < 0 || max_num_computed_tokens < 0 ||
+      num_speculative_tokens < 0 || max_model_len < 1 || block_size < 1)
+    return KVS_EINVAL;
+  const auto blocks_for = [&](int64_t len) { return (int32_t)((len + block_size - 1) / block_size); };
+  if (!buckets) {  // feature off: the full table every step
+    *bucket_len_out = max_model_len;
+    *walk_blocks_out = blocks_for(max_model_len);
+    return KVS_OK;
+  }
+  // "Validation": non-empty, positive, strictly ascending, below
+  // max_model_len, divisible by P_MAX = 128.
+  if (num_buckets == 0) return KVS_EBUCKET;
+  for (int32_t i = 0; i < num_buckets; ++i) {
+    const int32_t b = buckets[i];
+    if (b <= 0 || b >= max_model_len || b % 128 != 0) return KVS_EBUCKET;
+    if (i > 0 && b <= buckets[i - 1]) return KVS_EBUCKET;
+  }
+  // "Per-step bucket selection": needed_seq = max(num_computed_tokens) + 1 +
+  // num_speculative_tokens; the smallest bucket >= needed_seq, falling back
+  // to max_model_len.
+  const int64_t needed_seq = max_num_computed_tokens + 1 + (int64_t)num_speculative_tokens;
+  if (needed_seq > max_model_len) return KVS_ERANGE;
+  int32_t bucket = max_model_len;
+  for (int32_t i = 0; i < num_buckets; ++i) {
+    if (buckets[i] >= needed_seq) {
+      bucket = buckets[i];  // ascending: the first that fits is the smallest
+      break;
+    }
+  }
+  *bucket_len_out = bucket;
+  *walk_blocks_out = blocks_for(bucket);  // head trim: the first ceil(bucket / bs) blocks
+  return KVS_OK;
+}
+
+int kv_map_to_kernel_blocks(const int32_t* src, int32_t rows, int32_t src_stride,
+                            int32_t manager_block_size, int32_t kernel_block_size, int32_t* dst,
+                            int32_t dst_stride) {
+  if (rows < 0 || src_stride < 1 || manager_block_size < 1 || kernel_block_size < 1)
+    return KVS_EINVAL;
+  if (manager_block_size % kernel_block_size != 0) return KVS_EINVAL;
+  const int32_t k = manager_block_size / kernel_block_size;
+  if ((int64_t)src_stride * k > dst_stride) return KVS_EINVAL;
+  if (rows == 0) return KVS_OK;
+  if (!src || !dst) return KVS_EINVAL;
+  for (int64_t r = 0; r < rows; ++r) {
+    const int32_t* s = src + r * src_stride;
+    int32_t* d = dst + r * dst_stride;
+    for (int32_t c = 0; c < src_stride; ++c) {
+      const int32_t m = s[c];
+      for (int32_t i = 0; i < k; ++i) {
+        if (m > 0) {
+          const int64_t id = (int64_t)m * k + i;
+          if (id > INT32_MAX) return KVS_EINVAL;
+          d[(int64_t)c * k + i] = (int32_t)id;
+        } else {
+          d[(int64_t)c * k + i] = m;
+        }
+      }
+    }
+  }
+  return KVS_OK;
+}
+
+size_t paged_decode_attention_workspace_bytes(int32_t num_seqs, int32_t q_len,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim) {
+  if (num_seqs < 0 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)
+    return 0;
+  return kvs::kCounterBytes +
+         kvs::decode_partial_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim);
+}
+
+int paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, int32_t table_stride, int32_t walk_blocks,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t q_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t total_blocks, float scale,
+                           kvs_dtype dtype, uint32_t flags, void* workspace,
+                           size_t workspace_bytes, float* out, void* stream) {
+  if (num_seqs < 0 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      block_size < 1 || table_stride < 1 || walk_blocks < 0 || walk_blocks > table_stride ||
+      total_blocks < 1 || !isfinite(scale))
+    return KVS_EINVAL;
+  if (num_q_heads % num_kv_heads != 0) return KVS_EINVAL;
+  if (flags & ~KVS_WALK_TABLE) return KVS_EINVAL;
+  if (!elem_bytes(dtype)) return KVS_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return KVS_EUNSUPPORTED;
+  if (!is_pow2(block_size) || block_size < 16 || block_size > 256) return KVS_EUNSUPPORTED;
+  if ((int64_t)(num_q_heads / num_kv_heads) * q_len > kMaxRows) return KVS_EUNSUPPORTED;
+  if (num_seqs > kMaxSeqs) return KVS_EUNSUPPORTED;
+  if ((int64_t)num_seqs * num_kv_heads > (int64_t)(kvs::kCounterBytes / sizeof(uint32_t)))
+    return KVS_EUNSUPPORTED;
+  if ((int64_t)table_stride * block_size > INT_MAX / 2) return KVS_EUNSUPPORTED;
+  if (num_seqs == 0) return KVS_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
+    return KVS_EINVAL;
+  const size_t need =
+      paged_decode_attention_workspace_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim);
+  if (workspace_bytes < need) return KVS_ENOSPACE;
+
+  kvs::DecodeParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.counters = (uint32_t*)workspace;
+  p.partials = (float*)((char*)workspace + kvs::kCounterBytes);
+  p.total_blocks = total_blocks;
+  p.table_stride = table_stride;
+  p.walk_blocks = walk_blocks;
+  p.num_seqs = num_seqs;
+  p.q_len = q_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.target_pairs = kvs::decode_target_pairs(num_kv_heads);
+  p.min_chunk_blocks = kvs::decode_min_chunk_blocks(block_size);
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  p.flags = flags;
+  p.is_bf16 = dtype == KVS_BF16;
+  return launch_status(kvs::launch_paged_decode(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Paged KV-cache write: scatter the step's new K/V rows to their slots.
+//
+// "Padding and Batching with Block KV", section "Slot ID -1: Padding
+// Tokens": the new K (V) of token t goes to K_cache[slot_ids[t]] and the
+// copy is skipped when the slot is out of bounds, so the pad slot -1 writes
+// nothing. A slot names one [num_kv_heads][head_dim] row of the
+// [total_blocks][block_size][num_kv_heads][head_dim] cache (section "Block
+// Structure"), so the write is a byte copy of whole rows.
+//
+// Each thread moves one 16-byte piece of a K row and the matching piece of
+// the V row; consecutive threads cover consecutive pieces, so every wave
+// reads and writes whole contiguous rows.
+#include "kvslot_internal.h"
+
+namespace kvs {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256)
+cache_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
+                   const int64_t* __restrict__ slot_mapping, int64_t num_tokens,
+                   u32x4* __restrict__ k_cache, u32x4* __restrict__ v_cache, int64_t total_slots,
+                   uint32_t pieces_per_row) {
+  const int64_t n = num_tokens * (int64_t)pieces_per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t t = i / pieces_per_row;
+    const int64_t piece = i - t * pieces_per_row;
+    const int64_t s = slot_mapping[t];
+    if (s < 0 || s >= total_slots) continue;  // pad slot or out of bounds: skip
+    const int64_t dst = s * pieces_per_row + piece;
+    const u32x4 kv = __builtin_nontemporal_load(&k_new[i]);
+    const u32x4 vv = __builtin_nontemporal_load(&v_new[i]);
+    k_cache[dst] = kv;
+    v_cache[dst] = vv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                              int64_t num_tokens, void* k_cache, void* v_cache,
+                              int64_t total_slots, int32_t row_bytes, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const uint32_t pieces = (uint32_t)(row_bytes / 16);
+  int64_t blocks = (num_tokens * pieces + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  cache_write_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      (const u32x4*)k_new, (const u32x4*)v_new, slot_mapping, num_tokens, (u32x4*)k_cache,
+      (u32x4*)v_cache, total_slots, pieces);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

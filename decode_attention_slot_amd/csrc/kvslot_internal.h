@@ -1,0 +1,55 @@
+// Internal launch interface between the C-ABI layer (abi.cpp) and the HIP
+// kernels. Not installed; the public interface is include/kvslot.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvs {
+
+hipError_t launch_slot_mapping(const int32_t* req_indices, const int64_t* positions,
+                               int64_t num_tokens, int64_t max_num_tokens,
+                               const int32_t* block_table, int32_t table_rows,
+                               int32_t table_stride, int32_t block_size, int64_t* slot_mapping,
+                               hipStream_t stream);
+
+hipError_t launch_cache_write(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                              int64_t num_tokens, void* k_cache, void* v_cache,
+                              int64_t total_slots, int32_t row_bytes, hipStream_t stream);
+
+// Everything the decode kernel needs; filled and checked by abi.cpp.
+struct DecodeParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* out;
+  float* partials;     // [pairs][num_kv_heads][rows][head_dim + 4]
+  uint32_t* counters;  // [num_seqs * num_kv_heads], zero between calls
+  int64_t total_blocks;
+  int32_t table_stride;
+  int32_t walk_blocks;
+  int32_t num_seqs;
+  int32_t q_len;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t target_pairs;      // split-K: aim for about this many (request, chunk) pairs
+  int32_t min_chunk_blocks;  // never split finer than this
+  float scale_log2;          // softmax scale times log2(e)
+  uint32_t flags;
+  int is_bf16;
+};
+
+// Workspace layout shared by the size query and the launch.
+constexpr size_t kCounterBytes = 65536 * sizeof(uint32_t);
+int32_t decode_target_pairs(int32_t num_kv_heads);
+int32_t decode_min_chunk_blocks(int32_t block_size);
+size_t decode_partial_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim);
+
+hipError_t launch_paged_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace kvs

@@ -1,0 +1,497 @@
+// GQA paged decode attention for gfx950.
+//
+// What is computed ("Padding and Batching with Block KV", sections "Block
+// Table", "Cache Masking" and "Multi-Token Decode"; "Decode Context-Length
+// Bucketing", sections "Problem" and "Block-table head-trim vs. SWA
+// tail-trim"): query token j of request r sits at position L - q_len + j,
+// where L counts this step's tokens, and attends to every earlier-or-equal
+// position p below walk_blocks * block_size whose block-table entry is
+// active; q head h reads KV head h / (Hq / Hkv). The result is the softmax of
+// scale * <q, k> over those keys applied to the values, in fp32.
+//
+// How, on CDNA4:
+// * Work unit: one wavefront per (request, chunk of context blocks, KV head).
+//   A workgroup holds the waves of up to NW KV heads of one (request,
+//   chunk), so the whole [block][token][head][dim] rows a workgroup reads
+//   are contiguous in HBM.
+// * Chunks are sized on the device from seq_lens (no host synchronisation):
+//   about target_pairs (request, chunk) pairs over the batch, at least
+//   min_chunk_blocks blocks each, whole blocks, aligned to logical block 0.
+//   The split depends only on the context lengths, so a head-trimmed walk,
+//   a full-table walk and the context walk produce the same partials.
+// * The block ids of a chunk are held one per lane in a VGPR and broadcast
+//   with readlane, so no LDS or barrier is needed.
+// * Tile of 16 tokens. S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (fp32 KV:
+//   v_mfma_f32_16x16x4f32): K is the A operand (lane l holds token l % 16,
+//   16 bytes of its head row per piece), Q^T the B operand (lane l holds
+//   query row l % 16; rows are (query token, head in group), at most 16).
+//   The result gives each lane four tokens of one query row.
+// * Online softmax per query row, in exp2 units, entirely inside the lane
+//   except one max over the four lane groups.
+// * O^T = V^T P^T on v_mfma_f32_16x16x4f32: lane l holds the fp32 value of
+//   dimension column l % 16 for token 4 * (l / 16) + i, which is exactly a
+//   16-byte slice of that token's head row, so V is read in its natural
+//   layout (each 16-lane group reads one whole 256-byte head row). The
+//   accumulator lands with query row = l % 16, matching the softmax state.
+// * Split-K partials (acc, m, l per row) go to the workspace; the last wave
+//   of a (request, KV head) to arrive, found with a device-scope counter,
+//   merges them in ascending chunk order and resets the counter.
+// * Masked keys are removed by select, never by multiplying by zero, and the
+//   values of keys past the context are zeroed, so unwritten (NaN canary)
+//   cache rows cannot leak into the output.
+#include <math.h>
+
+#include "kvslot_internal.h"
+
+namespace kvs {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kFlagWalkTable = 0x1u;
+// Never set by the host. Testing it keeps the table-walk loads alive.
+constexpr uint32_t kFlagSink = 0x80000000u;
+constexpr int kTile = 16;
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float max_over_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float sum_over_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Context positions of a request that a walk of walk_tok positions can see.
+__device__ __forceinline__ int visible_len(int L, int walk_tok) {
+  return L <= 0 ? 0 : (L < walk_tok ? L : walk_tok);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <bool BF16, int D, int NW>
+__global__ void __launch_bounds__(NW * 64)
+paged_decode_kernel(const DecodeParams p, int bs_shift) {
+  constexpr int ES = BF16 ? 2 : 4;       // bytes per element
+  constexpr int EP = 16 / ES;            // elements per 16-byte piece
+  constexpr int NP = D / (4 * EP);       // 16-byte K pieces per lane per token
+  constexpr int NT = D / 16;             // P.V n-tiles (dimension columns of 16)
+  constexpr int NVW = NT * ES / 4;       // V dwords per lane per token
+  constexpr int PSTRIDE = D + 4;         // floats per partial row (acc, m, l, pad)
+  static_assert(NP >= 1 && NVW >= 2, "unsupported head_dim");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rho = lane & 15;  // query row owned by this lane (MFMA column)
+  const int jg = lane >> 4;   // lane group: tokens 4*jg .. 4*jg+3 of a tile
+
+  const int B = p.num_seqs;
+  const int bs = 1 << bs_shift;
+  const int walk_tok = p.walk_blocks << bs_shift;
+  const bool table_walk = (p.flags & kFlagWalkTable) != 0;
+  const int Hkv = p.num_kv_heads;
+  const int Hq = p.num_q_heads;
+  const int G = Hq / Hkv;
+  const int Sq = p.q_len;
+  const int nrows = G * Sq;
+  const int HG = (Hkv + NW - 1) / NW;
+  const int64_t block_bytes = ((int64_t)Hkv * D * ES) << bs_shift;
+  const uint32_t row_bytes = (uint32_t)(Hkv * D * ES);
+
+  // ---- chunk size, from the context blocks of the whole batch ------------
+  int64_t ctx_blocks_total = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int r = base + lane;
+    int nb = 0;
+    if (r < B) nb = (visible_len(p.seq_lens[r], walk_tok) + bs - 1) >> bs_shift;
+    ctx_blocks_total += wave_sum(nb);
+  }
+  int64_t cb64 = (ctx_blocks_total + p.target_pairs - 1) / p.target_pairs;
+  if (cb64 < p.min_chunk_blocks) cb64 = p.min_chunk_blocks;
+  const int cb = uniform((int)cb64);  // blocks per chunk
+  const int chunk_tok = cb << bs_shift;
+  const int walk_chunks = (p.walk_blocks + cb - 1) / cb;
+
+  // ---- requests with no visible context produce zeros --------------------
+  {
+    const int row_floats = Sq * Hq * D;
+    for (int r = blockIdx.x; r < B; r += gridDim.x) {
+      if (visible_len(p.seq_lens[r], walk_tok) == 0) {
+        float* o = p.out + (int64_t)r * row_floats;
+        for (int i = threadIdx.x; i < row_floats; i += NW * 64) o[i] = 0.0f;
+      }
+    }
+  }
+
+  uint32_t sink = 0;
+
+  for (int64_t uw = blockIdx.x;; uw += gridDim.x) {
+    const int64_t pair = uw / HG;
+    const int hg = (int)(uw - pair * HG);
+
+    // ---- locate (request, chunk) of this pair ----------------------------
+    int r = -1, c = 0;
+    int64_t pidx0 = 0;  // index of (r, chunk 0) among the pairs that hold context
+    if (!table_walk) {
+      int64_t carry = 0;
+      for (int base = 0; base < B; base += 64) {
+        const int rr = base + lane;
+        int C = 0;
+        if (rr < B) {
+          const int nb = (visible_len(p.seq_lens[rr], walk_tok) + bs - 1) >> bs_shift;
+          C = (nb + cb - 1) / cb;
+        }
+        const int incl = wave_inclusive_scan(C, lane);
+        const int tot = __shfl(incl, 63);
+        if (pair < carry + tot) {
+          const uint64_t hit = __ballot(carry + incl > pair);
+          const int src = __builtin_ctzll(hit);
+          const int excl = __shfl(incl - C, src);
+          r = base + src;
+          pidx0 = carry + excl;
+          c = (int)(pair - pidx0);
+          break;
+        }
+        carry += tot;
+      }
+    } else if (walk_chunks > 0) {
+      const int64_t rq = pair / walk_chunks;
+      if (rq < B) {
+        r = (int)rq;
+        c = (int)(pair - rq * walk_chunks);
+        int64_t carry = 0;
+        for (int base = 0; base < r; base += 64) {
+          const int rr = base + lane;
+          int C = 0;
+          if (rr < r) {
+            const int nb = (visible_len(p.seq_lens[rr], walk_tok) + bs - 1) >> bs_shift;
+            C = (nb + cb - 1) / cb;
+          }
+          carry += wave_sum(C);
+        }
+        pidx0 = carry;
+      }
+    }
+    r = uniform(r);
+    if (r < 0) break;  // every pair is done
+
+    const int g = hg * NW + wave;
+    if (g >= Hkv) continue;
+
+    const int L = uniform(p.seq_lens[r]);
+    const int E = visible_len(L, walk_tok);
+    const int nb_r = (E + bs - 1) >> bs_shift;
+    const int Cv = (nb_r + cb - 1) / cb;  // chunks of r that hold context
+    const bool pair_valid = c < Cv;
+    const int tok0 = c * chunk_tok;
+    const int tok_valid_end = min(tok0 + chunk_tok, E);
+    const int tok_walk_end = table_walk ? min(tok0 + chunk_tok, walk_tok) : tok_valid_end;
+
+    // ---- query operand (B operand of the score MFMA) ---------------------
+    const int jrow = rho / G;
+    const int hh = rho - jrow * G;
+    const int qpos = rho < nrows ? L - Sq + jrow : -1;
+    const int qpos_min = L - Sq;
+    u32x4 qp[NP];
+    {
+      const char* qrow = (const char*)p.q +
+                         ((((int64_t)r * Sq + jrow) * Hq + (int64_t)g * G + hh) * D) * ES;
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        qp[pp] = (u32x4){0u, 0u, 0u, 0u};
+        if (pair_valid && rho < nrows)
+          qp[pp] = *(const u32x4*)(qrow + pp * 64 + jg * 16);
+      }
+    }
+
+    // ---- running softmax state of query row rho --------------------------
+    float m_run = -INFINITY;
+    float l_run = 0.0f;  // partial: this lane's tokens only
+    f32x4 acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int32_t* trow = p.block_table + (int64_t)r * p.table_stride;
+    const int blk0 = tok0 >> bs_shift;
+    int stage_lo = -1;  // first chunk-relative block held in `staged`
+    int staged = 0;
+
+    const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
+    const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
+
+    for (int tt = tok0; tt < tok_walk_end; tt += kTile) {
+      const int rel = (tt >> bs_shift) - blk0;
+      if (stage_lo < 0 || rel >= stage_lo + 64) {
+        stage_lo = rel & ~63;
+        const int col = blk0 + stage_lo + lane;
+        staged = col < p.table_stride ? trow[col] : 0;
+      }
+      const int bid = __builtin_amdgcn_readlane(staged, rel - stage_lo);
+      const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
+      if (!table_walk && !active) continue;  // the context walk never reads it
+      const bool compute = pair_valid && active && tt < tok_valid_end;
+
+      const char* kb = (const char*)p.k_cache + (int64_t)(active ? bid : 0) * block_bytes;
+      const char* vb = (const char*)p.v_cache + (int64_t)(active ? bid : 0) * block_bytes;
+      const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
+
+      u32x4 kp[NP];
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) kp[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
+      uint32_t vw[4][NVW];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* src = vb + in_blk + v_lane_off + i * row_bytes;
+        if constexpr (NVW == 2) {
+          const u32x2 x = *(const u32x2*)src;
+          vw[i][0] = x[0]; vw[i][1] = x[1];
+        } else {
+#pragma unroll
+          for (int w = 0; w < NVW; w += 4) {
+            const u32x4 x = *(const u32x4*)(src + w * 4);
+            vw[i][w] = x[0]; vw[i][w + 1] = x[1]; vw[i][w + 2] = x[2]; vw[i][w + 3] = x[3];
+          }
+        }
+      }
+
+      if (!compute) {
+        // Fixed-shape walk past the context: read, never used.
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) sink ^= kp[pp][0] ^ kp[pp][1] ^ kp[pp][2] ^ kp[pp][3];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int w = 0; w < NVW; ++w) sink ^= vw[i][w];
+        continue;
+      }
+
+      // ---- scores: S^T[token 4*jg+i][row rho] ----------------------------
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        if constexpr (BF16) {
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kp[pp]),
+                                                      __builtin_bit_cast(bf16x8, qp[pp]), s, 0,
+                                                      0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kp[pp][e]),
+                                                     __uint_as_float(qp[pp][e]), s, 0, 0, 0);
+        }
+      }
+
+      float sx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sx[i] = s[i] * p.scale_log2;
+      const bool full = (tt + kTile <= tok_valid_end) && (tt + kTile - 1 <= qpos_min);
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = tt + 4 * jg + i;
+          const bool kv_ok = pos < E;
+          if (!(kv_ok && pos <= qpos)) sx[i] = -INFINITY;
+          if (!kv_ok) {
+#pragma unroll
+            for (int w = 0; w < NVW; ++w) vw[i][w] = 0u;
+          }
+        }
+      }
+
+      // ---- online softmax ------------------------------------------------
+      float mx = fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3]));
+      mx = max_over_groups(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sx[i] - m_use);
+      l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      }
+      m_run = m_new;
+
+      // ---- O^T += V^T P^T --------------------------------------------------
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          float v;
+          if constexpr (BF16) {
+            v = (n & 1) ? bf16_hi(vw[i][n >> 1]) : bf16_lo(vw[i][n >> 1]);
+          } else {
+            v = __uint_as_float(vw[i][n]);
+          }
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pr[i], acc[n], 0, 0, 0);
+        }
+      }
+    }
+
+    if (!pair_valid) continue;
+
+    // acc[n][i] holds dimension (4*jg + i) * NT + n of query row rho.
+    const float l_tot = sum_over_groups(l_run);
+    const int d_base = 4 * jg * NT;
+
+    if (Cv == 1) {
+      if (rho < nrows) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        float* o = p.out + (((int64_t)r * Sq + jrow) * Hq + (int64_t)g * G + hh) * D + d_base;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int n0 = 0; n0 < NT; n0 += 4) {
+            f32x4 v = {acc[n0][i] * inv, acc[n0 + 1][i] * inv, acc[n0 + 2][i] * inv,
+                       acc[n0 + 3][i] * inv};
+            *(f32x4*)(o + i * NT + n0) = v;
+          }
+        }
+      }
+      continue;
+    }
+
+    // ---- split-K: publish this chunk's partial ----------------------------
+    const int64_t pidx = pidx0 + c;
+    {
+      float* prow = p.partials + ((pidx * Hkv + g) * nrows + rho) * PSTRIDE;
+      if (rho < nrows) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int n0 = 0; n0 < NT; n0 += 4) {
+            f32x4 v = {acc[n0][i], acc[n0 + 1][i], acc[n0 + 2][i], acc[n0 + 3][i]};
+            *(f32x4*)(prow + d_base + i * NT + n0) = v;
+          }
+        }
+        if (jg == 0) {
+          prow[D] = m_run;
+          prow[D + 1] = l_tot;
+        }
+      }
+    }
+    __threadfence();
+    uint32_t* counter = p.counters + (int64_t)r * Hkv + g;
+    uint32_t prev = 0;
+    if (lane == 0) prev = atomicAdd(counter, 1u);
+    prev = __shfl(prev, 0);
+    if (prev != (uint32_t)(Cv - 1)) continue;
+
+    // ---- last chunk to finish: merge all partials in chunk order -----------
+    __threadfence();
+    if (rho < nrows) {
+      const float* pbase = p.partials + ((pidx0 * Hkv + g) * nrows + rho) * PSTRIDE;
+      const int64_t cstride = (int64_t)Hkv * nrows * PSTRIDE;
+      float M = -INFINITY;
+      for (int cc = 0; cc < Cv; ++cc) M = fmaxf(M, pbase[cc * cstride + D]);
+      float lsum = 0.0f;
+      f32x4 o4[D / 16];
+#pragma unroll
+      for (int k = 0; k < D / 16; ++k) o4[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
+        for (int cc = 0; cc < Cv; ++cc) {
+          const float* pr = pbase + cc * cstride;
+          const float mc = pr[D];
+          if (mc == -INFINITY) continue;
+          const float w = __builtin_amdgcn_exp2f(mc - M);
+          lsum += w * pr[D + 1];
+#pragma unroll
+          for (int k = 0; k < D / 16; ++k) o4[k] += w * *(const f32x4*)(pr + d_base + 4 * k);
+        }
+      }
+      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+      float* o = p.out + (((int64_t)r * Sq + jrow) * Hq + (int64_t)g * G + hh) * D + d_base;
+#pragma unroll
+      for (int k = 0; k < D / 16; ++k) *(f32x4*)(o + 4 * k) = o4[k] * inv;
+    }
+    if (lane == 0) atomicExch(counter, 0u);
+  }
+
+  if (p.flags & kFlagSink) p.out[0] = __uint_as_float(sink);
+}
+
+template <bool BF16, int D, int NW>
+hipError_t launch_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) {
+  const int HG = (p.num_kv_heads + NW - 1) / NW;
+  int64_t pairs;
+  if (p.flags & kFlagWalkTable) {
+    const int64_t cpr = (p.walk_blocks + p.min_chunk_blocks - 1) / p.min_chunk_blocks;
+    pairs = (int64_t)p.num_seqs * (cpr > 0 ? cpr : 1);
+  } else {
+    pairs = (int64_t)p.target_pairs + p.num_seqs;
+  }
+  int64_t grid = pairs * HG;
+  if (grid < 1) grid = 1;
+  if (grid > (1 << 20)) grid = 1 << 20;
+  paged_decode_kernel<BF16, D, NW><<<dim3((unsigned)grid), dim3(NW * 64), 0, stream>>>(p,
+                                                                                      bs_shift);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t launch_heads(const DecodeParams& p, int bs_shift, hipStream_t stream) {
+  const int h = p.num_kv_heads;
+  if (h % 8 == 0) return launch_typed<BF16, D, 8>(p, bs_shift, stream);
+  if (h % 4 == 0) return launch_typed<BF16, D, 4>(p, bs_shift, stream);
+  if (h % 2 == 0) return launch_typed<BF16, D, 2>(p, bs_shift, stream);
+  return launch_typed<BF16, D, 1>(p, bs_shift, stream);
+}
+
+}  // namespace
+
+int32_t decode_target_pairs(int32_t num_kv_heads) {
+  // About 2048 waves in flight over the 1024 SIMDs of a 256-CU part.
+  const int32_t t = 2048 / (num_kv_heads > 0 ? num_kv_heads : 1);
+  return t > 16 ? t : 16;
+}
+
+int32_t decode_min_chunk_blocks(int32_t block_size) {
+  // At least 128 tokens per chunk keeps the partial traffic a few percent
+  // of the KV bytes the chunk reads.
+  const int32_t b = 128 / block_size;
+  return b > 1 ? b : 1;
+}
+
+size_t decode_partial_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim) {
+  const size_t pairs = (size_t)decode_target_pairs(num_kv_heads) + (size_t)num_seqs;
+  return pairs * (size_t)num_q_heads * (size_t)q_len * (size_t)(head_dim + 4) * sizeof(float);
+}
+
+hipError_t launch_paged_decode(const DecodeParams& p, hipStream_t stream) {
+  const int bs_shift = __builtin_ctz((unsigned)p.block_size);
+  if (p.is_bf16) {
+    if (p.head_dim == 128) return launch_heads<true, 128>(p, bs_shift, stream);
+    return launch_heads<true, 64>(p, bs_shift, stream);
+  }
+  if (p.head_dim == 128) return launch_heads<false, 128>(p, bs_shift, stream);
+  return launch_heads<false, 64>(p, bs_shift, stream);
+}
+
+}  // namespace kvs

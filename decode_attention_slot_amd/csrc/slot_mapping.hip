@@ -1,0 +1,64 @@
+// Slot mapping: the physical cache slot of every token of a step.
+//
+// "Padding and Batching with Block KV", sections "The Core Formula" and
+// "Slot Mapping Computation": the slot of a token at position p of request r
+// is block_table[r][p / block_size] * block_size + p % block_size. Padding
+// tokens (request index -1) and inactive table entries (null block 0, the -1
+// sentinel) give the pad slot -1 (sections "Slot ID -1" and "Block ID 0 vs.
+// Sentinel -1"), and the tail of a fixed-size slot buffer is padded with -1
+// (the vLLM block-table notes, data-flow listing).
+//
+// One thread per output entry. The vLLM kernel runs one program per request;
+// a flat grid over tokens keeps every lane busy whatever the length mix.
+#include "kvslot_internal.h"
+
+namespace kvs {
+namespace {
+
+__global__ void __launch_bounds__(256)
+slot_mapping_kernel(const int32_t* __restrict__ req_indices, const int64_t* __restrict__ positions,
+                    int64_t num_tokens, int64_t max_num_tokens,
+                    const int32_t* __restrict__ block_table, int32_t table_rows,
+                    int32_t table_stride, int32_t block_size, int32_t block_shift,
+                    int64_t* __restrict__ slot_mapping) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < max_num_tokens; t += stride) {
+    int64_t slot = -1;
+    if (t < num_tokens) {
+      const int32_t r = req_indices[t];
+      const int64_t p = positions[t];
+      if (r >= 0 && r < table_rows && p >= 0) {
+        // block_shift >= 0 when block_size is a power of two
+        const int64_t logical_block = block_shift >= 0 ? (p >> block_shift) : p / block_size;
+        if (logical_block < table_stride) {
+          const int32_t block = block_table[(int64_t)r * table_stride + logical_block];
+          if (block > 0) {
+            const int64_t offset = p - logical_block * block_size;
+            slot = (int64_t)block * block_size + offset;
+          }
+        }
+      }
+    }
+    slot_mapping[t] = slot;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(const int32_t* req_indices, const int64_t* positions,
+                               int64_t num_tokens, int64_t max_num_tokens,
+                               const int32_t* block_table, int32_t table_rows,
+                               int32_t table_stride, int32_t block_size, int64_t* slot_mapping,
+                               hipStream_t stream) {
+  if (max_num_tokens == 0) return hipSuccess;
+  const int shift =
+      (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
+  int64_t blocks = (max_num_tokens + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  slot_mapping_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      req_indices, positions, num_tokens, max_num_tokens, block_table, table_rows, table_stride,
+      block_size, shift, slot_mapping);
+  return hipGetLastError();
+}
+
+}  // namespace kvs

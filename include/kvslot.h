@@ -1,0 +1,221 @@
+/*
+ * kvslot.h - C ABI of the Block KV decode hot path for AMD Instinct MI355X
+ * (gfx950): slot mapping, the paged KV-cache write, GQA paged decode
+ * attention and per-step context-length bucket selection.
+ *
+ * Pages cited (by title):
+ *   [BKV] "Padding and Batching with Block KV" (AWS Neuron vllm-neuron docs)
+ *   [BT]  "Block table: logical token -> physical KV block" (vLLM v0.25.1 notes)
+ *   [CLB] "Decode Context-Length Bucketing" (AWS Neuron vllm-neuron docs)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Cache layout ([BKV] "Block Structure"): each of k_cache and v_cache is a
+ *   dense row-major array [total_blocks][block_size][num_kv_heads][head_dim]
+ *   of the cache element type. A slot s = block * block_size + offset names
+ *   one [num_kv_heads][head_dim] row.
+ * - Block table ([BKV] "Block Table"): int32 [rows][table_stride], row =
+ *   request, column j = physical block of logical block j. An entry <= 0 is
+ *   inactive: 0 is the null block, -1 the sentinel ([BKV] "Block ID 0 vs.
+ *   Sentinel -1"); both behave identically in every entry point.
+ * - Pointers of the GPU entry points are device pointers; each of those
+ *   entry points only enqueues kernels on `stream` (a hipStream_t; NULL is
+ *   the null stream) and returns. No entry point synchronises, reads device
+ *   memory on the host, or allocates or frees memory. The caller owns every
+ *   buffer.
+ * - Only scalar arguments and pointers are checked. A bad value inside a
+ *   device array (a block id, a slot, a length) is a caller error: the
+ *   kernels clamp their reads to the given sizes and skip what is out of
+ *   range, so such a value never faults, but the result is unspecified.
+ * - Return values: KVS_OK (0) or a negative KVS_E* status; nothing is
+ *   enqueued when the status is not KVS_OK, except for KVS_EHIP, which
+ *   reports a failed launch.
+ */
+#ifndef KVSLOT_H
+#define KVSLOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVS_OK 0
+#define KVS_EINVAL (-1)       /* null pointer, negative size, bad scalar      */
+#define KVS_EUNSUPPORTED (-2) /* dtype, head_dim, block_size or shape          */
+#define KVS_EBUCKET (-3)      /* bucket list fails the [CLB] validation rules  */
+#define KVS_ERANGE (-4)       /* needed_seq beyond max_model_len               */
+#define KVS_ENOSPACE (-5)     /* workspace smaller than required               */
+#define KVS_EHIP (-6)         /* a kernel launch failed (hipGetLastError)      */
+
+/* Element type of caches, new K/V rows and q. */
+typedef enum { KVS_F32 = 0, KVS_BF16 = 1 } kvs_dtype;
+
+/* paged_decode_attention flag: walk every one of the first walk_blocks table
+ * columns of every row, as a fixed-shape kernel does; inactive entries read
+ * null block 0. The output is identical to the default context walk, which
+ * reads only the blocks that cover each request's context. This mode exists
+ * to measure the traffic of a fixed-shape step ([CLB] "Problem"). */
+#define KVS_WALK_TABLE 0x1u
+
+/* Short English text for a status code (static storage). */
+const char* kvs_status_string(int status);
+
+/*
+ * kv_slot_mapping - slot of every token ([BKV] "The Core Formula" and "Slot
+ * Mapping Computation"; tail padding as in the [BT] data-flow listing).
+ *
+ * For t < num_tokens, with r = req_indices[t] and p = positions[t]:
+ *   slot_mapping[t] = block_table[r * table_stride + p / block_size]
+ *                     * block_size + p % block_size
+ * and slot_mapping[t] = -1 instead when r < 0 (a padding token, [BKV] "Slot
+ * Mapping for Padded Tokens"), r >= table_rows, p < 0, p / block_size >=
+ * table_stride, or the table entry is <= 0 (null block or sentinel). For
+ * num_tokens <= t < max_num_tokens, slot_mapping[t] = -1.
+ *
+ *   req_indices   int32 [num_tokens], device
+ *   positions     int64 [num_tokens], device
+ *   block_table   int32 [table_rows][table_stride], device
+ *   slot_mapping  int64 [max_num_tokens], device, written
+ * Errors: KVS_EINVAL for null pointers (when the matching size is > 0),
+ * num_tokens < 0, max_num_tokens < num_tokens, table_rows < 0,
+ * table_stride < 1 or block_size < 1.
+ */
+int kv_slot_mapping(const int32_t* req_indices, const int64_t* positions, int64_t num_tokens,
+                    int64_t max_num_tokens, const int32_t* block_table, int32_t table_rows,
+                    int32_t table_stride, int32_t block_size, int64_t* slot_mapping,
+                    void* stream);
+
+/*
+ * kv_cache_write - scatter new K/V rows into the paged caches ([BKV] "Slot
+ * ID -1: Padding Tokens": the write to K_cache[slot_ids] skips
+ * out-of-bounds slots).
+ *
+ * For every t < num_tokens with 0 <= s = slot_mapping[t] < total_blocks *
+ * block_size, copies row t of k_new (num_kv_heads * head_dim elements) to
+ * slot s of k_cache, and the same for v_new / v_cache. Other tokens write
+ * nothing. The copy is of raw elements, so the cache receives the exact
+ * bytes of k_new / v_new.
+ *
+ *   k_new, v_new      [num_tokens][num_kv_heads][head_dim] of dtype, device
+ *   slot_mapping      int64 [num_tokens], device
+ *   k_cache, v_cache  cache layout above, device, updated in place
+ * Two tokens with one slot is a caller error (which row lands is
+ * unspecified). k_new / v_new must not overlap the caches.
+ * Errors: KVS_EINVAL (null pointers, negative sizes, num_kv_heads < 1,
+ * block_size < 1, total_blocks < 1); KVS_EUNSUPPORTED when a row is not a
+ * multiple of 16 bytes or dtype is unknown.
+ */
+int kv_cache_write(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                   int64_t num_tokens, void* k_cache, void* v_cache, int64_t total_blocks,
+                   int32_t block_size, int32_t num_kv_heads, int32_t head_dim, kvs_dtype dtype,
+                   void* stream);
+
+/*
+ * select_ctx_bucket - per-step decode context bucket ([CLB] "Per-step
+ * bucket selection", "Validation", "Block-table head-trim vs. SWA
+ * tail-trim", "Backwards compatibility"). Host only; pointers are host
+ * pointers; no GPU work.
+ *
+ * buckets == NULL means the feature is off: returns max_model_len and
+ * ceil(max_model_len / block_size). Otherwise the list must be non-empty,
+ * positive, strictly ascending, each value below max_model_len and
+ * divisible by 128 (else KVS_EBUCKET); needed_seq = max_num_computed_tokens
+ * + 1 + num_speculative_tokens must not exceed max_model_len (else
+ * KVS_ERANGE); the result is the smallest bucket >= needed_seq among the
+ * list and max_model_len, and walk_blocks = ceil(bucket / block_size), the
+ * table columns a head-trimmed step keeps.
+ * Errors: KVS_EINVAL for null outputs, num_buckets < 0, negative
+ * max_num_computed_tokens or num_speculative_tokens, max_model_len < 1 or
+ * block_size < 1.
+ */
+int select_ctx_bucket(int64_t max_num_computed_tokens, int32_t num_speculative_tokens,
+                      const int32_t* buckets, int32_t num_buckets, int32_t max_model_len,
+                      int32_t block_size, int32_t* bucket_len_out, int32_t* walk_blocks_out);
+
+/*
+ * kv_map_to_kernel_blocks - expand a block table from manager blocks to
+ * kernel blocks ([BT] design motivation: one manager block becomes
+ * manager_block_size / kernel_block_size kernel blocks; a kernel size that
+ * does not divide the manager size is rejected). Host only.
+ *
+ * With k = manager_block_size / kernel_block_size, entry m of column c
+ * becomes entries m * k + i at columns c * k + i (i < k) when m > 0; an
+ * inactive entry (<= 0) is copied to all k columns. This is the layout a
+ * [N][manager_bs][H][D] pool has when viewed as [N * k][kernel_bs][H][D].
+ *
+ *   src  int32 [rows][src_stride], host
+ *   dst  int32 [rows][dst_stride], host, dst_stride >= src_stride * k
+ * Errors: KVS_EINVAL (null pointers, rows < 0, bad strides or sizes,
+ * kernel_block_size not dividing manager_block_size, or an expanded id that
+ * does not fit int32).
+ */
+int kv_map_to_kernel_blocks(const int32_t* src, int32_t rows, int32_t src_stride,
+                            int32_t manager_block_size, int32_t kernel_block_size, int32_t* dst,
+                            int32_t dst_stride);
+
+/*
+ * paged_decode_attention_workspace_bytes - bytes of device workspace a
+ * paged_decode_attention call with these sizes needs. Depends on these
+ * arguments only (not on context lengths or walk_blocks), so one workspace
+ * serves every bucket. Returns 0 for invalid sizes.
+ */
+size_t paged_decode_attention_workspace_bytes(int32_t num_seqs, int32_t q_len,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim);
+
+/*
+ * paged_decode_attention - GQA decode attention over the paged cache
+ * ([BKV] "Cache Masking", "Block ID 0 vs. Sentinel -1", "Multi-Token
+ * Decode"; [CLB] "Problem" and "Block-table head-trim vs. SWA tail-trim").
+ *
+ * Request r has context length L = seq_lens[r], which counts the q_len
+ * tokens of this step (already written to the cache). Query token j of
+ * request r sits at position L - q_len + j; q head h reads KV head
+ * h / (num_q_heads / num_kv_heads). It attends to every position p with
+ * p <= its own position and p < walk_blocks * block_size whose table entry
+ * block_table[r * table_stride + p / block_size] is active (> 0 and <
+ * total_blocks): key K = k_cache[block][p % block_size][kv_head], value
+ * likewise, score = scale * <q, K>, output = softmax-weighted sum of the
+ * values, accumulated in fp32. A request with L <= 0 (a padded row) and a
+ * query that sees no key produce zeros.
+ *
+ *   q            [num_seqs][q_len][num_q_heads][head_dim] of dtype, device
+ *   k_cache, v_cache   cache layout above, dtype, device
+ *   block_table  int32 [num_seqs][table_stride], device; walk_blocks <=
+ *                table_stride columns of it are read (the head trim)
+ *   seq_lens     int32 [num_seqs], device
+ *   out          float [num_seqs][q_len][num_q_heads][head_dim], device
+ *   workspace    device memory of at least
+ *                paged_decode_attention_workspace_bytes(...) bytes. It must
+ *                be zero-filled before its first use; every call leaves it
+ *                ready for the next call on the same stream. Calls that run
+ *                concurrently must not share a workspace.
+ *   flags        0 (context walk: only blocks covering each request's
+ *                context are read) or KVS_WALK_TABLE.
+ * By default only the blocks covering min(L, walk_blocks * block_size)
+ * positions are read. Results do not depend on walk_blocks beyond that
+ * trim, on the flags, on the physical block ids, or on whether unused
+ * entries hold 0 or -1: they are bitwise identical across those.
+ * Supported: head_dim 64 or 128; block_size 16, 32, 64, 128 or 256;
+ * (num_q_heads / num_kv_heads) * q_len <= 16; num_seqs <= 8192;
+ * num_seqs * num_kv_heads <= 65536.
+ * Errors: KVS_EINVAL (null pointers, non-positive sizes, num_q_heads not a
+ * multiple of num_kv_heads, walk_blocks outside [0, table_stride]),
+ * KVS_EUNSUPPORTED (outside the supported set), KVS_ENOSPACE (workspace
+ * too small), KVS_EHIP.
+ */
+int paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, int32_t table_stride, int32_t walk_blocks,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t q_len,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t total_blocks, float scale,
+                           kvs_dtype dtype, uint32_t flags, void* workspace,
+                           size_t workspace_bytes, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSLOT_H */

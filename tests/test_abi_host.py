@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU.
+
+The library loads and exports every function include/kvslot.h declares; the
+host-only entry points (bucket selection, manager-to-kernel expansion) match
+the oracle exactly; the GPU entry points reject bad scalars before any
+device work (null pointers, so nothing could run even if the checks failed
+open would crash rather than compute, and the calls return first).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvslot.h")
+
+
+@pytest.fixture(scope="module")
+def K():
+    import decode_attention_slot_amd as K
+
+    if not os.path.exists(K.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    K.load()
+    return K
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(K):
+    names = declared_functions()
+    assert len(names) >= 7
+    assert set(names) == set(K.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(K.load(), n)
+
+
+def test_status_strings(K):
+    lib = K.load()
+    for code in K.STATUS:
+        assert lib.kvs_status_string(code).decode() != "unknown status"
+
+
+def test_select_ctx_bucket_matches_oracle(K):
+    configs = [([4096, 8192, 16384], 131072, 64), ([16384], 131072, 64), ([128, 512, 640], 1024, 16),
+               (None, 131072, 64), (None, 1000, 64), ([128], 1000, 64)]
+    rng = np.random.default_rng(0)
+    for buckets, mml, bs in configs:
+        ctxs = list(range(0, min(mml, 1100))) + list(rng.integers(0, mml + 10, size=300))
+        for m in ctxs:
+            for spec in (0, 1, 3):
+                try:
+                    want = O.select_ctx_bucket(int(m), spec, buckets, mml, bs)
+                except O.OracleError as e:
+                    with pytest.raises(K.KvslotError) as ke:
+                        K.select_ctx_bucket(int(m), spec, buckets, mml, bs)
+                    assert ke.value.name == {"range": "KVS_ERANGE", "bucket": "KVS_EBUCKET"}[e.code]
+                    continue
+                assert K.select_ctx_bucket(int(m), spec, buckets, mml, bs) == want
+
+
+def test_select_ctx_bucket_validation_matches_oracle(K):
+    import json
+
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "clb_bucket_examples.json")))
+    for bl in g["validation"]["invalid"]:
+        with pytest.raises(K.KvslotError) as e:
+            K.select_ctx_bucket(10, 0, bl, 131072, 64)
+        assert e.value.name == "KVS_EBUCKET"
+    for bl in g["validation"]["valid"]:
+        K.select_ctx_bucket(10, 0, bl, 131072, 64)
+    with pytest.raises(K.KvslotError) as e:
+        K.select_ctx_bucket(-1, 0, [4096], 131072, 64)
+    assert e.value.name == "KVS_EINVAL"
+
+
+def test_map_to_kernel_blocks_matches_oracle(K):
+    rng = np.random.default_rng(3)
+    for mgr_bs, kern_bs in ((32, 16), (64, 16), (16, 16), (256, 64)):
+        t = rng.integers(-1, 5000, size=(9, 13)).astype(np.int32)
+        assert np.array_equal(K.kv_map_to_kernel_blocks(t, mgr_bs, kern_bs),
+                              O.map_to_kernel_blocks(t, mgr_bs, kern_bs))
+    with pytest.raises(K.KvslotError):
+        K.kv_map_to_kernel_blocks(np.ones((2, 2), np.int32), 32, 24)
+    with pytest.raises(K.KvslotError):  # expanded id beyond int32
+        K.kv_map_to_kernel_blocks(np.array([[2**30]], np.int32), 64, 16)
+
+
+def test_gpu_entry_points_reject_bad_scalars(K):
+    lib = K.load()
+    null = None
+    # kv_slot_mapping: negative sizes, max < num, bad stride / block size
+    assert lib.kv_slot_mapping(null, null, -1, 0, null, 0, 1, 16, null, null) == -1
+    assert lib.kv_slot_mapping(null, null, 5, 4, null, 0, 1, 16, null, null) == -1
+    assert lib.kv_slot_mapping(null, null, 0, 0, null, 0, 0, 16, null, null) == -1
+    assert lib.kv_slot_mapping(null, null, 0, 0, null, 0, 1, 0, null, null) == -1
+    assert lib.kv_slot_mapping(null, null, 3, 3, null, 0, 1, 16, null, null) == -1  # null ptrs
+    # kv_cache_write: bad dtype, row not a multiple of 16 bytes, null pointers
+    assert lib.kv_cache_write(null, null, null, 1, null, null, 4, 16, 1, 64, 7, null) == -2
+    assert lib.kv_cache_write(null, null, null, 1, null, null, 4, 16, 1, 2, 1, null) == -2
+    assert lib.kv_cache_write(null, null, null, 1, null, null, 4, 16, 1, 64, 1, null) == -1
+    assert lib.kv_cache_write(null, null, null, 0, null, null, 4, 16, 1, 64, 1, null) == 0
+
+    def pda(**kw):
+        a = dict(q=null, k=null, v=null, bt=null, stride=4, walk=4, sl=null, B=1, sq=1, hq=8, hkv=2,
+                 d=128, bs=64, nb=10, scale=0.1, dtype=1, flags=0, ws=null, wsb=1 << 30, out=null)
+        a.update(kw)
+        return lib.paged_decode_attention(a["q"], a["k"], a["v"], a["bt"], a["stride"], a["walk"],
+                                          a["sl"], a["B"], a["sq"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                          a["nb"], a["scale"], a["dtype"], a["flags"], a["ws"], a["wsb"],
+                                          a["out"], null)
+
+    assert pda() == -1                      # null pointers
+    assert pda(B=0) == 0                    # nothing to do
+    assert pda(hq=7) == -1                  # Hq not a multiple of Hkv
+    assert pda(walk=5) == -1                # walk beyond the table
+    assert pda(flags=2) == -1               # unknown flag
+    assert pda(d=96) == -2                  # head_dim
+    assert pda(bs=48) == -2                 # block size
+    assert pda(bs=8) == -2
+    assert pda(sq=5) == -2                  # 4 * 5 = 20 rows > 16
+    assert pda(dtype=5) == -2
+    assert pda(B=9000) == -2
+    assert pda(scale=float("nan")) == -1
+    assert lib.paged_decode_attention_workspace_bytes(1, 0, 8, 2, 128) == 0
+    assert lib.paged_decode_attention_workspace_bytes(12, 1, 32, 8, 128) > 0
+
+
+def test_no_fallback_when_library_missing(K, tmp_path, monkeypatch):
+    from decode_attention_slot_amd import _lib
+
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.select_ctx_bucket(1, 0, None, 128, 16)

@@ -1,0 +1,383 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Slot mappings and cache byte images must be bit-exact; attention must be
+within max-abs-error 1e-5 (fp32 KV) or 2e-2 (bf16 KV, fp32 accumulate) of the
+fp64 oracle. Invariants the pages state (null vs sentinel entries, bucketed
+vs full walks, physical block relabelling) must hold bitwise on the GPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_slot_amd as K
+import oracle as O
+import workloads as W
+from oracle.runner import OracleStep
+from workloads import device as dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """Device cache/tensor -> host array of its raw bits (uint16 / uint32)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    """Host storage array -> raw bits (NaN canaries compare equal as bits)."""
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def max_err(gpu_out: torch.Tensor, ref: np.ndarray, rows=None) -> float:
+    g = gpu_out.double().cpu().numpy()
+    if rows is not None:
+        g, ref = g[rows], ref[rows]
+    assert np.isfinite(g).all()
+    return float(np.abs(g - ref).max()) if g.size else 0.0
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+# ---------------------------------------------------------------------------
+# the five configurations
+# ---------------------------------------------------------------------------
+def full_parity(w, cuda):
+    """Whole-image parity: prefill image, step slots, step image, attention."""
+    s = dev.build(w, cuda)
+    ref = OracleStep(w, s.host_table)
+    assert np.array_equal(host_bits(s.k_cache), bits(ref.k_cache))
+    assert np.array_equal(host_bits(s.v_cache), bits(ref.v_cache))
+    slots, out = dev.run_step(s)
+    torch.cuda.synchronize()
+    want_slots = ref.write_step()
+    assert np.array_equal(slots.cpu().numpy(), want_slots)
+    assert np.array_equal(host_bits(s.k_cache), bits(ref.k_cache))
+    assert np.array_equal(host_bits(s.v_cache), bits(ref.v_cache))
+    want = ref.attention(w.q())
+    err = max_err(out, want)
+    assert err <= TOL[w.dtype], err
+    return s, ref, out
+
+
+def test_tiny_fp32(cuda):
+    w = W.make_workload(0)
+    full_parity(w, cuda)
+
+
+def test_block_config_bf16(cuda):
+    w = W.make_workload(1)
+    full_parity(w, cuda)
+
+
+def test_block_config_bf16_other_seeds(cuda):
+    for seed in (7, 8):
+        full_parity(W.make_workload(1, seed=seed), cuda)
+
+
+@pytest.mark.parametrize("forced", [4095, 8191, 16383, 16384, None])
+def test_ctx_bucketing(cuda, forced):
+    w = W.make_workload(2, forced_max_ctx=forced) if forced else W.make_workload(2)
+    # bucket choice: library vs oracle
+    max_ctx = int(w.computed[: w.num_reqs].max())
+    b_lib = K.select_ctx_bucket(max_ctx, 0, w.buckets, w.max_model_len, w.block_size)
+    b_ref = O.select_ctx_bucket(max_ctx, 0, w.buckets, w.max_model_len, w.block_size)
+    assert b_lib == b_ref
+    walk = b_lib[1]
+    s = dev.build(w, cuda)
+    slots, ctx = dev.run_step(s)  # context walk over the full-width table
+    ws = K.make_workspace(w.num_rows, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim, cuda)
+    args = (s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens, w.scale)
+    bucketed = K.paged_decode_attention(*args, walk_blocks=walk, flags=K.KVS_WALK_TABLE,
+                                        workspace=ws)
+    full = K.paged_decode_attention(*args, flags=K.KVS_WALK_TABLE, workspace=ws)
+    trimmed_ctx = K.paged_decode_attention(*args, walk_blocks=walk, workspace=ws)
+    torch.cuda.synchronize()
+    for o in (bucketed, full, trimmed_ctx):
+        assert torch.equal(o.view(torch.int32), ctx.view(torch.int32))
+    # oracle on the longest request and two others
+    order = np.argsort(-w.seq_lens[: w.num_reqs])
+    rows = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])})
+    ref = OracleStep(w, s.host_table, requests=rows, full_image=False)
+    want_slots = ref.write_step()
+    assert np.array_equal(slots.cpu().numpy(), want_slots)
+    want = ref.attention(w.q(), walk_blocks=walk)
+    assert max_err(ctx, want, rows) <= TOL[w.dtype]
+
+
+def test_bucket_selection_seeds():
+    """Bucket picks for seeds 0-7 of the lognormal draw: library == oracle."""
+    for seed in range(8):
+        w = W.make_workload(2, seed=seed)
+        m = int(w.computed[: w.num_reqs].max())
+        for spec in (0, 3):
+            try:
+                want = O.select_ctx_bucket(m, spec, w.buckets, w.max_model_len, w.block_size)
+            except O.OracleError as e:
+                with pytest.raises(K.KvslotError) as ke:
+                    K.select_ctx_bucket(m, spec, w.buckets, w.max_model_len, w.block_size)
+                assert ke.value.name == {"range": "KVS_ERANGE", "bucket": "KVS_EBUCKET"}[e.code]
+                continue
+            assert K.select_ctx_bucket(m, spec, w.buckets, w.max_model_len, w.block_size) == want
+
+
+@pytest.fixture(scope="module")
+def large_batch(cuda):
+    w = W.make_workload(3)
+    return w, dev.build(w, cuda, threads=16)
+
+
+def test_large_batch_block_split(cuda, large_batch):
+    w, s = large_batch
+    want_table = O.map_to_kernel_blocks(w.mgr_block_table, w.mgr_block_size, w.block_size)
+    assert np.array_equal(s.host_table, want_table)
+    slots, out = dev.run_step(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    real = w.num_reqs
+    rows = sorted({0, real - 1, *map(int, rng.choice(real, 4, replace=False)),
+                   int(np.argmax(w.seq_lens[:real])), int(np.argmin(w.seq_lens[:real]))})
+    ref = OracleStep(w, s.host_table, requests=rows, full_image=False)
+    want_slots = ref.write_step()
+    got_slots = slots.cpu().numpy()
+    assert np.array_equal(got_slots, want_slots)  # every slot, including the 8 pads
+    assert (got_slots[real:] == -1).all()
+    # the decode rows landed at their slots; nothing else changed there
+    kc = s.k_cache.view(-1, w.num_kv_heads, w.head_dim)
+    live = torch.from_numpy(got_slots[got_slots >= 0]).to(cuda)
+    assert torch.equal(kc[live].view(torch.int16), s.dec_k[: len(live)].view(torch.int16))
+    # sampled never-written rows still hold the canary
+    canary_rows = torch.tensor([1 * w.block_size + 3, 2 * w.block_size - 1], device=cuda)
+    assert (kc[canary_rows].view(torch.int16) == W.CANARY_BITS["bf16"]).all()
+    assert max_err(out, ref.attention(w.q()), rows) <= TOL[w.dtype]
+    assert (out[real:] == 0).all()  # padded rows produce zeros
+
+
+def test_large_batch_manager_view_equals_kernel_view(cuda, large_batch):
+    """The same pool read at manager block size 32 gives the same output."""
+    w, s = large_batch
+    mgr_bt = torch.from_numpy(w.mgr_block_table).to(cuda)
+    nb = w.total_blocks // 2
+    kc = s.k_cache.view(nb, 32, w.num_kv_heads, w.head_dim)
+    vc = s.v_cache.view(nb, 32, w.num_kv_heads, w.head_dim)
+    a = K.paged_decode_attention(s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens, w.scale)
+    b = K.paged_decode_attention(s.q, kc, vc, mgr_bt, s.seq_lens, w.scale)
+    torch.cuda.synchronize()
+    err = (a - b).abs().max().item()
+    assert err <= 1e-5, err  # block size changes the tile walk, not the result
+
+
+def test_ragged_spec_decode(cuda):
+    w = W.make_workload(4)
+    s = dev.build(w, cuda, threads=16)
+    slots, out = dev.run_step(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = sorted({0, w.num_reqs - 1, *map(int, rng.choice(w.num_reqs, 4, replace=False))})
+    ref = OracleStep(w, s.host_table, requests=rows, full_image=False)
+    want_slots = ref.write_step()
+    assert np.array_equal(slots.cpu().numpy(), want_slots)  # all 8192 + 256 tokens
+    assert max_err(out, ref.attention(w.q()), rows) <= TOL[w.dtype]
+
+
+# ---------------------------------------------------------------------------
+# small generic cases: shapes, edge cases, invariants
+# ---------------------------------------------------------------------------
+def small_case(cuda, seed, lens, bs, hkv, g, sq, d, dtype, width=None, fill=-1):
+    """Random small batch: oracle caches built block-wise, GPU caches a copy."""
+    rng = np.random.default_rng(seed)
+    width = width or max(-(-L // bs) for L in lens) + 2
+    total = sum(-(-L // bs) for L in lens) + 3
+    table = np.full((len(lens), width), fill, np.int32)
+    perm = rng.permutation(np.arange(1, total))
+    off = 0
+    for r, L in enumerate(lens):
+        n = -(-L // bs)
+        table[r, :n] = perm[off:off + n]
+        off += n
+    wl = W.Workload(name="", index=0, seed=seed, dtype=dtype, block_size=bs, total_blocks=total,
+                    num_kv_heads=hkv, num_q_heads=hkv * g, head_dim=d, q_len=sq,
+                    num_reqs=len(lens), computed=np.array(lens) - sq, chunk_lens=np.zeros(len(lens)),
+                    seq_lens=np.array(lens, np.int32), block_table=table, max_model_len=width * bs)
+    wl.scale = 1 / math.sqrt(d)
+    kc, vc = wl.canary_cache(), wl.canary_cache()
+    for r, L in enumerate(lens):
+        for j in range(-(-L // bs)):
+            n = min(bs, L - j * bs)
+            kc[table[r, j], :n] = W.to_storage(rng.standard_normal((n, hkv, d)).astype(np.float32), dtype)
+            vc[table[r, j], :n] = W.to_storage(rng.standard_normal((n, hkv, d)).astype(np.float32), dtype)
+    q = W.to_storage(rng.standard_normal((len(lens), sq, hkv * g, d)).astype(np.float32), dtype)
+    return dict(w=wl, table=table, kc=kc, vc=vc, q=q,
+                d_kc=dev.upload_storage(kc, dtype, cuda), d_vc=dev.upload_storage(vc, dtype, cuda),
+                d_q=dev.upload_storage(q, dtype, cuda),
+                d_bt=torch.from_numpy(table).to(cuda),
+                d_sl=torch.from_numpy(np.array(lens, np.int32)).to(cuda))
+
+
+def gpu_attn(c, **kw):
+    return K.paged_decode_attention(c["d_q"], c["d_kc"], c["d_vc"], c["d_bt"], c["d_sl"],
+                                    c["w"].scale, **kw)
+
+
+def ref_attn(c, walk=None, table=None, lens=None):
+    w = c["w"]
+    t = c["table"] if table is None else table
+    return O.paged_decode_attention(c["q"], c["kc"], c["vc"], t,
+                                    w.seq_lens if lens is None else lens,
+                                    t.shape[1] if walk is None else walk, w.scale, w.dtype)
+
+
+SHAPES = [
+    # (dtype, d, bs, hkv, g, sq, lens)
+    ("f32", 64, 64, 2, 4, 1, [4, 101]),
+    ("f32", 128, 16, 1, 1, 1, [1, 17, 300]),
+    ("f32", 64, 32, 4, 2, 3, [3, 64, 65, 700]),
+    ("bf16", 128, 64, 8, 4, 1, [1, 63, 64, 65, 129, 2000]),
+    ("bf16", 128, 16, 8, 8, 1, [16, 17, 513, 1500]),
+    ("bf16", 128, 64, 8, 4, 4, [4, 5, 66, 67, 900]),
+    ("bf16", 64, 128, 2, 2, 2, [2, 128, 129, 1000]),
+    ("bf16", 64, 256, 1, 16, 1, [1, 255, 256, 257, 3000]),
+    ("bf16", 128, 32, 4, 1, 16, [16, 40, 2100]),
+    ("bf16", 128, 16, 2, 3, 5, [5, 6, 49, 5000]),  # G*Sq = 15, long split-K
+    ("f32", 128, 16, 8, 1, 1, [9000, 9000]),        # many chunks per request
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}-d{s[1]}-bs{s[2]}-h{s[3]}x{s[4]}-q{s[5]}")
+def test_shapes_vs_oracle(cuda, shape):
+    dtype, d, bs, hkv, g, sq, lens = shape
+    c = small_case(cuda, 42, lens, bs, hkv, g, sq, d, dtype)
+    out = gpu_attn(c)
+    torch.cuda.synchronize()
+    err = max_err(out, ref_attn(c))
+    assert err <= TOL[dtype], err
+
+
+def test_invariants_bitwise(cuda):
+    c = small_case(cuda, 3, [1, 50, 64, 700, 3000], 64, 8, 4, 2, 128, "bf16", width=64)
+    base = gpu_attn(c)
+    # null block 0 instead of sentinel -1 in unused entries
+    t0 = c["d_bt"].clone()
+    t0[t0 < 0] = 0
+    null = K.paged_decode_attention(c["d_q"], c["d_kc"], c["d_vc"], t0, c["d_sl"], c["w"].scale)
+    # head trim to the blocks the longest request needs, table walk and context walk
+    walk = -(-3000 // 64)
+    trim = gpu_attn(c, walk_blocks=walk)
+    trim_tw = gpu_attn(c, walk_blocks=walk, flags=K.KVS_WALK_TABLE)
+    full_tw = gpu_attn(c, flags=K.KVS_WALK_TABLE)
+    full_tw0 = K.paged_decode_attention(c["d_q"], c["d_kc"], c["d_vc"], t0, c["d_sl"],
+                                        c["w"].scale, flags=K.KVS_WALK_TABLE)
+    # relabel physical blocks
+    total = c["kc"].shape[0]
+    rng = np.random.default_rng(1)
+    relabel = np.concatenate([[0], rng.permutation(np.arange(1, total))])
+    inv = torch.from_numpy(np.argsort(relabel)).to(cuda)
+    kc2, vc2 = c["d_kc"][inv], c["d_vc"][inv]
+    t2 = torch.from_numpy(np.where(c["table"] > 0, relabel[np.maximum(c["table"], 0)],
+                                   c["table"]).astype(np.int32)).to(cuda)
+    rel = K.paged_decode_attention(c["d_q"], kc2, vc2, t2, c["d_sl"], c["w"].scale)
+    torch.cuda.synchronize()
+    for o in (null, trim, trim_tw, full_tw, full_tw0, rel):
+        assert torch.equal(o.view(torch.int32), base.view(torch.int32))
+    assert max_err(base, ref_attn(c)) <= TOL["bf16"]
+
+
+def test_edge_lengths_and_trim(cuda):
+    # L < q_len (no visible key for early queries), L = 0 rows, narrow trim
+    c = small_case(cuda, 5, [2, 9, 200], 16, 2, 2, 4, 64, "bf16", width=16)
+    lens = np.array([2, 0, 200], np.int32)
+    c["d_sl"] = torch.from_numpy(lens).to(cuda)
+    out = gpu_attn(c)
+    narrow = gpu_attn(c, walk_blocks=3)
+    none = gpu_attn(c, walk_blocks=0)
+    torch.cuda.synchronize()
+    assert max_err(out, ref_attn(c, lens=lens)) <= TOL["bf16"]
+    assert max_err(narrow, ref_attn(c, walk=3, lens=lens)) <= TOL["bf16"]
+    assert (none == 0).all()
+    assert (out[1] == 0).all() and (out[0, :2] == 0).all()
+
+
+def test_inactive_entry_inside_context(cuda):
+    c = small_case(cuda, 6, [300], 64, 2, 2, 1, 128, "bf16")
+    t = c["table"].copy()
+    t[0, 2] = -1
+    c["d_bt"] = torch.from_numpy(t).to(cuda)
+    out = gpu_attn(c)
+    tw = gpu_attn(c, flags=K.KVS_WALK_TABLE)
+    torch.cuda.synchronize()
+    assert max_err(out, ref_attn(c, table=t)) <= TOL["bf16"]
+    assert torch.equal(out.view(torch.int32), tw.view(torch.int32))
+
+
+def test_empty_inputs(cuda):
+    bt = torch.zeros((1, 4), dtype=torch.int32, device=cuda)
+    e32 = torch.zeros(0, dtype=torch.int32, device=cuda)
+    e64 = torch.zeros(0, dtype=torch.int64, device=cuda)
+    s = K.kv_slot_mapping(e32, e64, bt, 64, max_num_tokens=5)
+    kc = torch.zeros((2, 64, 1, 64), dtype=torch.bfloat16, device=cuda)
+    K.kv_cache_write(torch.zeros((0, 1, 64), dtype=torch.bfloat16, device=cuda),
+                     torch.zeros((0, 1, 64), dtype=torch.bfloat16, device=cuda), s, kc, kc.clone())
+    q = torch.zeros((0, 1, 1, 64), dtype=torch.bfloat16, device=cuda)
+    out = K.paged_decode_attention(q, kc, kc, bt, e32, 0.125)
+    torch.cuda.synchronize()
+    assert s.cpu().tolist() == [-1] * 5 and out.shape[0] == 0
+
+
+@pytest.mark.parametrize("bs", [1, 3, 16, 64, 100])
+def test_slot_mapping_edges_vs_oracle(cuda, bs):
+    rng = np.random.default_rng(bs)
+    rows, width, T = 6, 7, 3000
+    table = rng.permutation(np.arange(1, rows * width + 1)).reshape(rows, width).astype(np.int32)
+    kill = rng.random((rows, width))
+    table = np.where(kill < 0.2, -1, np.where(kill < 0.3, 0, table)).astype(np.int32)
+    req = rng.integers(-1, rows + 2, size=T).astype(np.int32)
+    pos = rng.integers(-3, (width + 2) * bs, size=T).astype(np.int64)
+    got = K.kv_slot_mapping(torch.from_numpy(req).to(cuda), torch.from_numpy(pos).to(cuda),
+                            torch.from_numpy(table).to(cuda), bs, max_num_tokens=T + 77)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), O.compute_slot_mapping(req, pos, table, bs, T + 77))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cache_write_image_vs_oracle(cuda, dtype):
+    rng = np.random.default_rng(9)
+    total, bs, hkv, d, T = 9, 16, 2, 64, 100
+    wl = W.Workload(name="", index=0, seed=0, dtype=dtype, block_size=bs, total_blocks=total,
+                    num_kv_heads=hkv, num_q_heads=hkv, head_dim=d, q_len=1, num_reqs=0,
+                    computed=None, chunk_lens=None, seq_lens=np.zeros(1), block_table=None)
+    slots = rng.permutation(np.arange(-20, total * bs + 20))[:T].astype(np.int64)
+    knew = W.to_storage(rng.standard_normal((T, hkv, d)).astype(np.float32), dtype)
+    vnew = W.to_storage(rng.standard_normal((T, hkv, d)).astype(np.float32), dtype)
+    kc, vc = wl.canary_cache(), wl.canary_cache()
+    O.reshape_and_cache(knew, vnew, slots, kc, vc)
+    dkc, dvc = dev.canary_cache(wl, cuda), dev.canary_cache(wl, cuda)
+    K.kv_cache_write(dev.upload_storage(knew, dtype, cuda), dev.upload_storage(vnew, dtype, cuda),
+                     torch.from_numpy(slots).to(cuda), dkc, dvc)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(dkc), bits(kc)) and np.array_equal(host_bits(dvc), bits(vc))
+
+
+def test_unsupported_shapes_raise(cuda):
+    c = small_case(cuda, 1, [10], 16, 1, 1, 1, 64, "bf16")
+    q96 = torch.zeros((1, 1, 1, 96), dtype=torch.bfloat16, device=cuda)
+    kc96 = torch.zeros((3, 16, 1, 96), dtype=torch.bfloat16, device=cuda)
+    with pytest.raises(K.KvslotError) as e:
+        K.paged_decode_attention(q96, kc96, kc96, c["d_bt"], c["d_sl"], 0.1)
+    assert e.value.name == "KVS_EUNSUPPORTED"
+    with pytest.raises(K.KvslotError) as e:
+        gpu_attn(c, walk_blocks=c["table"].shape[1] + 1)
+    assert e.value.name == "KVS_EINVAL"
+    small_ws = torch.zeros(16, dtype=torch.uint8, device=cuda)
+    with pytest.raises(K.KvslotError) as e:
+        gpu_attn(c, workspace=small_ws)
+    assert e.value.name == "KVS_ENOSPACE"
