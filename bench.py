@@ -1,0 +1,338 @@
+"""Benchmark of the Block KV decode step on one MI355X.
+
+One step = the whole hot path over one batch: the host bucket pick
+(select_ctx_bucket), then on the GPU kv_slot_mapping and kv_cache_write of
+the step's new tokens, then paged_decode_attention. Inputs are seeded and
+synthetic and already resident in HBM when the timed region starts (the
+prior context is prefilled through the library beforehand, untimed).
+
+The step rotates over several identical copies of the KV cache so that the
+bytes a step reads come from HBM, not from the last step's L2 / MALL lines.
+
+Prints one JSON line: whole-step throughput (algorithmic bytes of every
+kernel / wall time per step), decode and slot-mapping tokens/s, a roofline
+entry for the attention kernel (algorithmic bytes / its event-timed average
+duration against 8 TB/s) and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOADS = {
+    "block_config_bf16": 1,
+    "ctx_bucketing": 2,
+    "large_batch_block_split": 3,
+    "ragged_spec_decode": 4,
+    "tiny_fp32": 0,
+}
+DESCRIPTIONS = {
+    0: "tiny fp32: 2 requests (ctx 3, 100), bs 64, Hkv 2, Hq 8, D 64",
+    1: "block config bf16: 12 decode requests, ctx U[1,5000], 1024 blocks of 64, Hkv 8, Hq 32, D 128",
+    2: "context-length bucketing bf16: 8 requests, lognormal ctx (median 4096), max_model_len 131072, "
+       "buckets [4096, 8192, 16384], bs 64, Hkv 8, Hq 32, D 128",
+    3: "large batch bf16: 256 requests (+8 padded rows), ctx U[512,8192], manager bs 32 split to "
+       "kernel bs 16, Hkv 8, Hq 64, D 128",
+    4: "ragged + speculative bf16: 64 requests, 8192-token ragged chunk, then 1+3 causal decode "
+       "tokens each, bs 64, Hkv 8, Hq 32, D 128",
+}
+KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_slot_amd", "csrc", "paged_decode.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def attention_bytes(w, walk_blocks: int, table_walk: bool) -> int:
+    """Algorithmic bytes of one attention launch (whole blocks, the DMA unit).
+
+    Per request: the KV blocks it must read (context blocks, or every walked
+    column in the fixed-shape walk) at 2 * bs * Hkv * D * es bytes each plus
+    a 4-byte table entry; q in the cache dtype, fp32 out, and its seq_len.
+    """
+    es = w.es
+    per_block = 2 * w.block_size * w.num_kv_heads * w.head_dim * es + 4
+    blocks = 0
+    for r in range(w.num_rows):
+        L = int(w.seq_lens[r])
+        vis = min(max(L, 0), walk_blocks * w.block_size)
+        blocks += walk_blocks if table_walk else -(-vis // w.block_size)
+    q_out = w.num_rows * w.q_len * w.num_q_heads * w.head_dim * (es + 4)
+    return blocks * per_block + q_out + 4 * w.num_rows
+
+
+def slot_map_bytes(T: int) -> int:
+    """24 bytes per token: request index, position, table entry, slot."""
+    return 24 * T
+
+
+def cache_write_bytes(w, T_live: int, T: int) -> int:
+    """Each written token reads and writes its K and V rows; every slot is read."""
+    row = w.num_kv_heads * w.head_dim * w.es
+    return T_live * 4 * row + 8 * T
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="block_config_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--walk", default="context", choices=["context", "bucket", "full"],
+                    help="context: read only covering blocks; bucket/full: fixed-shape walk of the "
+                         "bucket's or the whole table's columns")
+    ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the steps, run one plain device copy of this size (counter scale)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every box here has one GPU); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import decode_attention_slot_amd as K
+    import workloads as W
+    from workloads import device as dev
+
+    if not os.path.exists(K.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    lib = K.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cuda = torch.device("cuda:0")
+    idx = WORKLOADS[args.workload]
+    w = W.make_workload(idx, seed=args.seed)
+
+    # ---- set-up (untimed): caches, prefill, rotation copies ---------------
+    t_setup = time.time()
+    s = dev.build(w, cuda, threads=16)
+    table_walk = args.walk != "context"
+    # tokens each request holds before its decode tokens (prior context + ragged chunk)
+    before = (w.computed + w.chunk_lens)[: w.num_reqs]
+    max_ctx = int(before.max()) if w.num_reqs else 0
+    num_spec = w.q_len - 1
+    buckets = w.buckets if args.walk == "bucket" else None
+    max_model_len = w.table_width * w.block_size
+    bucket_len, walk_blocks = K.select_ctx_bucket(max_ctx, num_spec, buckets, max_model_len,
+                                                  w.block_size)
+    walk_blocks = min(walk_blocks, w.table_width)
+
+    step_req = torch.cat([s.chunk_req, s.dec_req]).contiguous()
+    step_pos = torch.cat([s.chunk_pos, s.dec_pos]).contiguous()
+    step_k = torch.cat([s.chunk_k, s.dec_k]).contiguous()
+    step_v = torch.cat([s.chunk_v, s.dec_v]).contiguous()
+    T = int(step_req.numel())
+    T_live = int((step_req >= 0).sum().item())
+    a_bytes = attention_bytes(w, walk_blocks, table_walk)
+    kv_bytes_touched = a_bytes
+    if args.rotate > 0:
+        R = args.rotate
+    else:
+        R = int(min(8, max(1, math.ceil((1 << 30) / max(kv_bytes_touched, 1)))))
+    caches = [(s.k_cache, s.v_cache)]
+    for _ in range(R - 1):
+        caches.append((s.k_cache.clone(), s.v_cache.clone()))
+    slots = torch.empty(T, dtype=torch.int64, device=cuda)
+    out = torch.empty((w.num_rows, w.q_len, w.num_q_heads, w.head_dim), dtype=torch.float32,
+                      device=cuda)
+    ws = K.make_workspace(w.num_rows, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim, cuda)
+    stream = torch.cuda.current_stream(cuda)
+    sp = int(stream.cuda_stream)
+    dt = K.KVS_BF16 if w.dtype == "bf16" else K.KVS_F32
+    flags = K.KVS_WALK_TABLE if table_walk else 0
+    rows, stride = s.block_table.shape
+    slot_args = (step_req.data_ptr(), step_pos.data_ptr(), T, T, s.block_table.data_ptr(),
+                 int(rows), int(stride), w.block_size, slots.data_ptr(), sp)
+    write_args = [(step_k.data_ptr(), step_v.data_ptr(), slots.data_ptr(), T, kc.data_ptr(),
+                   vc.data_ptr(), w.total_blocks, w.block_size, w.num_kv_heads, w.head_dim, dt, sp)
+                  for kc, vc in caches]
+    attn_args = [(s.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), s.block_table.data_ptr(), int(stride),
+                  int(walk_blocks), s.seq_lens.data_ptr(), w.num_rows, w.q_len, w.num_q_heads,
+                  w.num_kv_heads, w.head_dim, w.block_size, w.total_blocks, w.scale, dt, flags,
+                  ws.data_ptr(), int(ws.numel()), out.data_ptr(), sp) for kc, vc in caches]
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    f_slot, f_write, f_attn = lib.kv_slot_mapping, lib.kv_cache_write, lib.paged_decode_attention
+    f_select = K.select_ctx_bucket
+
+    def step(i, ev=None):
+        # host: the per-step bucket pick the pages describe (feature off unless bucketed)
+        f_select(max_ctx, num_spec, buckets, max_model_len, w.block_size)
+        j = i % R
+        if ev is not None:
+            ev[0].record(stream)
+        st = f_slot(*slot_args)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= f_write(*write_args[j])
+        if ev is not None:
+            ev[2].record(stream)
+        st |= f_attn(*attn_args[j])
+        if ev is not None:
+            ev[3].record(stream)
+        if st:
+            raise RuntimeError(f"library call failed with status {st}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_slot = np.mean([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
+    t_write = np.mean([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
+    t_attn = np.mean([e[2].elapsed_time(e[3]) for e in events]) * 1e-3
+    ms_per_step = wall / args.steps * 1e3
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=cuda).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    step_bytes = slot_map_bytes(T) + cache_write_bytes(w, T_live, T) + a_bytes
+    decode_tokens = w.num_reqs * w.q_len
+    attn_gbps = a_bytes / t_attn / 1e9
+    result = {
+        "metric": "paged decode attention HBM GB/s (% of peak) + decode tokens/s; slot_map tok/s",
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, seeded block permutation; no dataset)",
+        "config": {
+            "workload": DESCRIPTIONS[idx],
+            "seed": w.seed,
+            "num_seqs": w.num_rows,
+            "q_len": w.q_len,
+            "walk": args.walk,
+            "walk_blocks": int(walk_blocks),
+            "bucket_len": int(bucket_len),
+            "step_tokens": T,
+            "cache_copies_rotated": R,
+            "parallelism": "single GPU",
+        },
+        "attention_gbps": round(attn_gbps, 2),
+        "attention_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "decode_tokens_per_s": round(decode_tokens / (ms_per_step * 1e-3), 1),
+        "slot_map_tokens_per_s": round(T / t_slot, 1),
+        "kernel_us": {"kv_slot_mapping": round(t_slot * 1e6, 3),
+                      "kv_cache_write": round(t_write * 1e6, 3),
+                      "paged_decode_attention": round(t_attn * 1e6, 3)},
+        "algorithmic_bytes": {"kv_slot_mapping": slot_map_bytes(T),
+                              "kv_cache_write": cache_write_bytes(w, T_live, T),
+                              "paged_decode_attention": a_bytes},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_attention",
+            "achieved": round(attn_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(args.workload, args.walk),
+        },
+        "setup_s": round(t_setup, 2),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, s.host_table, walk_blocks, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def measured_traffic(workload: str, walk: str):
+    """HBM bytes per launch from the committed counter summary, or None.
+
+    The summary records the kernel source hash it was taken with; once the
+    kernel has changed the figure no longer applies and None is reported.
+    """
+    path = os.path.join(ROOT, "profiles", f"paged_decode_attention_{workload}_{walk}_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, table, walk_blocks, seconds):
+    """The oracle as it stands, on the host cores, over a bounded sample.
+
+    Untimed: the oracle builds its own caches (prefill + step writes). Timed:
+    the oracle's paged_decode_attention, one request at a time in a cycle
+    over the batch, until ``seconds`` have passed. Throughput is the
+    algorithmic attention bytes of the requests processed per second. BLAS
+    is pinned to one thread, so the oracle runs on one core.
+    """
+    from threadpoolctl import threadpool_limits
+
+    from oracle.runner import OracleStep
+
+    with threadpool_limits(limits=1):
+        ref = OracleStep(w, table, full_image=False)
+        ref.write_step()
+        q = w.q()
+        es = w.es
+        per_block = 2 * w.block_size * w.num_kv_heads * w.head_dim * es + 4
+        per_req_fixed = w.q_len * w.num_q_heads * w.head_dim * (es + 4) + 4
+        done_bytes, n, r = 0, 0, 0
+        real = [i for i in range(w.num_reqs) if w.seq_lens[i] > 0]
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            rr = real[r % len(real)]
+            ref.attention(q, walk_blocks=walk_blocks, requests=[rr])
+            vis = min(int(w.seq_lens[rr]), walk_blocks * w.block_size)
+            done_bytes += -(-vis // w.block_size) * per_block + per_req_fixed
+            n += 1
+            r += 1
+        el = time.perf_counter() - t0
+    return {
+        "value": round(done_bytes / el / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"oracle fp64 paged_decode_attention, {n} request-steps of this workload "
+                  f"(cycling over its {len(real)} requests) in {el:.1f} s, BLAS on 1 thread; "
+                  f"host {os.cpu_count()} logical CPUs",
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -146,7 +146,7 @@ size_t paged_decode_attention_workspace_bytes(int32_t num_seqs, int32_t q_len,
                                               int32_t head_dim) {
   if (num_seqs < 0 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)
     return 0;
-  return kvs::kCounterBytes +
+  return kvs::decode_meta_bytes(num_seqs) +
          kvs::decode_partial_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim);
 }
 
@@ -168,8 +168,6 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
   if (!is_pow2(block_size) || block_size < 16 || block_size > 256) return KVS_EUNSUPPORTED;
   if ((int64_t)(num_q_heads / num_kv_heads) * q_len > kMaxRows) return KVS_EUNSUPPORTED;
   if (num_seqs > kMaxSeqs) return KVS_EUNSUPPORTED;
-  if ((int64_t)num_seqs * num_kv_heads > (int64_t)(kvs::kCounterBytes / sizeof(uint32_t)))
-    return KVS_EUNSUPPORTED;
   if ((int64_t)table_stride * block_size > INT_MAX / 2) return KVS_EUNSUPPORTED;
   if (num_seqs == 0) return KVS_OK;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
@@ -185,8 +183,8 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
   p.block_table = block_table;
   p.seq_lens = seq_lens;
   p.out = out;
-  p.counters = (uint32_t*)workspace;
-  p.partials = (float*)((char*)workspace + kvs::kCounterBytes);
+  p.chunk_meta = (int32_t*)workspace;
+  p.partials = (float*)((char*)workspace + kvs::decode_meta_bytes(num_seqs));
   p.total_blocks = total_blocks;
   p.table_stride = table_stride;
   p.walk_blocks = walk_blocks;

@@ -25,8 +25,8 @@ struct DecodeParams {
   const int32_t* block_table;
   const int32_t* seq_lens;
   float* out;
-  float* partials;     // [pairs][num_kv_heads][rows][head_dim + 4]
-  uint32_t* counters;  // [num_seqs * num_kv_heads], zero between calls
+  float* partials;      // [pairs][num_kv_heads][rows][head_dim + 4]
+  int32_t* chunk_meta;  // [num_seqs][2]: first pair index and chunk count
   int64_t total_blocks;
   int32_t table_stride;
   int32_t walk_blocks;
@@ -43,8 +43,9 @@ struct DecodeParams {
   int is_bf16;
 };
 
-// Workspace layout shared by the size query and the launch.
-constexpr size_t kCounterBytes = 65536 * sizeof(uint32_t);
+// Workspace layout shared by the size query and the launch:
+// [chunk_meta, rounded up to 256 bytes][partials].
+size_t decode_meta_bytes(int32_t num_seqs);
 int32_t decode_target_pairs(int32_t num_kv_heads);
 int32_t decode_min_chunk_blocks(int32_t block_size);
 size_t decode_partial_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads,

@@ -19,8 +19,14 @@
 //   min_chunk_blocks blocks each, whole blocks, aligned to logical block 0.
 //   The split depends only on the context lengths, so a head-trimmed walk,
 //   a full-table walk and the context walk produce the same partials.
-// * The block ids of a chunk are held one per lane in a VGPR and broadcast
-//   with readlane, so no LDS or barrier is needed.
+// * The block ids of a chunk are staged in LDS by the workgroup (pieces of
+//   up to 256 blocks), so each tile's block id is an LDS read that does not
+//   hold up the vector-memory pipeline.
+// * The tile loop is straight-line: the loads of tile t+1 are issued before
+//   tile t is computed and are never under a data-dependent branch (an
+//   inactive table entry reads null block 0 and is masked; the loop tail
+//   re-loads its last tile, which hits in cache), so one tile stays in
+//   flight behind the one being computed.
 // * Tile of 16 tokens. S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (fp32 KV:
 //   v_mfma_f32_16x16x4f32): K is the A operand (lane l holds token l % 16,
 //   16 bytes of its head row per piece), Q^T the B operand (lane l holds
@@ -37,8 +43,12 @@
 //   of a (request, KV head) to arrive, found with a device-scope counter,
 //   merges them in ascending chunk order and resets the counter.
 // * Masked keys are removed by select, never by multiplying by zero, and the
-//   values of keys past the context are zeroed, so unwritten (NaN canary)
-//   cache rows cannot leak into the output.
+//   values of keys past the context are replaced by -0.0, so unwritten (NaN
+//   canary) cache rows cannot leak into the output and a masked product is
+//   -0.0, which leaves every accumulator bit-unchanged.
+// * The fixed-shape table walk is a separate instantiation: it reads every
+//   walked column and folds the bytes it does not need into a sink that is
+//   stored only under a flag the host never sets.
 #include <math.h>
 
 #include "kvslot_internal.h"
@@ -50,11 +60,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kFlagWalkTable = 0x1u;
 // Never set by the host. Testing it keeps the table-walk loads alive.
 constexpr uint32_t kFlagSink = 0x80000000u;
 constexpr int kTile = 16;
+constexpr int kStage = 256;  // block ids staged in LDS at a time
 
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
@@ -93,8 +105,8 @@ __device__ __forceinline__ int visible_len(int L, int walk_tok) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-template <bool BF16, int D, int NW>
-__global__ void __launch_bounds__(NW * 64)
+template <bool BF16, int D, int NW, bool TW>
+__global__ void __launch_bounds__(NW * 64, 2)
 paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int ES = BF16 ? 2 : 4;       // bytes per element
   constexpr int EP = 16 / ES;            // elements per 16-byte piece
@@ -102,7 +114,14 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int NT = D / 16;             // P.V n-tiles (dimension columns of 16)
   constexpr int NVW = NT * ES / 4;       // V dwords per lane per token
   constexpr int PSTRIDE = D + 4;         // floats per partial row (acc, m, l, pad)
+  constexpr uint32_t kNegZero = BF16 ? 0x80008000u : 0x80000000u;
   static_assert(NP >= 1 && NVW >= 2, "unsupported head_dim");
+  struct TileBuf {
+    u32x4 k[NP];         // K pieces of token rho of the tile
+    uint32_t v[4][NVW];  // V slices of tokens 4*jg .. 4*jg+3
+    int bid;             // block id the tile was read from (<= 0: inactive)
+  };
+  __shared__ int s_blk[kStage];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -112,13 +131,12 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   const int B = p.num_seqs;
   const int bs = 1 << bs_shift;
   const int walk_tok = p.walk_blocks << bs_shift;
-  const bool table_walk = (p.flags & kFlagWalkTable) != 0;
   const int Hkv = p.num_kv_heads;
   const int Hq = p.num_q_heads;
   const int G = Hq / Hkv;
   const int Sq = p.q_len;
   const int nrows = G * Sq;
-  const int HG = (Hkv + NW - 1) / NW;
+  const int HG = Hkv / NW;  // the launcher picks NW dividing Hkv
   const int64_t block_bytes = ((int64_t)Hkv * D * ES) << bs_shift;
   const uint32_t row_bytes = (uint32_t)(Hkv * D * ES);
 
@@ -156,7 +174,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     // ---- locate (request, chunk) of this pair ----------------------------
     int r = -1, c = 0;
     int64_t pidx0 = 0;  // index of (r, chunk 0) among the pairs that hold context
-    if (!table_walk) {
+    if constexpr (!TW) {
       int64_t carry = 0;
       for (int base = 0; base < B; base += 64) {
         const int rr = base + lane;
@@ -197,11 +215,9 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       }
     }
     r = uniform(r);
-    if (r < 0) break;  // every pair is done
+    if (r < 0) break;  // every pair is done (uniform over the workgroup)
 
     const int g = hg * NW + wave;
-    if (g >= Hkv) continue;
-
     const int L = uniform(p.seq_lens[r]);
     const int E = visible_len(L, walk_tok);
     const int nb_r = (E + bs - 1) >> bs_shift;
@@ -209,7 +225,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     const bool pair_valid = c < Cv;
     const int tok0 = c * chunk_tok;
     const int tok_valid_end = min(tok0 + chunk_tok, E);
-    const int tok_walk_end = table_walk ? min(tok0 + chunk_tok, walk_tok) : tok_valid_end;
+    const int tok_walk_end = TW ? min(tok0 + chunk_tok, walk_tok) : tok_valid_end;
 
     // ---- query operand (B operand of the score MFMA) ---------------------
     const int jrow = rho / G;
@@ -236,121 +252,143 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     for (int n = 0; n < NT; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     const int32_t* trow = p.block_table + (int64_t)r * p.table_stride;
-    const int blk0 = tok0 >> bs_shift;
-    int stage_lo = -1;  // first chunk-relative block held in `staged`
-    int staged = 0;
-
     const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
     const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
 
-    for (int tt = tok0; tt < tok_walk_end; tt += kTile) {
-      const int rel = (tt >> bs_shift) - blk0;
-      if (stage_lo < 0 || rel >= stage_lo + 64) {
-        stage_lo = rel & ~63;
-        const int col = blk0 + stage_lo + lane;
-        staged = col < p.table_stride ? trow[col] : 0;
+    const int blk_first = tok0 >> bs_shift;
+    const int blk_end = tok_walk_end > tok0 ? ((tok_walk_end - 1) >> bs_shift) + 1 : blk_first;
+    for (int pb = blk_first; pb < blk_end; pb += kStage) {
+      const int pn = min(kStage, blk_end - pb);
+      __syncthreads();  // the previous piece is consumed by every wave
+      for (int i = threadIdx.x; i < pn; i += NW * 64) {
+        const int col = pb + i;
+        s_blk[i] = col < p.table_stride ? trow[col] : 0;
       }
-      const int bid = __builtin_amdgcn_readlane(staged, rel - stage_lo);
-      const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
-      if (!table_walk && !active) continue;  // the context walk never reads it
-      const bool compute = pair_valid && active && tt < tok_valid_end;
+      __syncthreads();
+      const int t_begin = max(tok0, pb << bs_shift);
+      const int t_end = min(tok_walk_end, (pb + pn) << bs_shift);
+      const int nt = (t_end - t_begin + kTile - 1) / kTile;
 
-      const char* kb = (const char*)p.k_cache + (int64_t)(active ? bid : 0) * block_bytes;
-      const char* vb = (const char*)p.v_cache + (int64_t)(active ? bid : 0) * block_bytes;
-      const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
-
-      u32x4 kp[NP];
+      // Loads of one tile: K as the score MFMA's A operand, V in row layout.
+      // Always issued: an inactive entry reads null block 0 and is masked.
+      auto load = [&](int tt, TileBuf& b) {
+        const int bid = uniform(s_blk[(tt >> bs_shift) - pb]);
+        const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
+        const int64_t base = (int64_t)(active ? bid : 0) * block_bytes;
+        const char* kb = (const char*)p.k_cache + base;
+        const char* vb = (const char*)p.v_cache + base;
+        const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
+        b.bid = active ? bid : 0;
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp) kp[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
-      uint32_t vw[4][NVW];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const char* src = vb + in_blk + v_lane_off + i * row_bytes;
-        if constexpr (NVW == 2) {
-          const u32x2 x = *(const u32x2*)src;
-          vw[i][0] = x[0]; vw[i][1] = x[1];
-        } else {
-#pragma unroll
-          for (int w = 0; w < NVW; w += 4) {
-            const u32x4 x = *(const u32x4*)(src + w * 4);
-            vw[i][w] = x[0]; vw[i][w + 1] = x[1]; vw[i][w + 2] = x[2]; vw[i][w + 3] = x[3];
-          }
-        }
-      }
-
-      if (!compute) {
-        // Fixed-shape walk past the context: read, never used.
-#pragma unroll
-        for (int pp = 0; pp < NP; ++pp) sink ^= kp[pp][0] ^ kp[pp][1] ^ kp[pp][2] ^ kp[pp][3];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int w = 0; w < NVW; ++w) sink ^= vw[i][w];
-        continue;
-      }
-
-      // ---- scores: S^T[token 4*jg+i][row rho] ----------------------------
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        if constexpr (BF16) {
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kp[pp]),
-                                                      __builtin_bit_cast(bf16x8, qp[pp]), s, 0,
-                                                      0, 0);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kp[pp][e]),
-                                                     __uint_as_float(qp[pp][e]), s, 0, 0, 0);
-        }
-      }
-
-      float sx[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sx[i] = s[i] * p.scale_log2;
-      const bool full = (tt + kTile <= tok_valid_end) && (tt + kTile - 1 <= qpos_min);
-      if (!full) {
+        for (int pp = 0; pp < NP; ++pp)
+          b.k[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int pos = tt + 4 * jg + i;
-          const bool kv_ok = pos < E;
-          if (!(kv_ok && pos <= qpos)) sx[i] = -INFINITY;
-          if (!kv_ok) {
-#pragma unroll
-            for (int w = 0; w < NVW; ++w) vw[i][w] = 0u;
-          }
-        }
-      }
-
-      // ---- online softmax ------------------------------------------------
-      float mx = fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3]));
-      mx = max_over_groups(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sx[i] - m_use);
-      l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-      }
-      m_run = m_new;
-
-      // ---- O^T += V^T P^T --------------------------------------------------
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          float v;
-          if constexpr (BF16) {
-            v = (n & 1) ? bf16_hi(vw[i][n >> 1]) : bf16_lo(vw[i][n >> 1]);
+          const char* src = vb + in_blk + v_lane_off + i * row_bytes;
+          if constexpr (NVW == 2) {
+            const u32x2 x = *(const u32x2*)src;
+            b.v[i][0] = x[0]; b.v[i][1] = x[1];
           } else {
-            v = __uint_as_float(vw[i][n]);
+#pragma unroll
+            for (int w = 0; w < NVW; w += 4) {
+              const u32x4 x = *(const u32x4*)(src + w * 4);
+              b.v[i][w] = x[0]; b.v[i][w + 1] = x[1]; b.v[i][w + 2] = x[2]; b.v[i][w + 3] = x[3];
+            }
           }
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pr[i], acc[n], 0, 0, 0);
         }
+      };
+
+      // Scores, online softmax and P.V for one tile whose loads have landed.
+      auto consume = [&](int tt, TileBuf& b) {
+        const bool active = b.bid > 0;
+        if constexpr (TW) {
+          if (!(pair_valid && active && tt < tok_valid_end)) {
+            // Fixed-shape walk past the context: read, never used.
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp)
+              sink ^= b.k[pp][0] ^ b.k[pp][1] ^ b.k[pp][2] ^ b.k[pp][3];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int w = 0; w < NVW; ++w) sink ^= b.v[i][w];
+            return;
+          }
+        }
+
+        // ---- scores: S^T[token 4*jg+i][row rho] ----------------------------
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          if constexpr (BF16) {
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[pp]),
+                                                        __builtin_bit_cast(bf16x8, qp[pp]), s,
+                                                        0, 0, 0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(b.k[pp][e]),
+                                                       __uint_as_float(qp[pp][e]), s, 0, 0, 0);
+          }
+        }
+
+        float sx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sx[i] = s[i] * p.scale_log2;
+        const bool full = active && (tt + kTile <= tok_valid_end) && (tt + kTile - 1 <= qpos_min);
+        if (!full) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pos = tt + 4 * jg + i;
+            const bool kv_ok = active && pos < E;
+            if (!(kv_ok && pos <= qpos)) sx[i] = -INFINITY;
+            if (!kv_ok) {
+#pragma unroll
+              for (int w = 0; w < NVW; ++w) b.v[i][w] = kNegZero;
+            }
+          }
+        }
+
+        // ---- online softmax ------------------------------------------------
+        float mx = fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3]));
+        mx = max_over_groups(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sx[i] - m_use);
+        l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+        }
+        m_run = m_new;
+
+        // ---- O^T += V^T P^T --------------------------------------------------
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            float v;
+            if constexpr (BF16) {
+              v = (n & 1) ? bf16_hi(b.v[i][n >> 1]) : bf16_lo(b.v[i][n >> 1]);
+            } else {
+              v = __uint_as_float(b.v[i][n]);
+            }
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pr[i], acc[n], 0, 0, 0);
+          }
+        }
+      };
+
+      // Two tile buffers: tile t+1 is in flight while tile t is computed.
+      TileBuf b0, b1;
+      load(t_begin, b0);
+      for (int t = 0; t < nt; t += 2) {
+        const int tt = t_begin + t * kTile;
+        load(t + 1 < nt ? tt + kTile : tt, b1);
+        consume(tt, b0);
+        load(t + 2 < nt ? tt + 2 * kTile : tt, b0);
+        if (t + 1 < nt) consume(tt + kTile, b1);
       }
     }
 
@@ -396,49 +434,152 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         }
       }
     }
-    __threadfence();
-    uint32_t* counter = p.counters + (int64_t)r * Hkv + g;
-    uint32_t prev = 0;
-    if (lane == 0) prev = atomicAdd(counter, 1u);
-    prev = __shfl(prev, 0);
-    if (prev != (uint32_t)(Cv - 1)) continue;
-
-    // ---- last chunk to finish: merge all partials in chunk order -----------
-    __threadfence();
-    if (rho < nrows) {
-      const float* pbase = p.partials + ((pidx0 * Hkv + g) * nrows + rho) * PSTRIDE;
-      const int64_t cstride = (int64_t)Hkv * nrows * PSTRIDE;
-      float M = -INFINITY;
-      for (int cc = 0; cc < Cv; ++cc) M = fmaxf(M, pbase[cc * cstride + D]);
-      float lsum = 0.0f;
-      f32x4 o4[D / 16];
-#pragma unroll
-      for (int k = 0; k < D / 16; ++k) o4[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (M != -INFINITY) {
-        for (int cc = 0; cc < Cv; ++cc) {
-          const float* pr = pbase + cc * cstride;
-          const float mc = pr[D];
-          if (mc == -INFINITY) continue;
-          const float w = __builtin_amdgcn_exp2f(mc - M);
-          lsum += w * pr[D + 1];
-#pragma unroll
-          for (int k = 0; k < D / 16; ++k) o4[k] += w * *(const f32x4*)(pr + d_base + 4 * k);
-        }
-      }
-      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-      float* o = p.out + (((int64_t)r * Sq + jrow) * Hq + (int64_t)g * G + hh) * D + d_base;
-#pragma unroll
-      for (int k = 0; k < D / 16; ++k) *(f32x4*)(o + 4 * k) = o4[k] * inv;
+    if (c == 0 && g == 0 && lane == 0) {
+      p.chunk_meta[2 * r] = (int32_t)pidx0;  // where request r's partials start
+      p.chunk_meta[2 * r + 1] = Cv;
     }
-    if (lane == 0) atomicExch(counter, 0u);
   }
 
-  if (p.flags & kFlagSink) p.out[0] = __uint_as_float(sink);
+  if constexpr (TW) {
+    if (p.flags & kFlagSink) p.out[0] = __uint_as_float(sink);
+  }
+}
+
+// Split-K merge: one workgroup of four waves per (request, KV head) whose
+// context was split over more than one chunk. Wave w merges chunks w, w+4,
+// ... in ascending order; the four partial states are then merged in wave
+// order through LDS. The assignment is fixed, so the result is the same on
+// every run and for every walk mode. Lane l of a wave owns output float4s
+// l + 64 k (k < KC) of the (row, dimension) block.
+template <int D, int KC>
+__global__ void __launch_bounds__(256)
+paged_decode_combine_kernel(const DecodeParams p, int bs_shift) {
+  constexpr int F4ROW = D / 4;
+  constexpr int PSTRIDE = D + 4;
+  constexpr int CB = 16 / KC;  // chunks whose loads are in flight together
+  constexpr int NWC = 4;       // waves per workgroup
+  __shared__ float s_m[NWC][KC * 64];
+  __shared__ float s_l[NWC][KC * 64];
+  __shared__ f32x4 s_o[NWC][KC * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int B = p.num_seqs;
+  const int bs = 1 << bs_shift;
+  const int walk_tok = p.walk_blocks << bs_shift;
+  const int Hkv = p.num_kv_heads;
+  const int Hq = p.num_q_heads;
+  const int G = Hq / Hkv;
+  const int Sq = p.q_len;
+  const int nrows = G * Sq;
+  const int f4_total = nrows * F4ROW;
+
+  // the chunk size pass 1 used (same inputs, same arithmetic)
+  int64_t ctx_blocks_total = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int r = base + lane;
+    int nb = 0;
+    if (r < B) nb = (visible_len(p.seq_lens[r], walk_tok) + bs - 1) >> bs_shift;
+    ctx_blocks_total += wave_sum(nb);
+  }
+  int64_t cb64 = (ctx_blocks_total + p.target_pairs - 1) / p.target_pairs;
+  if (cb64 < p.min_chunk_blocks) cb64 = p.min_chunk_blocks;
+  const int cb = uniform((int)cb64);
+
+  int roff[KC], moff[KC];
+  bool ok[KC];
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    const int f = lane + 64 * k;
+    const int row = f / F4ROW;
+    ok[k] = f < f4_total;
+    roff[k] = row * PSTRIDE + (f - row * F4ROW) * 4;
+    moff[k] = row * PSTRIDE + D;
+  }
+
+  for (int64_t u = blockIdx.x; u < (int64_t)B * Hkv; u += gridDim.x) {
+    const int r = (int)(u / Hkv);
+    const int g = (int)(u - (int64_t)r * Hkv);
+    const int E = visible_len(p.seq_lens[r], walk_tok);
+    const int Cv = (((E + bs - 1) >> bs_shift) + cb - 1) / cb;
+    if (Cv <= 1) continue;  // pass 1 wrote this output directly
+    const int64_t pidx0 = p.chunk_meta[2 * r];
+    const int64_t cstride = (int64_t)Hkv * nrows * PSTRIDE;
+    const float* pbase = p.partials + (pidx0 * Hkv + g) * nrows * PSTRIDE;
+
+    float Mx[KC], Ls[KC];
+    f32x4 o[KC];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      Mx[k] = -INFINITY;
+      Ls[k] = 0.0f;
+      o[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    for (int c0 = wave; c0 < Cv; c0 += NWC * CB) {
+      f32x4 a[CB][KC];
+      f32x2 ml[CB][KC];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        const int cc = c0 + j * NWC;
+        const float* pc = pbase + (int64_t)cc * cstride;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          if (cc < Cv && ok[k]) {
+            a[j][k] = *(const f32x4*)(pc + roff[k]);
+            ml[j][k] = *(const f32x2*)(pc + moff[k]);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          if (c0 + j * NWC < Cv && ok[k] && ml[j][k][0] != -INFINITY) {
+            const float mn = fmaxf(Mx[k], ml[j][k][0]);
+            const float so = __builtin_amdgcn_exp2f(Mx[k] - mn);
+            const float sn = __builtin_amdgcn_exp2f(ml[j][k][0] - mn);
+            Ls[k] = Ls[k] * so + ml[j][k][1] * sn;
+            o[k] = o[k] * so + a[j][k] * sn;
+            Mx[k] = mn;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      s_m[wave][lane + 64 * k] = Mx[k];
+      s_l[wave][lane + 64 * k] = Ls[k];
+      s_o[wave][lane + 64 * k] = o[k];
+    }
+    __syncthreads();
+    for (int f = threadIdx.x; f < f4_total; f += NWC * 64) {
+      float M = -INFINITY, Lt = 0.0f;
+      f32x4 ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NWC; ++w) {
+        const float mw = s_m[w][f];
+        if (mw == -INFINITY) continue;
+        const float mn = fmaxf(M, mw);
+        const float so = __builtin_amdgcn_exp2f(M - mn);
+        const float sn = __builtin_amdgcn_exp2f(mw - mn);
+        Lt = Lt * so + s_l[w][f] * sn;
+        ot = ot * so + s_o[w][f] * sn;
+        M = mn;
+      }
+      const int row = f / F4ROW;
+      const int jr = row / G;
+      const int hr = row - jr * G;
+      const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+      float* orow = p.out + (((int64_t)r * Sq + jr) * Hq + (int64_t)g * G + hr) * D;
+      *(f32x4*)(orow + (f - row * F4ROW) * 4) = ot * inv;
+    }
+    __syncthreads();
+  }
 }
 
 template <bool BF16, int D, int NW>
 hipError_t launch_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) {
-  const int HG = (p.num_kv_heads + NW - 1) / NW;
+  const int HG = p.num_kv_heads / NW;
   int64_t pairs;
   if (p.flags & kFlagWalkTable) {
     const int64_t cpr = (p.walk_blocks + p.min_chunk_blocks - 1) / p.min_chunk_blocks;
@@ -449,8 +590,23 @@ hipError_t launch_typed(const DecodeParams& p, int bs_shift, hipStream_t stream)
   int64_t grid = pairs * HG;
   if (grid < 1) grid = 1;
   if (grid > (1 << 20)) grid = 1 << 20;
-  paged_decode_kernel<BF16, D, NW><<<dim3((unsigned)grid), dim3(NW * 64), 0, stream>>>(p,
-                                                                                      bs_shift);
+  if (p.flags & kFlagWalkTable)
+    paged_decode_kernel<BF16, D, NW, true>
+        <<<dim3((unsigned)grid), dim3(NW * 64), 0, stream>>>(p, bs_shift);
+  else
+    paged_decode_kernel<BF16, D, NW, false>
+        <<<dim3((unsigned)grid), dim3(NW * 64), 0, stream>>>(p, bs_shift);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t cgrid = (int64_t)p.num_seqs * p.num_kv_heads;
+  if (cgrid > 65536) cgrid = 65536;
+  const int nrows = p.num_q_heads / p.num_kv_heads * p.q_len;
+  const int kc = (nrows * (D / 4) + 63) / 64;
+  const dim3 cg((unsigned)cgrid), cb(256);
+  if (kc <= 1) paged_decode_combine_kernel<D, 1><<<cg, cb, 0, stream>>>(p, bs_shift);
+  else if (kc <= 2) paged_decode_combine_kernel<D, 2><<<cg, cb, 0, stream>>>(p, bs_shift);
+  else if (kc <= 4) paged_decode_combine_kernel<D, 4><<<cg, cb, 0, stream>>>(p, bs_shift);
+  else paged_decode_combine_kernel<D, 8><<<cg, cb, 0, stream>>>(p, bs_shift);
   return hipGetLastError();
 }
 
@@ -466,8 +622,9 @@ hipError_t launch_heads(const DecodeParams& p, int bs_shift, hipStream_t stream)
 }  // namespace
 
 int32_t decode_target_pairs(int32_t num_kv_heads) {
-  // About 2048 waves in flight over the 1024 SIMDs of a 256-CU part.
-  const int32_t t = 2048 / (num_kv_heads > 0 ? num_kv_heads : 1);
+  // About 8192 waves of work over the 1024 SIMDs of a 256-CU part, so the
+  // (request, chunk) units spread evenly over the CUs.
+  const int32_t t = 8192 / (num_kv_heads > 0 ? num_kv_heads : 1);
   return t > 16 ? t : 16;
 }
 
@@ -476,6 +633,10 @@ int32_t decode_min_chunk_blocks(int32_t block_size) {
   // of the KV bytes the chunk reads.
   const int32_t b = 128 / block_size;
   return b > 1 ? b : 1;
+}
+
+size_t decode_meta_bytes(int32_t num_seqs) {
+  return ((size_t)num_seqs * 2 * sizeof(int32_t) + 255) / 256 * 256;
 }
 
 size_t decode_partial_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads,

@@ -188,10 +188,9 @@ size_t paged_decode_attention_workspace_bytes(int32_t num_seqs, int32_t q_len,
  *   seq_lens     int32 [num_seqs], device
  *   out          float [num_seqs][q_len][num_q_heads][head_dim], device
  *   workspace    device memory of at least
- *                paged_decode_attention_workspace_bytes(...) bytes. It must
- *                be zero-filled before its first use; every call leaves it
- *                ready for the next call on the same stream. Calls that run
- *                concurrently must not share a workspace.
+ *                paged_decode_attention_workspace_bytes(...) bytes, scratch
+ *                for the split-K partials; no initial contents are needed.
+ *                Calls that run concurrently must not share a workspace.
  *   flags        0 (context walk: only blocks covering each request's
  *                context are read) or KVS_WALK_TABLE.
  * By default only the blocks covering min(L, walk_blocks * block_size)
@@ -199,8 +198,7 @@ size_t paged_decode_attention_workspace_bytes(int32_t num_seqs, int32_t q_len,
  * trim, on the flags, on the physical block ids, or on whether unused
  * entries hold 0 or -1: they are bitwise identical across those.
  * Supported: head_dim 64 or 128; block_size 16, 32, 64, 128 or 256;
- * (num_q_heads / num_kv_heads) * q_len <= 16; num_seqs <= 8192;
- * num_seqs * num_kv_heads <= 65536.
+ * (num_q_heads / num_kv_heads) * q_len <= 16; num_seqs <= 8192.
  * Errors: KVS_EINVAL (null pointers, non-positive sizes, num_q_heads not a
  * multiple of num_kv_heads, walk_blocks outside [0, table_stride]),
  * KVS_EUNSUPPORTED (outside the supported set), KVS_ENOSPACE (workspace
