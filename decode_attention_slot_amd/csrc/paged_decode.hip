@@ -67,6 +67,7 @@ constexpr uint32_t kFlagWalkTable = 0x1u;
 constexpr uint32_t kFlagSink = 0x80000000u;
 constexpr int kTile = 16;
 constexpr int kStage = 256;  // block ids staged in LDS at a time
+constexpr int kSlices = 8;   // 64-request slices of seq_lens kept in registers
 
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
@@ -140,30 +141,37 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   const int64_t block_bytes = ((int64_t)Hkv * D * ES) << bs_shift;
   const uint32_t row_bytes = (uint32_t)(Hkv * D * ES);
 
+  // ---- context blocks of every request ------------------------------------
+  // Batches of up to 64 * kSlices requests keep their block counts in
+  // registers (lane l of slice k: request 64 k + l), loaded in one round
+  // trip, so a workgroup's set-up costs one memory latency.
+  const bool in_regs = B <= 64 * kSlices;
+  int nbr[kSlices];
+#pragma unroll
+  for (int k = 0; k < kSlices; ++k) {
+    const int rr = 64 * k + lane;
+    nbr[k] = 0;
+    if (in_regs && rr < B) nbr[k] = (visible_len(p.seq_lens[rr], walk_tok) + bs - 1) >> bs_shift;
+  }
+  auto blocks_of = [&](int rr) {  // large batches only
+    return rr < B ? (visible_len(p.seq_lens[rr], walk_tok) + bs - 1) >> bs_shift : 0;
+  };
+
   // ---- chunk size, from the context blocks of the whole batch ------------
   int64_t ctx_blocks_total = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int r = base + lane;
-    int nb = 0;
-    if (r < B) nb = (visible_len(p.seq_lens[r], walk_tok) + bs - 1) >> bs_shift;
-    ctx_blocks_total += wave_sum(nb);
+  if (in_regs) {
+    int t = 0;
+#pragma unroll
+    for (int k = 0; k < kSlices; ++k) t += nbr[k];
+    ctx_blocks_total = wave_sum(t);
+  } else {
+    for (int base = 0; base < B; base += 64) ctx_blocks_total += wave_sum(blocks_of(base + lane));
   }
   int64_t cb64 = (ctx_blocks_total + p.target_pairs - 1) / p.target_pairs;
   if (cb64 < p.min_chunk_blocks) cb64 = p.min_chunk_blocks;
   const int cb = uniform((int)cb64);  // blocks per chunk
   const int chunk_tok = cb << bs_shift;
   const int walk_chunks = (p.walk_blocks + cb - 1) / cb;
-
-  // ---- requests with no visible context produce zeros --------------------
-  {
-    const int row_floats = Sq * Hq * D;
-    for (int r = blockIdx.x; r < B; r += gridDim.x) {
-      if (visible_len(p.seq_lens[r], walk_tok) == 0) {
-        float* o = p.out + (int64_t)r * row_floats;
-        for (int i = threadIdx.x; i < row_floats; i += NW * 64) o[i] = 0.0f;
-      }
-    }
-  }
 
   uint32_t sink = 0;
 
@@ -175,46 +183,51 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     int r = -1, c = 0;
     int64_t pidx0 = 0;  // index of (r, chunk 0) among the pairs that hold context
     if constexpr (!TW) {
+      // pair = (sum of chunk counts of requests before r) + c
       int64_t carry = 0;
-      for (int base = 0; base < B; base += 64) {
-        const int rr = base + lane;
-        int C = 0;
-        if (rr < B) {
-          const int nb = (visible_len(p.seq_lens[rr], walk_tok) + bs - 1) >> bs_shift;
-          C = (nb + cb - 1) / cb;
-        }
+      auto visit = [&](int base, int nb) {
+        const int C = (nb + cb - 1) / cb;
         const int incl = wave_inclusive_scan(C, lane);
         const int tot = __shfl(incl, 63);
-        if (pair < carry + tot) {
+        if (r < 0 && pair < carry + tot) {
           const uint64_t hit = __ballot(carry + incl > pair);
           const int src = __builtin_ctzll(hit);
           const int excl = __shfl(incl - C, src);
           r = base + src;
           pidx0 = carry + excl;
           c = (int)(pair - pidx0);
-          break;
         }
         carry += tot;
+      };
+      if (in_regs) {
+#pragma unroll
+        for (int k = 0; k < kSlices; ++k)
+          if (64 * k < B) visit(64 * k, nbr[k]);
+      } else {
+        for (int base = 0; base < B && r < 0; base += 64) visit(base, blocks_of(base + lane));
       }
     } else if (walk_chunks > 0) {
       const int64_t rq = pair / walk_chunks;
       if (rq < B) {
         r = (int)rq;
         c = (int)(pair - rq * walk_chunks);
-        int64_t carry = 0;
-        for (int base = 0; base < r; base += 64) {
-          const int rr = base + lane;
-          int C = 0;
-          if (rr < r) {
-            const int nb = (visible_len(p.seq_lens[rr], walk_tok) + bs - 1) >> bs_shift;
-            C = (nb + cb - 1) / cb;
-          }
-          carry += wave_sum(C);
+        int carry = 0;  // chunks holding context of the requests before r
+        if (in_regs) {
+#pragma unroll
+          for (int k = 0; k < kSlices; ++k)
+            carry += (64 * k + lane < r) ? (nbr[k] + cb - 1) / cb : 0;
+        } else {
+          for (int base = 0; base < r; base += 64)
+            carry += (base + lane < r) ? (blocks_of(base + lane) + cb - 1) / cb : 0;
         }
-        pidx0 = carry;
+        pidx0 = wave_sum(carry);
       }
     }
+    // The scan leaves these in vector registers; they are the same in every
+    // lane, and saying so keeps the tile loop below under scalar control.
     r = uniform(r);
+    c = uniform(c);
+    pidx0 = uniform((int)pidx0);  // < target_pairs + num_seqs
     if (r < 0) break;  // every pair is done (uniform over the workgroup)
 
     const int g = hg * NW + wave;
@@ -437,6 +450,17 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     if (c == 0 && g == 0 && lane == 0) {
       p.chunk_meta[2 * r] = (int32_t)pidx0;  // where request r's partials start
       p.chunk_meta[2 * r + 1] = Cv;
+    }
+  }
+
+  // ---- requests with no visible context produce zeros --------------------
+  {
+    const int row_floats = Sq * Hq * D;
+    for (int r = blockIdx.x; r < B; r += gridDim.x) {
+      if (visible_len(p.seq_lens[r], walk_tok) == 0) {
+        float* o = p.out + (int64_t)r * row_floats;
+        for (int i = threadIdx.x; i < row_floats; i += NW * 64) o[i] = 0.0f;
+      }
     }
   }
 
