@@ -411,6 +411,11 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     const float l_tot = sum_over_groups(l_run);
     const int d_base = 4 * jg * NT;
 
+    if (c == 0 && g == 0 && lane == 0) {
+      p.chunk_meta[2 * r] = (int32_t)pidx0;  // where request r's partials start
+      p.chunk_meta[2 * r + 1] = Cv;          // read by the merge kernel
+    }
+
     if (Cv == 1) {
       if (rho < nrows) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
@@ -447,10 +452,6 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         }
       }
     }
-    if (c == 0 && g == 0 && lane == 0) {
-      p.chunk_meta[2 * r] = (int32_t)pidx0;  // where request r's partials start
-      p.chunk_meta[2 * r + 1] = Cv;
-    }
   }
 
   // ---- requests with no visible context produce zeros --------------------
@@ -460,6 +461,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       if (visible_len(p.seq_lens[r], walk_tok) == 0) {
         float* o = p.out + (int64_t)r * row_floats;
         for (int i = threadIdx.x; i < row_floats; i += NW * 64) o[i] = 0.0f;
+        if (threadIdx.x == 0) p.chunk_meta[2 * r + 1] = 0;
       }
     }
   }
@@ -469,19 +471,27 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   }
 }
 
-// Split-K merge: one workgroup of four waves per (request, KV head) whose
-// context was split over more than one chunk. Wave w merges chunks w, w+4,
-// ... in ascending order; the four partial states are then merged in wave
-// order through LDS. The assignment is fixed, so the result is the same on
-// every run and for every walk mode. Lane l of a wave owns output float4s
-// l + 64 k (k < KC) of the (row, dimension) block.
+// Split-K merge: one workgroup per (request, KV head) whose context was
+// split over more than one chunk. Wave w merges chunks w, w + NWC, ... in
+// ascending order; the NWC partial states are then merged in wave order
+// through LDS. The assignment is fixed, so the result is the same on every
+// run and for every walk mode. Lane l of a wave owns output float4s
+// l + 64 k (k < KC) of the (row, dimension) block. Fewer float4s per lane
+// leave room for more waves, so long contexts (many chunks) merge with
+// 16 waves.
+template <int KC>
+struct MergeShape {
+  static constexpr int NWC = KC <= 2 ? 16 : 32 / KC;  // waves per workgroup
+  static constexpr int CB = KC == 1 ? 8 : (KC == 2 ? 3 : (KC == 4 ? 2 : 1));  // chunks in flight per wave
+};
+
 template <int D, int KC>
-__global__ void __launch_bounds__(256)
-paged_decode_combine_kernel(const DecodeParams p, int bs_shift) {
+__global__ void __launch_bounds__(MergeShape<KC>::NWC * 64)
+paged_decode_combine_kernel(const DecodeParams p) {
   constexpr int F4ROW = D / 4;
   constexpr int PSTRIDE = D + 4;
-  constexpr int CB = 16 / KC;  // chunks whose loads are in flight together
-  constexpr int NWC = 4;       // waves per workgroup
+  constexpr int CB = MergeShape<KC>::CB;
+  constexpr int NWC = MergeShape<KC>::NWC;
   __shared__ float s_m[NWC][KC * 64];
   __shared__ float s_l[NWC][KC * 64];
   __shared__ f32x4 s_o[NWC][KC * 64];
@@ -489,26 +499,12 @@ paged_decode_combine_kernel(const DecodeParams p, int bs_shift) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int B = p.num_seqs;
-  const int bs = 1 << bs_shift;
-  const int walk_tok = p.walk_blocks << bs_shift;
   const int Hkv = p.num_kv_heads;
   const int Hq = p.num_q_heads;
   const int G = Hq / Hkv;
   const int Sq = p.q_len;
   const int nrows = G * Sq;
   const int f4_total = nrows * F4ROW;
-
-  // the chunk size pass 1 used (same inputs, same arithmetic)
-  int64_t ctx_blocks_total = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int r = base + lane;
-    int nb = 0;
-    if (r < B) nb = (visible_len(p.seq_lens[r], walk_tok) + bs - 1) >> bs_shift;
-    ctx_blocks_total += wave_sum(nb);
-  }
-  int64_t cb64 = (ctx_blocks_total + p.target_pairs - 1) / p.target_pairs;
-  if (cb64 < p.min_chunk_blocks) cb64 = p.min_chunk_blocks;
-  const int cb = uniform((int)cb64);
 
   int roff[KC], moff[KC];
   bool ok[KC];
@@ -524,9 +520,8 @@ paged_decode_combine_kernel(const DecodeParams p, int bs_shift) {
   for (int64_t u = blockIdx.x; u < (int64_t)B * Hkv; u += gridDim.x) {
     const int r = (int)(u / Hkv);
     const int g = (int)(u - (int64_t)r * Hkv);
-    const int E = visible_len(p.seq_lens[r], walk_tok);
-    const int Cv = (((E + bs - 1) >> bs_shift) + cb - 1) / cb;
-    if (Cv <= 1) continue;  // pass 1 wrote this output directly
+    const int Cv = p.chunk_meta[2 * r + 1];  // pass 1 records it for every request
+    if (Cv <= 1) continue;                    // pass 1 wrote this output directly
     const int64_t pidx0 = p.chunk_meta[2 * r];
     const int64_t cstride = (int64_t)Hkv * nrows * PSTRIDE;
     const float* pbase = p.partials + (pidx0 * Hkv + g) * nrows * PSTRIDE;
@@ -604,13 +599,13 @@ paged_decode_combine_kernel(const DecodeParams p, int bs_shift) {
 template <bool BF16, int D, int NW>
 hipError_t launch_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) {
   const int HG = p.num_kv_heads / NW;
-  int64_t pairs;
-  if (p.flags & kFlagWalkTable) {
-    const int64_t cpr = (p.walk_blocks + p.min_chunk_blocks - 1) / p.min_chunk_blocks;
-    pairs = (int64_t)p.num_seqs * (cpr > 0 ? cpr : 1);
-  } else {
+  // Upper bound on the (request, chunk) pairs, from host-known sizes only:
+  // no request has more than ceil(walk_blocks / min_chunk_blocks) chunks,
+  // and the context walk never has more than target_pairs + num_seqs.
+  const int64_t cpr = (p.walk_blocks + p.min_chunk_blocks - 1) / p.min_chunk_blocks;
+  int64_t pairs = (int64_t)p.num_seqs * (cpr > 0 ? cpr : 1);
+  if (!(p.flags & kFlagWalkTable) && pairs > (int64_t)p.target_pairs + p.num_seqs)
     pairs = (int64_t)p.target_pairs + p.num_seqs;
-  }
   int64_t grid = pairs * HG;
   if (grid < 1) grid = 1;
   if (grid > (1 << 20)) grid = 1 << 20;
@@ -626,11 +621,15 @@ hipError_t launch_typed(const DecodeParams& p, int bs_shift, hipStream_t stream)
   if (cgrid > 65536) cgrid = 65536;
   const int nrows = p.num_q_heads / p.num_kv_heads * p.q_len;
   const int kc = (nrows * (D / 4) + 63) / 64;
-  const dim3 cg((unsigned)cgrid), cb(256);
-  if (kc <= 1) paged_decode_combine_kernel<D, 1><<<cg, cb, 0, stream>>>(p, bs_shift);
-  else if (kc <= 2) paged_decode_combine_kernel<D, 2><<<cg, cb, 0, stream>>>(p, bs_shift);
-  else if (kc <= 4) paged_decode_combine_kernel<D, 4><<<cg, cb, 0, stream>>>(p, bs_shift);
-  else paged_decode_combine_kernel<D, 8><<<cg, cb, 0, stream>>>(p, bs_shift);
+  const dim3 cg((unsigned)cgrid);
+#define KVS_MERGE(KC)                                                             \
+  paged_decode_combine_kernel<D, KC>                                              \
+      <<<cg, dim3(MergeShape<KC>::NWC * 64), 0, stream>>>(p)
+  if (kc <= 1) KVS_MERGE(1);
+  else if (kc <= 2) KVS_MERGE(2);
+  else if (kc <= 4) KVS_MERGE(4);
+  else KVS_MERGE(8);
+#undef KVS_MERGE
   return hipGetLastError();
 }
 
