@@ -96,6 +96,8 @@ def main(argv=None) -> int:
     ap.add_argument("--walk", default="context", choices=["context", "bucket", "full"],
                     help="context: read only covering blocks; bucket/full: fixed-shape walk of the "
                          "bucket's or the whole table's columns")
+    ap.add_argument("--max-ctx", type=int, default=None,
+                    help="bucketing workload: clip the drawn context lengths and pin the largest")
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -122,7 +124,8 @@ def main(argv=None) -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cuda = torch.device("cuda:0")
     idx = WORKLOADS[args.workload]
-    w = W.make_workload(idx, seed=args.seed)
+    extra = {"forced_max_ctx": args.max_ctx} if (idx == 2 and args.max_ctx is not None) else {}
+    w = W.make_workload(idx, seed=args.seed, **extra)
 
     # ---- set-up (untimed): caches, prefill, rotation copies ---------------
     t_setup = time.time()
@@ -239,6 +242,7 @@ def main(argv=None) -> int:
         "config": {
             "workload": DESCRIPTIONS[idx],
             "seed": w.seed,
+            "max_ctx": int((w.computed + w.chunk_lens)[: w.num_reqs].max()),
             "num_seqs": w.num_rows,
             "q_len": w.q_len,
             "walk": args.walk,
