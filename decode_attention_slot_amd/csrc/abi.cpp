@@ -22,7 +22,7 @@ int elem_bytes(kvs_dtype d) {
 }
 
 constexpr int kMaxRows = 16;        // (Hq / Hkv) * q_len: one MFMA column tile
-constexpr int kMaxSeqs = 8192;
+constexpr int kMaxSeqs = kvs::kDecodeMaxSeqs;
 
 }  // namespace
 
@@ -169,6 +169,8 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
   if ((int64_t)(num_q_heads / num_kv_heads) * q_len > kMaxRows) return KVS_EUNSUPPORTED;
   if (num_seqs > kMaxSeqs) return KVS_EUNSUPPORTED;
   if ((int64_t)table_stride * block_size > INT_MAX / 2) return KVS_EUNSUPPORTED;
+  // the batch's 16-token tiles are counted in 32 bits, with headroom
+  if ((int64_t)num_seqs * walk_blocks * (block_size / 16) > INT_MAX / 2) return KVS_EUNSUPPORTED;
   if (num_seqs == 0) return KVS_OK;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
     return KVS_EINVAL;
@@ -194,8 +196,8 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
   p.num_kv_heads = num_kv_heads;
   p.head_dim = head_dim;
   p.block_size = block_size;
-  p.target_pairs = kvs::decode_target_pairs(num_kv_heads);
-  p.min_chunk_blocks = kvs::decode_min_chunk_blocks(block_size);
+  p.max_slices = kvs::decode_max_slices(num_kv_heads);
+  p.min_tiles = 8;  // 128 tokens: partial traffic stays a few percent of the KV a slice reads
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   p.flags = flags;
   p.is_bf16 = dtype == KVS_BF16;

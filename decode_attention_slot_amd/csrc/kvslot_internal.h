@@ -25,8 +25,8 @@ struct DecodeParams {
   const int32_t* block_table;
   const int32_t* seq_lens;
   float* out;
-  float* partials;      // [pairs][num_kv_heads][rows][head_dim + 4]
-  int32_t* chunk_meta;  // [num_seqs][2]: first pair index and chunk count
+  float* partials;      // [slots][num_kv_heads][rows][head_dim + 4]
+  int32_t* chunk_meta;  // [num_seqs][2]: first partial slot and partial count
   int64_t total_blocks;
   int32_t table_stride;
   int32_t walk_blocks;
@@ -36,20 +36,25 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t block_size;
-  int32_t target_pairs;      // split-K: aim for about this many (request, chunk) pairs
-  int32_t min_chunk_blocks;  // never split finer than this
+  int32_t max_slices;  // partial storage bound on the slices (per head group)
+  int32_t slices;      // set by the launcher: slices the batch's tiles are cut into
+  int32_t min_tiles;   // never cut a slice shorter than this many 16-token tiles
   float scale_log2;          // softmax scale times log2(e)
   uint32_t flags;
   int is_bf16;
 };
 
+// Largest batch the decode kernels take (their LDS holds one int per request).
+constexpr int32_t kDecodeMaxSeqs = 8192;
+
 // Workspace layout shared by the size query and the launch:
 // [chunk_meta, rounded up to 256 bytes][partials].
 size_t decode_meta_bytes(int32_t num_seqs);
-int32_t decode_target_pairs(int32_t num_kv_heads);
-int32_t decode_min_chunk_blocks(int32_t block_size);
+int32_t decode_max_slices(int32_t num_kv_heads);
 size_t decode_partial_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
                             int32_t num_kv_heads, int32_t head_dim);
+// Dynamic LDS of the pass-1 kernel: the batch's tile prefix.
+size_t decode_lds_bytes(int32_t num_seqs);
 
 hipError_t launch_paged_decode(const DecodeParams& p, hipStream_t stream);
 

@@ -10,16 +10,20 @@
 // scale * <q, k> over those keys applied to the values, in fp32.
 //
 // How, on CDNA4:
-// * Work unit: one wavefront per (request, chunk of context blocks, KV head).
-//   A workgroup holds the waves of up to NW KV heads of one (request,
-//   chunk), so the whole [block][token][head][dim] rows a workgroup reads
-//   are contiguous in HBM.
-// * Chunks are sized on the device from seq_lens (no host synchronisation):
-//   about target_pairs (request, chunk) pairs over the batch, at least
-//   min_chunk_blocks blocks each, whole blocks, aligned to logical block 0.
-//   The split depends only on the context lengths, so a head-trimmed walk,
-//   a full-table walk and the context walk produce the same partials.
-// * The block ids of a chunk are staged in LDS by the workgroup (pieces of
+// * Work split: the 16-token tiles of every request's context, laid end to
+//   end over the batch, are cut into `slices` equal ranges, one per
+//   resident workgroup slot, so every workgroup streams the same number of
+//   bytes and all finish together (no rounds, no tail of short units). A
+//   range may start or end inside a request and may span requests; each
+//   (slice, request) piece is a segment. One wavefront per KV head; a
+//   workgroup holds the waves of NW KV heads, so the [block][token][head]
+//   rows it reads are contiguous in HBM.
+// * The cut is made on the device from seq_lens (no host synchronisation):
+//   every workgroup scans the batch's tile counts into an LDS prefix. It
+//   depends only on the visible context lengths and the device, so a
+//   head-trimmed walk, a full-table walk and the context walk produce the
+//   same partials.
+// * The block ids of a segment are staged in LDS by the workgroup (pieces of
 //   up to 256 blocks), so each tile's block id is an LDS read that does not
 //   hold up the vector-memory pipeline.
 // * The tile loop is straight-line: the loads of tile t+1 are issued before
@@ -33,23 +37,27 @@
 //   query row l % 16; rows are (query token, head in group), at most 16).
 //   The result gives each lane four tokens of one query row.
 // * Online softmax per query row, in exp2 units, entirely inside the lane
-//   except one max over the four lane groups.
+//   except one max over the four lane groups (two permlane swaps).
 // * O^T = V^T P^T on v_mfma_f32_16x16x4f32: lane l holds the fp32 value of
 //   dimension column l % 16 for token 4 * (l / 16) + i, which is exactly a
 //   16-byte slice of that token's head row, so V is read in its natural
 //   layout (each 16-lane group reads one whole 256-byte head row). The
 //   accumulator lands with query row = l % 16, matching the softmax state.
-// * Split-K partials (acc, m, l per row) go to the workspace; the last wave
-//   of a (request, KV head) to arrive, found with a device-scope counter,
-//   merges them in ascending chunk order and resets the counter.
+// * A segment that holds a whole request writes its output. Otherwise its
+//   partial state (acc, m, l per row) goes to slot slice + request of the
+//   workspace; a second kernel merges a request's partials in slice order,
+//   so results do not depend on scheduling.
 // * Masked keys are removed by select, never by multiplying by zero, and the
 //   values of keys past the context are replaced by -0.0, so unwritten (NaN
 //   canary) cache rows cannot leak into the output and a masked product is
 //   -0.0, which leaves every accumulator bit-unchanged.
-// * The fixed-shape table walk is a separate instantiation: it reads every
-//   walked column and folds the bytes it does not need into a sink that is
-//   stored only under a flag the host never sets.
+// * The fixed-shape table walk is a separate instantiation: it computes
+//   the same segments, then reads every walked column past each context
+//   (cut the same way over the slices) and folds those bytes into a sink
+//   that is stored only under a flag the host never sets.
 #include <math.h>
+
+#include <atomic>
 
 #include "kvslot_internal.h"
 
@@ -67,33 +75,43 @@ constexpr uint32_t kFlagWalkTable = 0x1u;
 constexpr uint32_t kFlagSink = 0x80000000u;
 constexpr int kTile = 16;
 constexpr int kStage = 256;  // block ids staged in LDS at a time
-constexpr int kSlices = 8;   // 64-request slices of seq_lens kept in registers
+constexpr int kDepth = 2;    // tiles in flight per wave
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+// Wavefront scans on DPP: four row shifts build the prefix inside each row
+// of 16 lanes, two row broadcasts carry it across rows. Values move lane to
+// lane in the VALU, with no LDS round trip. Every lane must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, false);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
 
+// Reductions over the four 16-lane groups of a wavefront (lanes l, l ^ 16,
+// l ^ 32, l ^ 48): permlane16_swap pairs rows 0-1 and 2-3, permlane32_swap
+// pairs the two halves. Each lane receives its partner's value; both
+// operands of the combine are then the same in every lane of the group.
 __device__ __forceinline__ float max_over_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float sum_over_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -115,14 +133,18 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int NT = D / 16;             // P.V n-tiles (dimension columns of 16)
   constexpr int NVW = NT * ES / 4;       // V dwords per lane per token
   constexpr int PSTRIDE = D + 4;         // floats per partial row (acc, m, l, pad)
+  constexpr int NTHR = NW * 64;
   constexpr uint32_t kNegZero = BF16 ? 0x80008000u : 0x80000000u;
   static_assert(NP >= 1 && NVW >= 2, "unsupported head_dim");
   struct TileBuf {
     u32x4 k[NP];         // K pieces of token rho of the tile
     uint32_t v[4][NVW];  // V slices of tokens 4*jg .. 4*jg+3
-    int bid;             // block id the tile was read from (<= 0: inactive)
+    int bid;             // block id the tile was read from (0: inactive entry)
   };
+  extern __shared__ int s_pref[];  // [num_seqs + 1]: first tile of each request
   __shared__ int s_blk[kStage];
+  __shared__ int s_wave[NW];
+  __shared__ int s_first[2];  // request holding this slice's first tile (context, padding)
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -132,115 +154,145 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   const int B = p.num_seqs;
   const int bs = 1 << bs_shift;
   const int walk_tok = p.walk_blocks << bs_shift;
+  const int walk_tiles = walk_tok / kTile;
   const int Hkv = p.num_kv_heads;
   const int Hq = p.num_q_heads;
   const int G = Hq / Hkv;
   const int Sq = p.q_len;
   const int nrows = G * Sq;
   const int HG = Hkv / NW;  // the launcher picks NW dividing Hkv
+  const int S = p.slices;
+  const int slice = blockIdx.x / HG;
+  const int hg = blockIdx.x - slice * HG;
+  const int g = hg * NW + wave;
   const int64_t block_bytes = ((int64_t)Hkv * D * ES) << bs_shift;
   const uint32_t row_bytes = (uint32_t)(Hkv * D * ES);
 
-  // ---- context blocks of every request ------------------------------------
-  // Batches of up to 64 * kSlices requests keep their block counts in
-  // registers (lane l of slice k: request 64 k + l), loaded in one round
-  // trip, so a workgroup's set-up costs one memory latency.
-  const bool in_regs = B <= 64 * kSlices;
-  int nbr[kSlices];
-#pragma unroll
-  for (int k = 0; k < kSlices; ++k) {
-    const int rr = 64 * k + lane;
-    nbr[k] = 0;
-    if (in_regs && rr < B) nbr[k] = (visible_len(p.seq_lens[rr], walk_tok) + bs - 1) >> bs_shift;
+  // ---- tile prefix of the batch, in LDS ------------------------------------
+  // The context tiles of all requests, laid end to end, are cut into S equal
+  // ranges, one per slice; a slice's range may start or end inside a
+  // request and may cover several requests. Its pieces are the segments.
+  for (int rr = threadIdx.x; rr < B; rr += NTHR)
+    s_pref[rr] = (visible_len(p.seq_lens[rr], walk_tok) + kTile - 1) / kTile;
+  if (threadIdx.x == 0) {
+    s_first[0] = 0;
+    s_first[1] = 0;
   }
-  auto blocks_of = [&](int rr) {  // large batches only
-    return rr < B ? (visible_len(p.seq_lens[rr], walk_tok) + bs - 1) >> bs_shift : 0;
-  };
-
-  // ---- chunk size, from the context blocks of the whole batch ------------
-  int64_t ctx_blocks_total = 0;
-  if (in_regs) {
-    int t = 0;
+  __syncthreads();
+  const int per = (B + NTHR - 1) / NTHR;  // contiguous requests per thread
+  const int rb = min((int)threadIdx.x * per, B);
+  const int re = min(rb + per, B);
+  int local = 0;
+  for (int rr = rb; rr < re; ++rr) local += s_pref[rr];
+  const int incl = wave_inclusive_scan(local);
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int total = 0, run = incl - local;
 #pragma unroll
-    for (int k = 0; k < kSlices; ++k) t += nbr[k];
-    ctx_blocks_total = wave_sum(t);
-  } else {
-    for (int base = 0; base < B; base += 64) ctx_blocks_total += wave_sum(blocks_of(base + lane));
+  for (int w = 0; w < NW; ++w) {
+    const int t = s_wave[w];
+    total += t;
+    run += w < wave ? t : 0;
   }
-  int64_t cb64 = (ctx_blocks_total + p.target_pairs - 1) / p.target_pairs;
-  if (cb64 < p.min_chunk_blocks) cb64 = p.min_chunk_blocks;
-  const int cb = uniform((int)cb64);  // blocks per chunk
-  const int chunk_tok = cb << bs_shift;
-  const int walk_chunks = (p.walk_blocks + cb - 1) / cb;
+  // total <= num_seqs * walk_tiles < 2^31 (checked by the host)
+  const int Q = max((total + S - 1) / S, p.min_tiles);  // tiles per slice
+  const int a = (int)min((int64_t)slice * Q, (int64_t)total);
+  const int b = (int)min((int64_t)a + Q, (int64_t)total);
+  // Fixed-shape walk: the columns past each request's context (its padding
+  // tiles) are cut the same way into a second range per slice.
+  const int pad_total = TW ? B * walk_tiles - total : 0;
+  const int Qp = max((pad_total + S - 1) / S, p.min_tiles);
+  const int pa = (int)min((int64_t)slice * Qp, (int64_t)pad_total);
+  const int pbnd = (int)min((int64_t)pa + Qp, (int64_t)pad_total);
+  for (int rr = rb; rr < re; ++rr) {
+    const int n = s_pref[rr];
+    if (run <= a && a < run + n) s_first[0] = rr;
+    if (TW) {
+      const int pr = rr * walk_tiles - run;  // padding tiles before request rr
+      if (pr <= pa && pa < pr + (walk_tiles - n)) s_first[1] = rr;
+    }
+    s_pref[rr] = run;
+    run += n;
+  }
+  if (threadIdx.x == 0) s_pref[B] = total;
+  __syncthreads();
 
   uint32_t sink = 0;
+  const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
+  const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
 
-  for (int64_t uw = blockIdx.x;; uw += gridDim.x) {
-    const int64_t pair = uw / HG;
-    const int hg = (int)(uw - pair * HG);
-
-    // ---- locate (request, chunk) of this pair ----------------------------
-    int r = -1, c = 0;
-    int64_t pidx0 = 0;  // index of (r, chunk 0) among the pairs that hold context
-    if constexpr (!TW) {
-      // pair = (sum of chunk counts of requests before r) + c
-      int64_t carry = 0;
-      auto visit = [&](int base, int nb) {
-        const int C = (nb + cb - 1) / cb;
-        const int incl = wave_inclusive_scan(C, lane);
-        const int tot = __shfl(incl, 63);
-        if (r < 0 && pair < carry + tot) {
-          const uint64_t hit = __ballot(carry + incl > pair);
-          const int src = __builtin_ctzll(hit);
-          const int excl = __shfl(incl - C, src);
-          r = base + src;
-          pidx0 = carry + excl;
-          c = (int)(pair - pidx0);
-        }
-        carry += tot;
-      };
-      if (in_regs) {
-#pragma unroll
-        for (int k = 0; k < kSlices; ++k)
-          if (64 * k < B) visit(64 * k, nbr[k]);
-      } else {
-        for (int base = 0; base < B && r < 0; base += 64) visit(base, blocks_of(base + lane));
+  // Tiles [tok_a, tok_b) (multiples of kTile) of table row trow, through
+  // fn(token of the tile, its loads). Block ids are staged in LDS in pieces
+  // of kStage; a ring of kDepth tile buffers keeps tiles t+1 .. t+kDepth-1
+  // in flight while tile t is used. Loads past the last tile re-load the
+  // last tile (a cache hit), so no load depends on a branch.
+  auto walk_tiles_of = [&](const int32_t* trow, int tok_a, int tok_b, auto&& fn) {
+    const int blk_first = tok_a >> bs_shift;
+    const int blk_end = ((tok_b - 1) >> bs_shift) + 1;
+    for (int pb = blk_first; pb < blk_end; pb += kStage) {
+      const int pn = min(kStage, blk_end - pb);
+      __syncthreads();  // the previous piece is consumed by every wave
+      for (int i = threadIdx.x; i < pn; i += NTHR) {
+        const int col = pb + i;
+        s_blk[i] = col < p.table_stride ? trow[col] : 0;
       }
-    } else if (walk_chunks > 0) {
-      const int64_t rq = pair / walk_chunks;
-      if (rq < B) {
-        r = (int)rq;
-        c = (int)(pair - rq * walk_chunks);
-        int carry = 0;  // chunks holding context of the requests before r
-        if (in_regs) {
+      __syncthreads();
+      const int t_begin = max(tok_a, pb << bs_shift);
+      const int t_end = min(tok_b, (pb + pn) << bs_shift);
+      const int nt = (t_end - t_begin) / kTile;
+
+      // K as the score MFMA's A operand, V in row layout. An inactive
+      // entry reads null block 0 and is masked by the caller.
+      auto load = [&](int tt, TileBuf& bf) {
+        const int bid = uniform(s_blk[(tt >> bs_shift) - pb]);
+        const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
+        const int64_t base = (int64_t)(active ? bid : 0) * block_bytes;
+        const char* kb = (const char*)p.k_cache + base;
+        const char* vb = (const char*)p.v_cache + base;
+        const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
+        bf.bid = active ? bid : 0;
 #pragma unroll
-          for (int k = 0; k < kSlices; ++k)
-            carry += (64 * k + lane < r) ? (nbr[k] + cb - 1) / cb : 0;
-        } else {
-          for (int base = 0; base < r; base += 64)
-            carry += (base + lane < r) ? (blocks_of(base + lane) + cb - 1) / cb : 0;
+        for (int pp = 0; pp < NP; ++pp)
+          bf.k[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const char* src = vb + in_blk + v_lane_off + i * row_bytes;
+          if constexpr (NVW == 2) {
+            const u32x2 x = *(const u32x2*)src;
+            bf.v[i][0] = x[0];
+            bf.v[i][1] = x[1];
+          } else {
+#pragma unroll
+            for (int w = 0; w < NVW; w += 4) {
+              const u32x4 x = *(const u32x4*)(src + w * 4);
+              bf.v[i][w] = x[0];
+              bf.v[i][w + 1] = x[1];
+              bf.v[i][w + 2] = x[2];
+              bf.v[i][w + 3] = x[3];
+            }
+          }
         }
-        pidx0 = wave_sum(carry);
+      };
+      TileBuf bufs[kDepth];
+      auto tile_at = [&](int t) { return t_begin + min(t, nt - 1) * kTile; };
+#pragma unroll
+      for (int s = 0; s < kDepth - 1; ++s) load(tile_at(s), bufs[s]);
+      for (int t = 0; t < nt; t += kDepth) {
+#pragma unroll
+        for (int s = 0; s < kDepth; ++s) {
+          load(tile_at(t + s + kDepth - 1), bufs[(s + kDepth - 1) % kDepth]);
+          if (t + s < nt) fn(t_begin + (t + s) * kTile, bufs[s]);
+        }
       }
     }
-    // The scan leaves these in vector registers; they are the same in every
-    // lane, and saying so keeps the tile loop below under scalar control.
-    r = uniform(r);
-    c = uniform(c);
-    pidx0 = uniform((int)pidx0);  // < target_pairs + num_seqs
-    if (r < 0) break;  // every pair is done (uniform over the workgroup)
+  };
 
-    const int g = hg * NW + wave;
+  // ---- one segment: tiles [t0, t1) of request r (nr tiles from tile pr) --
+  auto segment = [&](int r, int t0, int t1, int nr, int pr) {
     const int L = uniform(p.seq_lens[r]);
     const int E = visible_len(L, walk_tok);
-    const int nb_r = (E + bs - 1) >> bs_shift;
-    const int Cv = (nb_r + cb - 1) / cb;  // chunks of r that hold context
-    const bool pair_valid = c < Cv;
-    const int tok0 = c * chunk_tok;
-    const int tok_valid_end = min(tok0 + chunk_tok, E);
-    const int tok_walk_end = TW ? min(tok0 + chunk_tok, walk_tok) : tok_valid_end;
 
-    // ---- query operand (B operand of the score MFMA) ---------------------
+    // query operand (B operand of the score MFMA)
     const int jrow = rho / G;
     const int hh = rho - jrow * G;
     const int qpos = rho < nrows ? L - Sq + jrow : -1;
@@ -252,232 +304,186 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp) {
         qp[pp] = (u32x4){0u, 0u, 0u, 0u};
-        if (pair_valid && rho < nrows)
-          qp[pp] = *(const u32x4*)(qrow + pp * 64 + jg * 16);
+        if (rho < nrows) qp[pp] = *(const u32x4*)(qrow + pp * 64 + jg * 16);
       }
     }
 
-    // ---- running softmax state of query row rho --------------------------
+    // running softmax state of query row rho
     float m_run = -INFINITY;
     float l_run = 0.0f;  // partial: this lane's tokens only
     f32x4 acc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    const int32_t* trow = p.block_table + (int64_t)r * p.table_stride;
-    const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
-    const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
-
-    const int blk_first = tok0 >> bs_shift;
-    const int blk_end = tok_walk_end > tok0 ? ((tok_walk_end - 1) >> bs_shift) + 1 : blk_first;
-    for (int pb = blk_first; pb < blk_end; pb += kStage) {
-      const int pn = min(kStage, blk_end - pb);
-      __syncthreads();  // the previous piece is consumed by every wave
-      for (int i = threadIdx.x; i < pn; i += NW * 64) {
-        const int col = pb + i;
-        s_blk[i] = col < p.table_stride ? trow[col] : 0;
-      }
-      __syncthreads();
-      const int t_begin = max(tok0, pb << bs_shift);
-      const int t_end = min(tok_walk_end, (pb + pn) << bs_shift);
-      const int nt = (t_end - t_begin + kTile - 1) / kTile;
-
-      // Loads of one tile: K as the score MFMA's A operand, V in row layout.
-      // Always issued: an inactive entry reads null block 0 and is masked.
-      auto load = [&](int tt, TileBuf& b) {
-        const int bid = uniform(s_blk[(tt >> bs_shift) - pb]);
-        const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
-        const int64_t base = (int64_t)(active ? bid : 0) * block_bytes;
-        const char* kb = (const char*)p.k_cache + base;
-        const char* vb = (const char*)p.v_cache + base;
-        const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
-        b.bid = active ? bid : 0;
+    // Scores, online softmax and P.V for one tile whose loads have landed.
+    auto consume = [&](int tt, TileBuf& bf) {
+      const bool active = bf.bid > 0;
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};  // S^T[token 4*jg+i][row rho]
 #pragma unroll
-        for (int pp = 0; pp < NP; ++pp)
-          b.k[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
+      for (int pp = 0; pp < NP; ++pp) {
+        if constexpr (BF16) {
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf.k[pp]),
+                                                      __builtin_bit_cast(bf16x8, qp[pp]), s, 0,
+                                                      0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(bf.k[pp][e]),
+                                                     __uint_as_float(qp[pp][e]), s, 0, 0, 0);
+        }
+      }
+
+      float sx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sx[i] = s[i] * p.scale_log2;
+      const bool full = active && (tt + kTile <= E) && (tt + kTile - 1 <= qpos_min);
+      if (!full) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const char* src = vb + in_blk + v_lane_off + i * row_bytes;
-          if constexpr (NVW == 2) {
-            const u32x2 x = *(const u32x2*)src;
-            b.v[i][0] = x[0]; b.v[i][1] = x[1];
-          } else {
+          const int pos = tt + 4 * jg + i;
+          const bool kv_ok = active && pos < E;
+          if (!(kv_ok && pos <= qpos)) sx[i] = -INFINITY;
+          if (!kv_ok) {
 #pragma unroll
-            for (int w = 0; w < NVW; w += 4) {
-              const u32x4 x = *(const u32x4*)(src + w * 4);
-              b.v[i][w] = x[0]; b.v[i][w + 1] = x[1]; b.v[i][w + 2] = x[2]; b.v[i][w + 3] = x[3];
-            }
+            for (int w = 0; w < NVW; ++w) bf.v[i][w] = kNegZero;
           }
         }
-      };
+      }
 
-      // Scores, online softmax and P.V for one tile whose loads have landed.
-      auto consume = [&](int tt, TileBuf& b) {
-        const bool active = b.bid > 0;
-        if constexpr (TW) {
-          if (!(pair_valid && active && tt < tok_valid_end)) {
-            // Fixed-shape walk past the context: read, never used.
+      // online softmax
+      float mx = fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3]));
+      mx = max_over_groups(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float pr4[4];
 #pragma unroll
-            for (int pp = 0; pp < NP; ++pp)
-              sink ^= b.k[pp][0] ^ b.k[pp][1] ^ b.k[pp][2] ^ b.k[pp][3];
+      for (int i = 0; i < 4; ++i) pr4[i] = __builtin_amdgcn_exp2f(sx[i] - m_use);
+      l_run = l_run * alpha + ((pr4[0] + pr4[1]) + (pr4[2] + pr4[3]));
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int w = 0; w < NVW; ++w) sink ^= b.v[i][w];
-            return;
-          }
-        }
+        for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      }
+      m_run = m_new;
 
-        // ---- scores: S^T[token 4*jg+i][row rho] ----------------------------
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      // O^T += V^T P^T
 #pragma unroll
-        for (int pp = 0; pp < NP; ++pp) {
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          float v;
           if constexpr (BF16) {
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[pp]),
-                                                        __builtin_bit_cast(bf16x8, qp[pp]), s,
-                                                        0, 0, 0);
+            v = (n & 1) ? bf16_hi(bf.v[i][n >> 1]) : bf16_lo(bf.v[i][n >> 1]);
           } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(b.k[pp][e]),
-                                                       __uint_as_float(qp[pp][e]), s, 0, 0, 0);
+            v = __uint_as_float(bf.v[i][n]);
           }
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pr4[i], acc[n], 0, 0, 0);
         }
-
-        float sx[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sx[i] = s[i] * p.scale_log2;
-        const bool full = active && (tt + kTile <= tok_valid_end) && (tt + kTile - 1 <= qpos_min);
-        if (!full) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int pos = tt + 4 * jg + i;
-            const bool kv_ok = active && pos < E;
-            if (!(kv_ok && pos <= qpos)) sx[i] = -INFINITY;
-            if (!kv_ok) {
-#pragma unroll
-              for (int w = 0; w < NVW; ++w) b.v[i][w] = kNegZero;
-            }
-          }
-        }
-
-        // ---- online softmax ------------------------------------------------
-        float mx = fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3]));
-        mx = max_over_groups(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float pr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(sx[i] - m_use);
-        l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-          for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-        }
-        m_run = m_new;
-
-        // ---- O^T += V^T P^T --------------------------------------------------
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            float v;
-            if constexpr (BF16) {
-              v = (n & 1) ? bf16_hi(b.v[i][n >> 1]) : bf16_lo(b.v[i][n >> 1]);
-            } else {
-              v = __uint_as_float(b.v[i][n]);
-            }
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pr[i], acc[n], 0, 0, 0);
-          }
-        }
-      };
-
-      // Two tile buffers: tile t+1 is in flight while tile t is computed.
-      TileBuf b0, b1;
-      load(t_begin, b0);
-      for (int t = 0; t < nt; t += 2) {
-        const int tt = t_begin + t * kTile;
-        load(t + 1 < nt ? tt + kTile : tt, b1);
-        consume(tt, b0);
-        load(t + 2 < nt ? tt + 2 * kTile : tt, b0);
-        if (t + 1 < nt) consume(tt + kTile, b1);
       }
-    }
-
-    if (!pair_valid) continue;
+    };
+    walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, t0 * kTile, t1 * kTile, consume);
 
     // acc[n][i] holds dimension (4*jg + i) * NT + n of query row rho.
     const float l_tot = sum_over_groups(l_run);
     const int d_base = 4 * jg * NT;
-
-    if (c == 0 && g == 0 && lane == 0) {
-      p.chunk_meta[2 * r] = (int32_t)pidx0;  // where request r's partials start
-      p.chunk_meta[2 * r + 1] = Cv;          // read by the merge kernel
+    const bool whole = t0 == 0 && t1 == nr;
+    if (t0 == 0 && hg == 0 && threadIdx.x == 0) {
+      // Request r's partials sit at slots slice + r .. last slice + r.
+      p.chunk_meta[2 * r] = slice + r;
+      p.chunk_meta[2 * r + 1] = whole ? 1 : (pr + nr - 1) / Q - slice + 1;
     }
-
-    if (Cv == 1) {
-      if (rho < nrows) {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        float* o = p.out + (((int64_t)r * Sq + jrow) * Hq + (int64_t)g * G + hh) * D + d_base;
+    if (rho >= nrows) return;
+    if (whole) {
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      float* o = p.out + (((int64_t)r * Sq + jrow) * Hq + (int64_t)g * G + hh) * D + d_base;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int n0 = 0; n0 < NT; n0 += 4) {
-            f32x4 v = {acc[n0][i] * inv, acc[n0 + 1][i] * inv, acc[n0 + 2][i] * inv,
-                       acc[n0 + 3][i] * inv};
-            *(f32x4*)(o + i * NT + n0) = v;
-          }
+        for (int n0 = 0; n0 < NT; n0 += 4) {
+          f32x4 v = {acc[n0][i] * inv, acc[n0 + 1][i] * inv, acc[n0 + 2][i] * inv,
+                     acc[n0 + 3][i] * inv};
+          *(f32x4*)(o + i * NT + n0) = v;
         }
       }
-      continue;
+      return;
     }
-
-    // ---- split-K: publish this chunk's partial ----------------------------
-    const int64_t pidx = pidx0 + c;
-    {
-      float* prow = p.partials + ((pidx * Hkv + g) * nrows + rho) * PSTRIDE;
-      if (rho < nrows) {
+    // split: publish this segment's partial state
+    float* prow = p.partials + ((((int64_t)slice + r) * Hkv + g) * nrows + rho) * PSTRIDE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int n0 = 0; n0 < NT; n0 += 4) {
-            f32x4 v = {acc[n0][i], acc[n0 + 1][i], acc[n0 + 2][i], acc[n0 + 3][i]};
-            *(f32x4*)(prow + d_base + i * NT + n0) = v;
-          }
-        }
-        if (jg == 0) {
-          prow[D] = m_run;
-          prow[D + 1] = l_tot;
-        }
+      for (int n0 = 0; n0 < NT; n0 += 4) {
+        f32x4 v = {acc[n0][i], acc[n0 + 1][i], acc[n0 + 2][i], acc[n0 + 3][i]};
+        *(f32x4*)(prow + d_base + i * NT + n0) = v;
       }
+    }
+    if (jg == 0) {
+      prow[D] = m_run;
+      prow[D + 1] = l_tot;
+    }
+  };
+
+  // ---- this slice's context tiles, request by request ---------------------
+  {
+    int r = uniform(s_first[0]);
+    int pos = a;
+    while (pos < b) {
+      const int pr = uniform(s_pref[r]);
+      const int pn = uniform(s_pref[r + 1]);
+      if (pn > pos) {
+        const int e = min(b, pn);
+        segment(r, pos - pr, e - pr, pn - pr, pr);
+        pos = e;
+      }
+      ++r;
     }
   }
 
   // ---- requests with no visible context produce zeros --------------------
-  {
-    const int row_floats = Sq * Hq * D;
-    for (int r = blockIdx.x; r < B; r += gridDim.x) {
-      if (visible_len(p.seq_lens[r], walk_tok) == 0) {
-        float* o = p.out + (int64_t)r * row_floats;
-        for (int i = threadIdx.x; i < row_floats; i += NW * 64) o[i] = 0.0f;
-        if (threadIdx.x == 0) p.chunk_meta[2 * r + 1] = 0;
-      }
+  for (int r = blockIdx.x; r < B; r += gridDim.x) {
+    if (s_pref[r + 1] == s_pref[r]) {
+      const int row_floats = Sq * Hq * D;
+      float* o = p.out + (int64_t)r * row_floats;
+      for (int i = threadIdx.x; i < row_floats; i += NTHR) o[i] = 0.0f;
+      if (threadIdx.x == 0) p.chunk_meta[2 * r + 1] = 0;
     }
   }
 
+  // ---- fixed-shape walk: read this slice's padding tiles, use none -------
   if constexpr (TW) {
+    auto drain = [&](int, TileBuf& bf) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) sink ^= bf.k[pp][0] ^ bf.k[pp][1] ^ bf.k[pp][2] ^ bf.k[pp][3];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < NVW; ++w) sink ^= bf.v[i][w];
+    };
+    int r = uniform(s_first[1]);
+    int pos = pa;
+    while (pos < pbnd) {
+      const int n = uniform(s_pref[r + 1]) - uniform(s_pref[r]);
+      const int pr = r * walk_tiles - uniform(s_pref[r]);
+      const int pn = pr + (walk_tiles - n);
+      if (pn > pos) {
+        const int e = min(pbnd, pn);
+        walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, (n + pos - pr) * kTile,
+                      (n + e - pr) * kTile, drain);
+        pos = e;
+      }
+      ++r;
+    }
     if (p.flags & kFlagSink) p.out[0] = __uint_as_float(sink);
   }
 }
 
 // Split-K merge: one workgroup per (request, KV head) whose context was
-// split over more than one chunk. Wave w merges chunks w, w + NWC, ... in
+// split over more than one slice. Wave w merges partials w, w + NWC, ... in
 // ascending order; the NWC partial states are then merged in wave order
 // through LDS. The assignment is fixed, so the result is the same on every
 // run and for every walk mode. Lane l of a wave owns output float4s
 // l + 64 k (k < KC) of the (row, dimension) block. Fewer float4s per lane
-// leave room for more waves, so long contexts (many chunks) merge with
+// leave room for more waves, so long contexts (many partials) merge with
 // 16 waves.
 template <int KC>
 struct MergeShape {
@@ -596,26 +602,48 @@ paged_decode_combine_kernel(const DecodeParams p) {
   }
 }
 
+// Pass-1 workgroups of one instantiation that the device holds at once, at
+// the largest LDS the kernel asks for. Queried once per device. The context
+// walk's figure serves both walks, so both cut the batch the same way.
 template <bool BF16, int D, int NW>
-hipError_t launch_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) {
-  const int HG = p.num_kv_heads / NW;
-  // Upper bound on the (request, chunk) pairs, from host-known sizes only:
-  // no request has more than ceil(walk_blocks / min_chunk_blocks) chunks,
-  // and the context walk never has more than target_pairs + num_seqs.
-  const int64_t cpr = (p.walk_blocks + p.min_chunk_blocks - 1) / p.min_chunk_blocks;
-  int64_t pairs = (int64_t)p.num_seqs * (cpr > 0 ? cpr : 1);
-  if (!(p.flags & kFlagWalkTable) && pairs > (int64_t)p.target_pairs + p.num_seqs)
-    pairs = (int64_t)p.target_pairs + p.num_seqs;
-  int64_t grid = pairs * HG;
-  if (grid < 1) grid = 1;
-  if (grid > (1 << 20)) grid = 1 << 20;
+hipError_t resident_workgroups(int* out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && (*out = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, false>), NW * 64,
+      decode_lds_bytes(kDecodeMaxSeqs));
+  if (e != hipSuccess) return e;
+  *out = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  if (cached) cache[dev].store(*out, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
+template <bool BF16, int D, int NW>
+hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t stream) {
+  const int HG = pin.num_kv_heads / NW;
+  int resident = 0;
+  hipError_t e = resident_workgroups<BF16, D, NW>(&resident);
+  if (e != hipSuccess) return e;
+  // One slice per resident workgroup slot (per head group), never more than
+  // the workspace holds partials for.
+  DecodeParams p = pin;
+  p.slices = resident / HG > 1 ? resident / HG : 1;
+  if (p.slices > p.max_slices) p.slices = p.max_slices;
+  const dim3 grid((unsigned)p.slices * (unsigned)HG);
+  const size_t lds = decode_lds_bytes(p.num_seqs);
   if (p.flags & kFlagWalkTable)
-    paged_decode_kernel<BF16, D, NW, true>
-        <<<dim3((unsigned)grid), dim3(NW * 64), 0, stream>>>(p, bs_shift);
+    paged_decode_kernel<BF16, D, NW, true><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
   else
-    paged_decode_kernel<BF16, D, NW, false>
-        <<<dim3((unsigned)grid), dim3(NW * 64), 0, stream>>>(p, bs_shift);
-  hipError_t e = hipGetLastError();
+    paged_decode_kernel<BF16, D, NW, false><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   int64_t cgrid = (int64_t)p.num_seqs * p.num_kv_heads;
   if (cgrid > 65536) cgrid = 65536;
@@ -644,18 +672,15 @@ hipError_t launch_heads(const DecodeParams& p, int bs_shift, hipStream_t stream)
 
 }  // namespace
 
-int32_t decode_target_pairs(int32_t num_kv_heads) {
-  // About 8192 waves of work over the 1024 SIMDs of a 256-CU part, so the
-  // (request, chunk) units spread evenly over the CUs.
+int32_t decode_max_slices(int32_t num_kv_heads) {
+  // Partial storage for up to 8192 waves' worth of slices (a 256-CU part
+  // holds 2048 decode waves at once), so every resident slot gets a slice.
   const int32_t t = 8192 / (num_kv_heads > 0 ? num_kv_heads : 1);
   return t > 16 ? t : 16;
 }
 
-int32_t decode_min_chunk_blocks(int32_t block_size) {
-  // At least 128 tokens per chunk keeps the partial traffic a few percent
-  // of the KV bytes the chunk reads.
-  const int32_t b = 128 / block_size;
-  return b > 1 ? b : 1;
+size_t decode_lds_bytes(int32_t num_seqs) {
+  return ((size_t)num_seqs + 1) * sizeof(int32_t);
 }
 
 size_t decode_meta_bytes(int32_t num_seqs) {
@@ -664,8 +689,10 @@ size_t decode_meta_bytes(int32_t num_seqs) {
 
 size_t decode_partial_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
                             int32_t num_kv_heads, int32_t head_dim) {
-  const size_t pairs = (size_t)decode_target_pairs(num_kv_heads) + (size_t)num_seqs;
-  return pairs * (size_t)num_q_heads * (size_t)q_len * (size_t)(head_dim + 4) * sizeof(float);
+  // Partial slot of (slice, request) is slice + request: every segment of
+  // a slice's range has its own slot, below max_slices + num_seqs.
+  const size_t slots = (size_t)decode_max_slices(num_kv_heads) + (size_t)num_seqs;
+  return slots * (size_t)num_q_heads * (size_t)q_len * (size_t)(head_dim + 4) * sizeof(float);
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, hipStream_t stream) {
