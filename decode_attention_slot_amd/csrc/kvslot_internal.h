@@ -39,6 +39,7 @@ struct DecodeParams {
   int32_t max_slices;  // partial storage bound on the slices (per head group)
   int32_t slices;      // set by the launcher: slices the batch's tiles are cut into
   int32_t min_tiles;   // never cut a slice shorter than this many 16-token tiles
+  int32_t start_tiles;  // units a request start counts for when cutting slices
   float scale_log2;          // softmax scale times log2(e)
   uint32_t flags;
   int is_bf16;

@@ -143,8 +143,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   };
   extern __shared__ int s_pref[];  // [num_seqs + 1]: first tile of each request
   __shared__ int s_blk[kStage];
-  __shared__ int s_wave[NW];
-  __shared__ int s_first[2];  // request holding this slice's first tile (context, padding)
+  __shared__ int s_wave[NW], s_wave_n[NW];
+  // request holding this slice's first unit (context), first padding tile,
+  // and the context tiles of the requests before the latter
+  __shared__ int s_first[3];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -168,51 +170,72 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   const int64_t block_bytes = ((int64_t)Hkv * D * ES) << bs_shift;
   const uint32_t row_bytes = (uint32_t)(Hkv * D * ES);
 
-  // ---- tile prefix of the batch, in LDS ------------------------------------
+  // ---- work prefix of the batch, in LDS ------------------------------------
   // The context tiles of all requests, laid end to end, are cut into S equal
   // ranges, one per slice; a slice's range may start or end inside a
   // request and may cover several requests. Its pieces are the segments.
+  // Each request with context also counts start_tiles units ahead of its
+  // tiles (the cost of starting a segment), so a slice that starts a
+  // request carries that many fewer tiles. s_pref holds these units.
+  const int X = p.start_tiles;
   for (int rr = threadIdx.x; rr < B; rr += NTHR)
     s_pref[rr] = (visible_len(p.seq_lens[rr], walk_tok) + kTile - 1) / kTile;
   if (threadIdx.x == 0) {
     s_first[0] = 0;
     s_first[1] = 0;
+    s_first[2] = 0;
   }
   __syncthreads();
   const int per = (B + NTHR - 1) / NTHR;  // contiguous requests per thread
   const int rb = min((int)threadIdx.x * per, B);
   const int re = min(rb + per, B);
-  int local = 0;
-  for (int rr = rb; rr < re; ++rr) local += s_pref[rr];
+  int local = 0, local_n = 0;  // units and tiles of this thread's requests
+  for (int rr = rb; rr < re; ++rr) {
+    const int n = s_pref[rr];
+    local += n > 0 ? n + X : 0;
+    local_n += n;
+  }
   const int incl = wave_inclusive_scan(local);
-  if (lane == 63) s_wave[wave] = incl;
+  const int incl_n = TW ? wave_inclusive_scan(local_n) : 0;
+  if (lane == 63) {
+    s_wave[wave] = incl;
+    s_wave_n[wave] = incl_n;
+  }
   __syncthreads();
-  int total = 0, run = incl - local;
+  int total = 0, run = incl - local, total_n = 0, run_n = incl_n - local_n;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     const int t = s_wave[w];
+    const int tn = s_wave_n[w];
     total += t;
     run += w < wave ? t : 0;
+    total_n += tn;
+    run_n += w < wave ? tn : 0;
   }
-  // total <= num_seqs * walk_tiles < 2^31 (checked by the host)
-  const int Q = max((total + S - 1) / S, p.min_tiles);  // tiles per slice
+  // total <= num_seqs * (walk_tiles + X) < 2^31 (checked by the host)
+  const int Q = max((total + S - 1) / S, p.min_tiles);  // units per slice
   const int a = (int)min((int64_t)slice * Q, (int64_t)total);
   const int b = (int)min((int64_t)a + Q, (int64_t)total);
   // Fixed-shape walk: the columns past each request's context (its padding
-  // tiles) are cut the same way into a second range per slice.
-  const int pad_total = TW ? B * walk_tiles - total : 0;
+  // tiles) are cut evenly into a second range per slice.
+  const int pad_total = TW ? B * walk_tiles - total_n : 0;
   const int Qp = max((pad_total + S - 1) / S, p.min_tiles);
   const int pa = (int)min((int64_t)slice * Qp, (int64_t)pad_total);
   const int pbnd = (int)min((int64_t)pa + Qp, (int64_t)pad_total);
   for (int rr = rb; rr < re; ++rr) {
     const int n = s_pref[rr];
-    if (run <= a && a < run + n) s_first[0] = rr;
+    const int wu = n > 0 ? n + X : 0;
+    if (run <= a && a < run + wu) s_first[0] = rr;
     if (TW) {
-      const int pr = rr * walk_tiles - run;  // padding tiles before request rr
-      if (pr <= pa && pa < pr + (walk_tiles - n)) s_first[1] = rr;
+      const int pr = rr * walk_tiles - run_n;  // padding tiles before request rr
+      if (pr <= pa && pa < pr + (walk_tiles - n)) {
+        s_first[1] = rr;
+        s_first[2] = run_n;
+      }
     }
     s_pref[rr] = run;
-    run += n;
+    run += wu;
+    run_n += n;
   }
   if (threadIdx.x == 0) s_pref[B] = total;
   __syncthreads();
@@ -287,7 +310,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     }
   };
 
-  // ---- one segment: tiles [t0, t1) of request r (nr tiles from tile pr) --
+  // ---- one segment: tiles [t0, t1) of request r (nr tiles, tile 0 at unit pr) --
   auto segment = [&](int r, int t0, int t1, int nr, int pr) {
     const int L = uniform(p.seq_lens[r]);
     const int E = visible_len(L, walk_tok);
@@ -432,7 +455,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       const int pn = uniform(s_pref[r + 1]);
       if (pn > pos) {
         const int e = min(b, pn);
-        segment(r, pos - pr, e - pr, pn - pr, pr);
+        const int t_base = pr + X;  // unit of r's tile 0
+        const int t0 = max(pos, t_base) - t_base;
+        const int t1 = e - t_base;
+        if (t1 > t0) segment(r, t0, t1, pn - t_base, t_base);
         pos = e;
       }
       ++r;
@@ -460,10 +486,12 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         for (int w = 0; w < NVW; ++w) sink ^= bf.v[i][w];
     };
     int r = uniform(s_first[1]);
+    int tp = uniform(s_first[2]);  // context tiles of the requests before r
     int pos = pa;
     while (pos < pbnd) {
-      const int n = uniform(s_pref[r + 1]) - uniform(s_pref[r]);
-      const int pr = r * walk_tiles - uniform(s_pref[r]);
+      const int wu = uniform(s_pref[r + 1]) - uniform(s_pref[r]);
+      const int n = wu > 0 ? wu - X : 0;
+      const int pr = r * walk_tiles - tp;
       const int pn = pr + (walk_tiles - n);
       if (pn > pos) {
         const int e = min(pbnd, pn);
@@ -471,6 +499,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
                       (n + e - pr) * kTile, drain);
         pos = e;
       }
+      tp += n;
       ++r;
     }
     if (p.flags & kFlagSink) p.out[0] = __uint_as_float(sink);
