@@ -6,7 +6,8 @@ the step's new tokens, then paged_decode_attention. Inputs are seeded and
 synthetic and already resident in HBM when the timed region starts (the
 prior context is prefilled through the library beforehand, untimed).
 HIP events on the launch stream bracket each attention call; the slot
-mapping and cache write kernels are timed after the steps, each in a run of
+mapping and cache write kernels (and their one-launch fusion, which the step
+uses unless --separate-write) are timed after the steps, each in a run of
 back-to-back launches.
 
 The step rotates over several identical copies of the KV cache so that the
@@ -104,6 +105,9 @@ def main(argv=None) -> int:
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="step uses kv_slot_mapping + kv_cache_write (two launches) instead of "
+                         "kv_slot_mapping_cache_write")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run one plain device copy of this size (counter scale)")
     args = ap.parse_args(argv)
@@ -181,14 +185,21 @@ def main(argv=None) -> int:
     t_setup = time.time() - t_setup
 
     f_slot, f_write, f_attn = lib.kv_slot_mapping, lib.kv_cache_write, lib.paged_decode_attention
+    f_fused = lib.kv_slot_mapping_cache_write
+    fused_args = [slot_args[:9] + (step_k.data_ptr(), step_v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                                   w.total_blocks, w.num_kv_heads, w.head_dim, dt, sp)
+                  for kc, vc in caches]
     f_select = K.select_ctx_bucket
 
     def step(i, ev=None):
         # host: the per-step bucket pick the pages describe (feature off unless bucketed)
         f_select(max_ctx, num_spec, buckets, max_model_len, w.block_size)
         j = i % R
-        st = f_slot(*slot_args)
-        st |= f_write(*write_args[j])
+        if args.separate_write:
+            st = f_slot(*slot_args)
+            st |= f_write(*write_args[j])
+        else:
+            st = f_fused(*fused_args[j])
         if ev is not None:
             ev[0].record(stream)
         st |= f_attn(*attn_args[j])
@@ -230,6 +241,7 @@ def main(argv=None) -> int:
 
     t_slot = back_to_back(f_slot, [slot_args], args.steps)
     t_write = back_to_back(f_write, write_args, args.steps)
+    t_fused = back_to_back(f_fused, fused_args, args.steps)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -239,7 +251,10 @@ def main(argv=None) -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    step_bytes = slot_map_bytes(T) + cache_write_bytes(w, T_live, T) + a_bytes
+    write_bytes = cache_write_bytes(w, T_live, T)
+    if not args.separate_write:
+        write_bytes -= 8 * T  # the one-launch write keeps the slots in registers
+    step_bytes = slot_map_bytes(T) + write_bytes + a_bytes
     decode_tokens = w.num_reqs * w.q_len
     attn_gbps = a_bytes / t_attn / 1e9
     result = {
@@ -266,6 +281,7 @@ def main(argv=None) -> int:
             "bucket_len": int(bucket_len),
             "step_tokens": T,
             "cache_copies_rotated": R,
+            "step_write": "separate" if args.separate_write else "fused",
             "parallelism": "single GPU",
         },
         "attention_gbps": round(attn_gbps, 2),
@@ -274,6 +290,7 @@ def main(argv=None) -> int:
         "slot_map_tokens_per_s": round(T / t_slot, 1),
         "kernel_us": {"kv_slot_mapping": round(t_slot * 1e6, 3),
                       "kv_cache_write": round(t_write * 1e6, 3),
+                      "kv_slot_mapping_cache_write": round(t_fused * 1e6, 3),
                       "paged_decode_attention": round(t_attn * 1e6, 3)},
         "algorithmic_bytes": {"kv_slot_mapping": slot_map_bytes(T),
                               "kv_cache_write": cache_write_bytes(w, T_live, T),

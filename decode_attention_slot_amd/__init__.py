@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     kv_cache_write,
     kv_map_to_kernel_blocks,
     kv_slot_mapping,
+    kv_slot_mapping_cache_write,
     load,
     make_workspace,
     paged_decode_attention,

@@ -31,6 +31,7 @@ EXPORTS = (
     "kvs_status_string",
     "kv_slot_mapping",
     "kv_cache_write",
+    "kv_slot_mapping_cache_write",
     "select_ctx_bucket",
     "kv_map_to_kernel_blocks",
     "paged_decode_attention_workspace_bytes",
@@ -64,6 +65,9 @@ def _lib():
         lib.kvs_status_string.restype = ctypes.c_char_p
         lib.kv_slot_mapping.argtypes = [vp, vp, i64, i64, vp, i32, i32, i32, vp, vp]
         lib.kv_cache_write.argtypes = [vp, vp, vp, i64, vp, vp, i64, i32, i32, i32, ctypes.c_int, vp]
+        lib.kv_slot_mapping_cache_write.argtypes = [
+            vp, vp, i64, i64, vp, i32, i32, i32, vp, vp, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp,
+        ]
         lib.select_ctx_bucket.argtypes = [i64, i32, vp, i32, i32, i32, vp, vp]
         lib.kv_map_to_kernel_blocks.argtypes = [vp, i32, i32, i32, i32, vp, i32]
         lib.paged_decode_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -72,7 +76,8 @@ def _lib():
             vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32, i64, f32,
             ctypes.c_int, u32, vp, sz, vp, vp,
         ]
-        for name in ("kv_slot_mapping", "kv_cache_write", "select_ctx_bucket",
+        for name in ("kv_slot_mapping", "kv_cache_write", "kv_slot_mapping_cache_write",
+                     "select_ctx_bucket",
                      "kv_map_to_kernel_blocks", "paged_decode_attention"):
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
@@ -149,6 +154,32 @@ def kv_cache_write(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch
         T, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), int(nb), int(bs), int(hkv), int(d),
         _kvs_dtype(k_cache), _stream(k_cache, stream))
     _check(st, "kv_cache_write")
+
+
+def kv_slot_mapping_cache_write(req_indices: torch.Tensor, positions: torch.Tensor,
+                                block_table: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                slot_mapping: Optional[torch.Tensor] = None,
+                                max_num_tokens: Optional[int] = None, stream=None) -> torch.Tensor:
+    """kv_slot_mapping then kv_cache_write in one launch; returns the slots. See kvslot.h."""
+    nb, bs, hkv, d = k_cache.shape
+    T = int(req_indices.numel())
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(k_new.shape) != (T, hkv, d) \
+            or v_new.shape != k_new.shape or k_new.dtype != k_cache.dtype \
+            or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise ValueError("kv_slot_mapping_cache_write: shape or dtype mismatch")
+    if slot_mapping is None:
+        n = T if max_num_tokens is None else int(max_num_tokens)
+        slot_mapping = torch.empty(n, dtype=torch.int64, device=block_table.device)
+    rows, stride = block_table.shape
+    st = _lib().kv_slot_mapping_cache_write(
+        _dev(req_indices, "req_indices", torch.int32, 1), _dev(positions, "positions", torch.int64, 1),
+        T, int(slot_mapping.numel()), _dev(block_table, "block_table", torch.int32, 2),
+        int(rows), int(stride), int(bs), _dev(slot_mapping, "slot_mapping", torch.int64, 1),
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        int(nb), int(hkv), int(d), _kvs_dtype(k_cache), _stream(k_cache, stream))
+    _check(st, "kv_slot_mapping_cache_write")
+    return slot_mapping
 
 
 def select_ctx_bucket(max_num_computed_tokens: int, num_speculative_tokens: int,

@@ -75,6 +75,32 @@ int kv_cache_write(const void* k_new, const void* v_new, const int64_t* slot_map
                                                (int32_t)row_bytes, (hipStream_t)stream));
 }
 
+int kv_slot_mapping_cache_write(const int32_t* req_indices, const int64_t* positions,
+                                int64_t num_tokens, int64_t max_num_tokens,
+                                const int32_t* block_table, int32_t table_rows,
+                                int32_t table_stride, int32_t block_size, int64_t* slot_mapping,
+                                const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, int64_t total_blocks, int32_t num_kv_heads,
+                                int32_t head_dim, kvs_dtype dtype, void* stream) {
+  if (num_tokens < 0 || max_num_tokens < num_tokens || table_rows < 0 || table_stride < 1 ||
+      block_size < 1 || total_blocks < 1 || num_kv_heads < 1 || head_dim < 1)
+    return KVS_EINVAL;
+  const int es = elem_bytes(dtype);
+  if (!es) return KVS_EUNSUPPORTED;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * es;
+  if (row_bytes % 16 != 0 || row_bytes > INT_MAX) return KVS_EUNSUPPORTED;
+  if (total_blocks > INT64_MAX / block_size) return KVS_EINVAL;
+  if (max_num_tokens > 0 && !slot_mapping) return KVS_EINVAL;
+  if (num_tokens > 0 &&
+      (!req_indices || !positions || !k_new || !v_new || !k_cache || !v_cache))
+    return KVS_EINVAL;
+  if (table_rows > 0 && !block_table) return KVS_EINVAL;
+  return launch_status(kvs::launch_slot_write(
+      req_indices, positions, num_tokens, max_num_tokens, block_table, table_rows, table_stride,
+      block_size, slot_mapping, k_new, v_new, k_cache, v_cache, total_blocks * block_size,
+      (int32_t)row_bytes, (hipStream_t)stream));
+}
+
 int select_ctx_bucket(int64_t max_num_computed_tokens, int32_t num_speculative_tokens,
                       const int32_t* buckets, int32_t num_buckets, int32_t max_model_len,
                       int32_t block_size, int32_t* bucket_len_out, int32_t* walk_blocks_out) {

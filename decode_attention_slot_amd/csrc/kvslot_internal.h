@@ -17,6 +17,13 @@ hipError_t launch_cache_write(const void* k_new, const void* v_new, const int64_
                               int64_t num_tokens, void* k_cache, void* v_cache,
                               int64_t total_slots, int32_t row_bytes, hipStream_t stream);
 
+hipError_t launch_slot_write(const int32_t* req_indices, const int64_t* positions,
+                             int64_t num_tokens, int64_t max_num_tokens,
+                             const int32_t* block_table, int32_t table_rows,
+                             int32_t table_stride, int32_t block_size, int64_t* slot_mapping,
+                             const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             int64_t total_slots, int32_t row_bytes, hipStream_t stream);
+
 // Everything the decode kernel needs; filled and checked by abi.cpp.
 struct DecodeParams {
   const void* q;

@@ -11,6 +11,7 @@
 // One thread per output entry. The vLLM kernel runs one program per request;
 // a flat grid over tokens keeps every lane busy whatever the length mix.
 #include "kvslot_internal.h"
+#include "slot_formula.h"
 
 namespace kvs {
 namespace {
@@ -23,23 +24,10 @@ slot_mapping_kernel(const int32_t* __restrict__ req_indices, const int64_t* __re
                     int64_t* __restrict__ slot_mapping) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < max_num_tokens; t += stride) {
-    int64_t slot = -1;
-    if (t < num_tokens) {
-      const int32_t r = req_indices[t];
-      const int64_t p = positions[t];
-      if (r >= 0 && r < table_rows && p >= 0) {
-        // block_shift >= 0 when block_size is a power of two
-        const int64_t logical_block = block_shift >= 0 ? (p >> block_shift) : p / block_size;
-        if (logical_block < table_stride) {
-          const int32_t block = block_table[(int64_t)r * table_stride + logical_block];
-          if (block > 0) {
-            const int64_t offset = p - logical_block * block_size;
-            slot = (int64_t)block * block_size + offset;
-          }
-        }
-      }
-    }
-    slot_mapping[t] = slot;
+    slot_mapping[t] = t < num_tokens ? token_slot(req_indices[t], positions[t], block_table,
+                                                  table_rows, table_stride, block_size,
+                                                  block_shift)
+                                     : -1;
   }
 }
 

@@ -113,6 +113,34 @@ int kv_cache_write(const void* k_new, const void* v_new, const int64_t* slot_map
                    void* stream);
 
 /*
+ * kv_slot_mapping_cache_write - kv_slot_mapping and kv_cache_write in one
+ * launch ([BKV] "The Core Formula" and "Slot ID -1: Padding Tokens": the
+ * cache write consumes the slot ids as they are computed).
+ *
+ * Writes slot_mapping exactly as kv_slot_mapping does with the same first
+ * nine arguments, and updates the caches exactly as kv_cache_write does
+ * with those slots, k_new, v_new, total_blocks, block_size, num_kv_heads,
+ * head_dim and dtype: the same bytes land in the same places, and
+ * slot_mapping is also the caller's for later use.
+ *
+ *   req_indices, positions, block_table, slot_mapping   as kv_slot_mapping
+ *   k_new, v_new      [num_tokens][num_kv_heads][head_dim] of dtype, device
+ *   k_cache, v_cache  cache layout above, device, updated in place
+ * Two tokens with one slot is a caller error (which row lands is
+ * unspecified). k_new / v_new must not overlap the caches or slot_mapping.
+ * Errors: KVS_EINVAL for null pointers (when the matching size is > 0) and
+ * every size kv_slot_mapping or kv_cache_write rejects; KVS_EUNSUPPORTED
+ * when a row is not a multiple of 16 bytes or dtype is unknown.
+ */
+int kv_slot_mapping_cache_write(const int32_t* req_indices, const int64_t* positions,
+                                int64_t num_tokens, int64_t max_num_tokens,
+                                const int32_t* block_table, int32_t table_rows,
+                                int32_t table_stride, int32_t block_size, int64_t* slot_mapping,
+                                const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, int64_t total_blocks, int32_t num_kv_heads,
+                                int32_t head_dim, kvs_dtype dtype, void* stream);
+
+/*
  * select_ctx_bucket - per-step decode context bucket ([CLB] "Per-step
  * bucket selection", "Validation", "Block-table head-trim vs. SWA
  * tail-trim", "Backwards compatibility"). Host only; pointers are host

@@ -117,6 +117,17 @@ def test_gpu_entry_points_reject_bad_scalars(K):
     assert lib.kv_cache_write(null, null, null, 1, null, null, 4, 16, 1, 64, 1, null) == -1
     assert lib.kv_cache_write(null, null, null, 0, null, null, 4, 16, 1, 64, 1, null) == 0
 
+    # kv_slot_mapping_cache_write: the union of both checks
+    def smw(T=1, M=1, rows=0, stride=1, bs=16, nb=4, hkv=1, d=64, dtype=1):
+        return lib.kv_slot_mapping_cache_write(null, null, T, M, null, rows, stride, bs, null, null,
+                                               null, null, null, nb, hkv, d, dtype, null)
+
+    assert smw(T=-1) == -1 and smw(T=5, M=4) == -1 and smw(stride=0) == -1 and smw(bs=0) == -1
+    assert smw(nb=0) == -1 and smw(hkv=0) == -1
+    assert smw(dtype=7) == -2 and smw(d=2) == -2   # dtype; row of 4 bytes
+    assert smw() == -1                             # null pointers
+    assert smw(T=0, M=0) == 0                      # nothing to do
+
     def pda(**kw):
         a = dict(q=null, k=null, v=null, bt=null, stride=4, walk=4, sl=null, B=1, sq=1, hq=8, hkv=2,
                  d=128, bs=64, nb=10, scale=0.1, dtype=1, flags=0, ws=null, wsb=1 << 30, out=null)

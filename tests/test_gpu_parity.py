@@ -367,6 +367,76 @@ def test_cache_write_image_vs_oracle(cuda, dtype):
     assert np.array_equal(host_bits(dkc), bits(kc)) and np.array_equal(host_bits(dvc), bits(vc))
 
 
+@pytest.mark.parametrize("bs,dtype", [(16, "bf16"), (64, "f32"), (3, "bf16")])
+def test_fused_slot_write_vs_oracle(cuda, bs, dtype):
+    """One-launch slot mapping + write: slots and byte images equal the oracle's
+    composition and the two-launch path, bit for bit (pads, inactive entries,
+    rows and columns outside the table, slots past the cache, the -1 tail)."""
+    rng = np.random.default_rng(100 + bs)
+    rows, width, T, hkv, d = 6, 7, 700, 2, 64
+    total = rows * width - 9  # the largest block ids fall outside the cache: skipped
+    table = rng.permutation(np.arange(1, rows * width + 1)).reshape(rows, width).astype(np.int32)
+    kill = rng.random((rows, width))
+    table = np.where(kill < 0.2, -1, np.where(kill < 0.3, 0, table)).astype(np.int32)
+    # request indices -1 (padding) .. rows (outside the table), each with
+    # distinct positions (some negative, some past the table), so no two
+    # tokens share a slot
+    per = min(T // 8, (width + 2) * bs + 3)
+    T = 8 * per
+    pos = np.concatenate([rng.permutation(np.arange(-3, (width + 2) * bs))[:per]
+                          for _ in range(8)]).astype(np.int64)
+    req = np.repeat(np.arange(-1, rows + 1), per).astype(np.int32)
+    wl = W.Workload(name="", index=0, seed=0, dtype=dtype, block_size=bs, total_blocks=total,
+                    num_kv_heads=hkv, num_q_heads=hkv, head_dim=d, q_len=1, num_reqs=0,
+                    computed=None, chunk_lens=None, seq_lens=np.zeros(1), block_table=None)
+    knew = W.to_storage(rng.standard_normal((T, hkv, d)).astype(np.float32), dtype)
+    vnew = W.to_storage(rng.standard_normal((T, hkv, d)).astype(np.float32), dtype)
+    M = T + 77
+    want_slots = O.compute_slot_mapping(req, pos, table, bs, M)
+    kc, vc = wl.canary_cache(), wl.canary_cache()
+    O.reshape_and_cache(knew, vnew, want_slots[:T], kc, vc)
+
+    d_req, d_pos = torch.from_numpy(req).to(cuda), torch.from_numpy(pos).to(cuda)
+    d_tab = torch.from_numpy(table).to(cuda)
+    d_k, d_v = dev.upload_storage(knew, dtype, cuda), dev.upload_storage(vnew, dtype, cuda)
+    fkc, fvc = dev.canary_cache(wl, cuda), dev.canary_cache(wl, cuda)
+    got = K.kv_slot_mapping_cache_write(d_req, d_pos, d_tab, d_k, d_v, fkc, fvc, max_num_tokens=M)
+    skc, svc = dev.canary_cache(wl, cuda), dev.canary_cache(wl, cuda)
+    two = K.kv_slot_mapping(d_req, d_pos, d_tab, bs, max_num_tokens=M)
+    K.kv_cache_write(d_k, d_v, two, skc, svc)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), want_slots)
+    assert np.array_equal(host_bits(fkc), bits(kc)) and np.array_equal(host_bits(fvc), bits(vc))
+    assert torch.equal(got, two)
+    assert torch.equal(fkc.view(torch.uint8), skc.view(torch.uint8))
+    assert torch.equal(fvc.view(torch.uint8), svc.view(torch.uint8))
+
+
+@pytest.mark.parametrize("index", [0, 4])
+def test_fused_step_vs_oracle(cuda, index):
+    """A whole step through the one-launch write (ragged chunk + decode tokens)."""
+    w = W.make_workload(index)
+    s = dev.build(w, cuda)
+    ref = OracleStep(w, s.host_table)
+    slots, out = dev.run_step(s, fused=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(), ref.write_step())
+    assert np.array_equal(host_bits(s.k_cache), bits(ref.k_cache))
+    assert np.array_equal(host_bits(s.v_cache), bits(ref.v_cache))
+    assert max_err(out, ref.attention(w.q())) <= TOL[w.dtype]
+
+
+def test_fused_slot_write_empty(cuda):
+    kc = torch.zeros((2, 16, 1, 64), dtype=torch.bfloat16, device=cuda)
+    e32 = torch.zeros(0, dtype=torch.int32, device=cuda)
+    e64 = torch.zeros(0, dtype=torch.int64, device=cuda)
+    ek = torch.zeros((0, 1, 64), dtype=torch.bfloat16, device=cuda)
+    bt = torch.ones((1, 1), dtype=torch.int32, device=cuda)
+    s = K.kv_slot_mapping_cache_write(e32, e64, bt, ek, ek, kc, kc, max_num_tokens=5)
+    torch.cuda.synchronize()
+    assert s.cpu().tolist() == [-1] * 5 and not kc.float().abs().sum().item()
+
+
 def test_unsupported_shapes_raise(cuda):
     c = small_case(cuda, 1, [10], 16, 1, 1, 1, 64, "bf16")
     q96 = torch.zeros((1, 1, 1, 96), dtype=torch.bfloat16, device=cuda)

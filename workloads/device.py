@@ -172,18 +172,24 @@ def build(w: Workload, device="cuda", threads: int = 8, batch_tokens: int = 1 <<
 
 
 def run_step(s: DeviceStep, walk_blocks: Optional[int] = None, flags: int = 0, workspace=None,
-             out=None, slots_out=None):
+             out=None, slots_out=None, fused: bool = False):
     """One step on the device: slot map + write of the step's tokens, then attention.
 
-    Returns (slot_mapping of the step tokens, attention output).
+    fused: one kv_slot_mapping_cache_write launch instead of kv_slot_mapping
+    followed by kv_cache_write. Returns (slot_mapping of the step tokens,
+    attention output).
     """
     w = s.w
     req = torch.cat([s.chunk_req, s.dec_req])
     pos = torch.cat([s.chunk_pos, s.dec_pos])
     k = torch.cat([s.chunk_k, s.dec_k])
     v = torch.cat([s.chunk_v, s.dec_v])
-    slots = K.kv_slot_mapping(req, pos, s.block_table, w.block_size, slot_mapping=slots_out)
-    K.kv_cache_write(k, v, slots, s.k_cache, s.v_cache)
+    if fused:
+        slots = K.kv_slot_mapping_cache_write(req, pos, s.block_table, k, v, s.k_cache, s.v_cache,
+                                              slot_mapping=slots_out)
+    else:
+        slots = K.kv_slot_mapping(req, pos, s.block_table, w.block_size, slot_mapping=slots_out)
+        K.kv_cache_write(k, v, slots, s.k_cache, s.v_cache)
     o = K.paged_decode_attention(s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens, w.scale,
                                  walk_blocks=walk_blocks, flags=flags, workspace=workspace, out=out)
     return slots, o
