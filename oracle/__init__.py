@@ -17,6 +17,7 @@ from .kvslot_oracle import (  # noqa: F401
     reshape_and_cache,
     select_ctx_bucket,
     smallest_bucket_at_least,
+    swa_tail_trim,
     validate_buckets,
     widen,
 )

@@ -134,7 +134,7 @@ def widen(x, dtype: str) -> np.ndarray:
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, walk_blocks, scale,
-                           dtype, requests=None):
+                           dtype, requests=None, window=0, kv_pos_offset=None):
     """GQA decode attention over the paged cache, fp64; out [B, S_q, Hq, D].
 
     For request r with context length L = seq_lens[r] (the step's S_q new
@@ -156,10 +156,21 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, walk_bloc
     * a request with L <= 0 (a padded row) or a query with no visible key
       yields zeros.
 
-    The key of position p is ``k_cache[block_table[r, p // bs], p % bs, g]``
-    ([BKV] "Block Table"); scores are ``scale * <q, k>``; the output is the
-    softmax-weighted sum of the values (max subtracted before exp).
-    ``requests`` limits the computation to a subset of rows (others zero).
+    Sliding window ([KVC] "Attention Type": a sliding-window layer keeps only
+    the recent tokens within the window; [CLB] "Block-table head-trim vs.
+    SWA tail-trim"): with ``window`` > 0 the query at position qpos sees only
+    keys at positions qpos - window + 1 .. qpos (the window counts the query's
+    own position). With ``kv_pos_offset`` given, column c of request r's
+    table row holds the block of absolute positions kv_pos_offset[r] + c * bs
+    onward (the tail-trimmed frame; positions stay absolute); only positions
+    from kv_pos_offset[r] up to kv_pos_offset[r] + walk_blocks * bs are
+    visible.
+
+    The key of position p is ``k_cache[block_table[r, (p - offset) // bs],
+    p % bs, g]`` ([BKV] "Block Table"); scores are ``scale * <q, k>``; the
+    output is the softmax-weighted sum of the values (max subtracted before
+    exp). ``requests`` limits the computation to a subset of rows (others
+    zero).
     """
     q64 = widen(q, dtype)
     B, S_q, Hq, D = q64.shape
@@ -173,9 +184,11 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, walk_bloc
         L = int(seq_lens[r])
         if L <= 0:
             continue
-        visible = min(L, int(walk_blocks) * bs)
-        positions = np.arange(visible)
-        blocks = table[r, positions // bs]
+        off = 0 if kv_pos_offset is None else int(kv_pos_offset[r])
+        assert off >= 0 and off % bs == 0
+        visible_end = min(L, off + int(walk_blocks) * bs)
+        positions = np.arange(off, max(visible_end, off))
+        blocks = table[r, (positions - off) // bs]
         active = blocks > 0
         positions, blocks = positions[active], blocks[active]
         K = widen(k_cache[blocks, positions % bs], dtype)  # [n, Hkv, D]
@@ -183,6 +196,8 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, walk_bloc
         for j in range(S_q):
             qpos = L - S_q + j
             seen = positions <= qpos
+            if window > 0:
+                seen &= positions >= qpos - window + 1
             if not seen.any():
                 continue
             Kj, Vj = K[seen], V[seen]
@@ -192,6 +207,37 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, walk_bloc
                 p = np.exp(s - s.max())
                 out[r, j, h] = (p @ Vj[:, g, :]) / p.sum()
     return out
+
+
+def swa_tail_trim(block_table, seq_lens, q_len, window, block_size):
+    """Tail-trim a block table for a sliding-window layer; host only.
+
+    [CLB] "Block-table head-trim vs. SWA tail-trim": a sliding-window layer
+    keeps only the last blocks of each request and passes the position of
+    the first kept block (swa_kv_pos_offset) so that positions stay
+    absolute. Reading: the kept width is the number of blocks any window of
+    this step can touch, ceil((window + q_len - 1) / bs) + 1 (the step's
+    q_len queries need keys from L - q_len - window + 1 to L - 1, at any
+    alignment; the page's window / block_size assumes one query and an
+    aligned window), capped at the table width. Request r keeps the
+    columns ending at its last context block (L - 1) // bs, starting no
+    earlier than column 0; kept columns past the source table read -1.
+    Returns (trimmed table [rows, width] int32, offsets [rows] int32).
+    """
+    t = np.asarray(block_table, dtype=np.int64)
+    rows, src_w = t.shape
+    width = min(src_w, -(-(window + q_len - 1) // block_size) + 1)
+    out = np.full((rows, width), PAD_SLOT_ID, dtype=np.int64)
+    offsets = np.zeros(rows, dtype=np.int64)
+    for r in range(rows):
+        L = int(seq_lens[r])
+        last = (L - 1) // block_size if L > 0 else 0
+        first = max(0, last - width + 1)
+        offsets[r] = first * block_size
+        for c in range(width):
+            if first + c < src_w:
+                out[r, c] = t[r, first + c]
+    return out.astype(np.int32), offsets.astype(np.int32)
 
 
 # ---------------------------------------------------------------------------

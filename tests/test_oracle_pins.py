@@ -66,11 +66,12 @@ def random_tables(rng, rows, width, lens, block_size, total_blocks, fill=-1):
     return table
 
 
-def sdpa_reference(q64, K, V, L, S_q, scale, G):
+def sdpa_reference(q64, K, V, L, S_q, scale, G, window=0):
     """torch's scaled_dot_product_attention (fp64, CPU) on contiguous keys.
 
     q64 [S_q, Hq, D]; K, V [n, Hkv, D] fp64 contiguous; query j sits at
-    position L - S_q + j and sees keys at positions <= its own.
+    position L - S_q + j and sees keys at positions <= its own (and, with a
+    window, above its own minus the window).
     """
     n = K.shape[0]
     qt = torch.from_numpy(q64).permute(1, 0, 2).unsqueeze(0)  # [1, Hq, S_q, D]
@@ -78,6 +79,8 @@ def sdpa_reference(q64, K, V, L, S_q, scale, G):
     vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
     qpos = torch.arange(S_q) + (L - S_q)
     mask = torch.arange(n)[None, :] <= qpos[:, None]  # [S_q, n]
+    if window > 0:
+        mask &= torch.arange(n)[None, :] > qpos[:, None] - window
     o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
     return o[0].permute(1, 0, 2).numpy()  # [S_q, Hq, D]
 
@@ -349,6 +352,79 @@ def test_attention_head_trim_sees_only_walked_blocks():
     want = sdpa_reference(O.widen(c["q"][0], "f32"), O.widen(c["ks"][0][:32], "f32"),
                           O.widen(c["vs"][0][:32], "f32"), 32, 1, 0.4, G)
     np.testing.assert_allclose(out[0], want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# sliding window and the SWA tail trim
+# ---------------------------------------------------------------------------
+def test_window_of_one_returns_each_querys_own_value():
+    rng = np.random.default_rng(11)
+    c = paged_case(rng, [40, 9], bs=16, Hkv=2, G=2, D=8, S_q=3)
+    out = O.paged_decode_attention(c["q"], c["kc"], c["vc"], c["table"], c["lens"], c["width"],
+                                   0.7, "f32", window=1)
+    for r, L in enumerate([40, 9]):
+        for j in range(3):
+            for h in range(4):
+                np.testing.assert_array_equal(out[r, j, h],
+                                              c["vs"][r][L - 3 + j, h // 2].astype(np.float64))
+
+
+@settings(max_examples=25, deadline=None)
+@given(seed=st.integers(0, 2**31 - 1), bs=st.sampled_from([1, 16, 64]), G=st.sampled_from([1, 4]),
+       S_q=st.integers(1, 4), window=st.integers(1, 120), dtype=st.sampled_from(["f32", "bf16"]))
+def test_window_matches_sdpa_band_mask(seed, bs, G, S_q, window, dtype):
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(S_q, 150, size=3)]
+    D = 16
+    c = paged_case(rng, lens, bs, 1, G, D, S_q, dtype)
+    out = O.paged_decode_attention(c["q"], c["kc"], c["vc"], c["table"], c["lens"], c["width"],
+                                   0.25, dtype, window=window)
+    for r, L in enumerate(lens):
+        want = sdpa_reference(O.widen(c["q"][r], dtype), O.widen(c["ks"][r], dtype),
+                              O.widen(c["vs"][r], dtype), L, S_q, 0.25, G, window=window)
+        np.testing.assert_allclose(out[r], want, rtol=0, atol=1e-12)
+
+
+def test_window_wider_than_context_is_full_attention():
+    rng = np.random.default_rng(12)
+    c = paged_case(rng, [33, 70], bs=16, Hkv=1, G=2, D=8, S_q=2)
+    args = (c["q"], c["kc"], c["vc"], c["table"], c["lens"], c["width"], 0.3, "f32")
+    np.testing.assert_array_equal(O.paged_decode_attention(*args, window=70),
+                                  O.paged_decode_attention(*args))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tail_trim_keeps_every_position_a_window_needs(seed):
+    rng = np.random.default_rng(seed)
+    bs = int(rng.choice([16, 32, 64]))
+    q_len, window = int(rng.integers(1, 5)), int(rng.integers(1, 300))
+    lens = [int(x) for x in rng.integers(-2, 900, size=7)]
+    src_w = max(-(-max(L, 1) // bs) for L in lens) + 2
+    table = rng.permutation(np.arange(1, 7 * src_w + 1)).reshape(7, src_w).astype(np.int32)
+    trimmed, off = O.swa_tail_trim(table, lens, q_len, window, bs)
+    width = trimmed.shape[1]
+    assert width == min(src_w, -(-(window + q_len - 1) // bs) + 1)
+    for r, L in enumerate(lens):
+        assert off[r] % bs == 0 and off[r] >= 0
+        if L <= 0:
+            continue
+        assert (L - 1) // bs < off[r] // bs + width  # the last context block is kept
+        for p in range(max(0, L - q_len - window + 1), L):  # every key any query sees
+            assert p >= off[r]
+            assert trimmed[r, (p - off[r]) // bs] == table[r, p // bs]
+
+
+def test_tail_trimmed_frame_equals_full_table_with_window():
+    rng = np.random.default_rng(13)
+    lens, bs, S_q, window = [300, 17, 129, 64], 16, 2, 50
+    c = paged_case(rng, lens, bs, 2, 2, 8, S_q)
+    full = O.paged_decode_attention(c["q"], c["kc"], c["vc"], c["table"], c["lens"], c["width"],
+                                    0.3, "f32", window=window)
+    trimmed, off = O.swa_tail_trim(c["table"], c["lens"], S_q, window, bs)
+    got = O.paged_decode_attention(c["q"], c["kc"], c["vc"], trimmed, c["lens"], trimmed.shape[1],
+                                   0.3, "f32", window=window, kv_pos_offset=off)
+    np.testing.assert_array_equal(got, full)
+    assert trimmed.shape[1] == 5 and off.tolist() == [224, 0, 64, 0]
 
 
 def test_bf16_widening_matches_torch():
