@@ -79,6 +79,29 @@ def attention_bytes(w, walk_blocks: int, table_walk: bool) -> int:
     return blocks * per_block + q_out + 4 * w.num_rows
 
 
+def window_attention_bytes(w, window: int, kv_off, width: int) -> int:
+    """Algorithmic bytes of one sliding-window launch over a tail-trimmed table.
+
+    Per request: the whole blocks holding the keys some query of the step
+    sees (positions L - S_q - window + 1 .. L - 1, within the trimmed
+    columns), plus a table entry each; q in, fp32 out, seq_len and offset.
+    """
+    per_block = 2 * w.block_size * w.num_kv_heads * w.head_dim * w.es + 4
+    bs = w.block_size
+    blocks = 0
+    for r in range(w.num_rows):
+        L = int(w.seq_lens[r])
+        if L <= 0:
+            continue
+        off = int(kv_off[r])
+        end = min(L, off + width * bs)
+        start = max(off, L - w.q_len - window + 1)
+        if end > start:
+            blocks += -(-end // bs) - start // bs
+    q_out = w.num_rows * w.q_len * w.num_q_heads * w.head_dim * (w.es + 4)
+    return blocks * per_block + q_out + 8 * w.num_rows
+
+
 def slot_map_bytes(T: int) -> int:
     """24 bytes per token: request index, position, table entry, slot."""
     return 24 * T
@@ -105,6 +128,9 @@ def main(argv=None) -> int:
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window layer: attend over a tail-trimmed table with this window "
+                         "(paged_decode_attention_swa); the trim is host metadata built untimed")
     ap.add_argument("--separate-write", action="store_true",
                     help="step uses kv_slot_mapping + kv_cache_write (two launches) instead of "
                          "kv_slot_mapping_cache_write")
@@ -155,6 +181,15 @@ def main(argv=None) -> int:
     T = int(step_req.numel())
     T_live = int((step_req >= 0).sum().item())
     a_bytes = attention_bytes(w, walk_blocks, table_walk)
+    if args.window:
+        if table_walk:
+            raise SystemExit("--window takes the context walk")
+        lens_h = w.seq_lens[: w.num_rows].astype(np.int32)
+        trimmed, kv_off = K.kv_swa_tail_trim(s.host_table, lens_h, w.q_len, args.window,
+                                             w.block_size)
+        d_trim = torch.from_numpy(trimmed).to(cuda)
+        d_off = torch.from_numpy(kv_off).to(cuda)
+        a_bytes = window_attention_bytes(w, args.window, kv_off, trimmed.shape[1])
     kv_bytes_touched = a_bytes
     if args.rotate > 0:
         R = args.rotate
@@ -177,14 +212,25 @@ def main(argv=None) -> int:
     write_args = [(step_k.data_ptr(), step_v.data_ptr(), slots.data_ptr(), T, kc.data_ptr(),
                    vc.data_ptr(), w.total_blocks, w.block_size, w.num_kv_heads, w.head_dim, dt, sp)
                   for kc, vc in caches]
-    attn_args = [(s.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), s.block_table.data_ptr(), int(stride),
-                  int(walk_blocks), s.seq_lens.data_ptr(), w.num_rows, w.q_len, w.num_q_heads,
-                  w.num_kv_heads, w.head_dim, w.block_size, w.total_blocks, w.scale, dt, flags,
-                  ws.data_ptr(), int(ws.numel()), out.data_ptr(), sp) for kc, vc in caches]
+    if args.window:
+        f_attn = lib.paged_decode_attention_swa
+        wt = int(trimmed.shape[1])
+        attn_args = [(s.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), d_trim.data_ptr(), wt, wt,
+                      s.seq_lens.data_ptr(), d_off.data_ptr(), int(args.window), w.num_rows, w.q_len,
+                      w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.total_blocks,
+                      w.scale, dt, ws.data_ptr(), int(ws.numel()), out.data_ptr(), sp)
+                     for kc, vc in caches]
+    else:
+        f_attn = lib.paged_decode_attention
+        attn_args = [(s.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), s.block_table.data_ptr(),
+                      int(stride), int(walk_blocks), s.seq_lens.data_ptr(), w.num_rows, w.q_len,
+                      w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.total_blocks,
+                      w.scale, dt, flags, ws.data_ptr(), int(ws.numel()), out.data_ptr(), sp)
+                     for kc, vc in caches]
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
-    f_slot, f_write, f_attn = lib.kv_slot_mapping, lib.kv_cache_write, lib.paged_decode_attention
+    f_slot, f_write = lib.kv_slot_mapping, lib.kv_cache_write
     f_fused = lib.kv_slot_mapping_cache_write
     fused_args = [slot_args[:9] + (step_k.data_ptr(), step_v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
                                    w.total_blocks, w.num_kv_heads, w.head_dim, dt, sp)
@@ -276,7 +322,7 @@ def main(argv=None) -> int:
             "max_ctx": int((w.computed + w.chunk_lens)[: w.num_reqs].max()),
             "num_seqs": w.num_rows,
             "q_len": w.q_len,
-            "walk": args.walk,
+            "walk": f"window {args.window} (tail-trimmed table)" if args.window else args.walk,
             "walk_blocks": int(walk_blocks),
             "bucket_len": int(bucket_len),
             "step_tokens": T,
@@ -302,12 +348,14 @@ def main(argv=None) -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(args.workload, args.walk),
+            "traffic": measured_traffic(args.workload,
+                                        f"window{args.window}" if args.window else args.walk),
         },
         "setup_s": round(t_setup, 2),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, s.host_table, walk_blocks, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, s.host_table, walk_blocks, args.cpu_seconds,
+                                              window=args.window)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -329,7 +377,7 @@ def measured_traffic(workload: str, walk: str):
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, table, walk_blocks, seconds):
+def cpu_baseline(w, table, walk_blocks, seconds, window=0):
     """The oracle as it stands, on the host cores, over a bounded sample.
 
     Untimed: the oracle builds its own caches (prefill + step writes). Timed:
@@ -354,9 +402,11 @@ def cpu_baseline(w, table, walk_blocks, seconds):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < seconds:
             rr = real[r % len(real)]
-            ref.attention(q, walk_blocks=walk_blocks, requests=[rr])
-            vis = min(int(w.seq_lens[rr]), walk_blocks * w.block_size)
-            done_bytes += -(-vis // w.block_size) * per_block + per_req_fixed
+            ref.attention(q, walk_blocks=walk_blocks, requests=[rr], window=window)
+            L = int(w.seq_lens[rr])
+            vis = min(L, walk_blocks * w.block_size)
+            first = max(0, L - w.q_len - window + 1) // w.block_size if window else 0
+            done_bytes += (-(-vis // w.block_size) - first) * per_block + per_req_fixed
             n += 1
             r += 1
         el = time.perf_counter() - t0

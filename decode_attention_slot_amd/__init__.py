@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     load,
     make_workspace,
     paged_decode_attention,
+    paged_decode_attention_swa,
+    kv_swa_tail_trim,
     paged_decode_attention_workspace_bytes,
     select_ctx_bucket,
 )

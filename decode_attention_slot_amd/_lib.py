@@ -36,6 +36,8 @@ EXPORTS = (
     "kv_map_to_kernel_blocks",
     "paged_decode_attention_workspace_bytes",
     "paged_decode_attention",
+    "paged_decode_attention_swa",
+    "kv_swa_tail_trim",
 )
 
 
@@ -76,9 +78,14 @@ def _lib():
             vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32, i64, f32,
             ctypes.c_int, u32, vp, sz, vp, vp,
         ]
+        lib.paged_decode_attention_swa.argtypes = [
+            vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, f32,
+            ctypes.c_int, vp, sz, vp, vp,
+        ]
+        lib.kv_swa_tail_trim.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, i32, vp, vp]
         for name in ("kv_slot_mapping", "kv_cache_write", "kv_slot_mapping_cache_write",
-                     "select_ctx_bucket",
-                     "kv_map_to_kernel_blocks", "paged_decode_attention"):
+                     "select_ctx_bucket", "kv_map_to_kernel_blocks", "paged_decode_attention",
+                     "paged_decode_attention_swa", "kv_swa_tail_trim"):
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -259,3 +266,56 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         _dev(out, "out", torch.float32), _stream(q, stream))
     _check(st, "paged_decode_attention")
     return out
+
+
+def paged_decode_attention_swa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                               sliding_window: int, kv_pos_offset: Optional[torch.Tensor] = None,
+                               walk_blocks: Optional[int] = None,
+                               workspace: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Sliding-window decode attention over a (tail-trimmed) table; see kvslot.h."""
+    B, Sq, Hq, D = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != D or q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype \
+            or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("paged_decode_attention_swa: shape or dtype mismatch")
+    if block_table.shape[0] < B or seq_lens.numel() < B or \
+            (kv_pos_offset is not None and kv_pos_offset.numel() < B):
+        raise ValueError("paged_decode_attention_swa: too few rows")
+    stride = int(block_table.shape[1])
+    walk = stride if walk_blocks is None else int(walk_blocks)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(B, Sq, Hq, hkv, D, q.device)
+    off = None if kv_pos_offset is None else _dev(kv_pos_offset, "kv_pos_offset", torch.int32, 1)
+    st = _lib().paged_decode_attention_swa(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table", torch.int32, 2), stride, walk,
+        _dev(seq_lens, "seq_lens", torch.int32), off, int(sliding_window), int(B), int(Sq), int(Hq),
+        int(hkv), int(D), int(bs), int(nb), float(scale), _kvs_dtype(k_cache),
+        _dev(workspace, "workspace", torch.uint8), int(workspace.numel()),
+        _dev(out, "out", torch.float32), _stream(q, stream))
+    _check(st, "paged_decode_attention_swa")
+    return out
+
+
+def kv_swa_tail_trim(block_table: np.ndarray, seq_lens, q_len: int, sliding_window: int,
+                     block_size: int):
+    """Tail-trim a host block table for a sliding-window layer; see kvslot.h.
+
+    Returns (trimmed table [rows, width] int32, kv_pos_offset [rows] int32).
+    """
+    src = np.ascontiguousarray(block_table, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    rows, width = src.shape
+    w = ctypes.c_int32()
+    cap = max(width, 1)
+    dst = np.empty((rows, cap), dtype=np.int32)
+    off = np.empty(rows, dtype=np.int32)
+    st = _lib().kv_swa_tail_trim(src.ctypes.data, int(rows), int(width), lens.ctypes.data,
+                                 int(q_len), int(sliding_window), int(block_size), dst.ctypes.data,
+                                 int(cap), off.ctypes.data, ctypes.byref(w))
+    _check(st, "kv_swa_tail_trim")
+    return np.ascontiguousarray(dst[:, : w.value]), off

@@ -26,6 +26,68 @@ constexpr int kMaxSeqs = kvs::kDecodeMaxSeqs;
 
 }  // namespace
 
+namespace {
+
+int decode_common(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_table, int32_t table_stride, int32_t walk_blocks,
+                  const int32_t* seq_lens, const int32_t* kv_pos_offset, int32_t window,
+                  int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int64_t total_blocks, float scale,
+                  kvs_dtype dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                  float* out, void* stream) {
+  if (num_seqs < 0 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      block_size < 1 || table_stride < 1 || walk_blocks < 0 || walk_blocks > table_stride ||
+      total_blocks < 1 || !isfinite(scale) || window < 0)
+    return KVS_EINVAL;
+  if (num_q_heads % num_kv_heads != 0) return KVS_EINVAL;
+  if (flags & ~KVS_WALK_TABLE) return KVS_EINVAL;
+  if (!elem_bytes(dtype)) return KVS_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return KVS_EUNSUPPORTED;
+  if (!is_pow2(block_size) || block_size < 16 || block_size > 256) return KVS_EUNSUPPORTED;
+  if ((int64_t)(num_q_heads / num_kv_heads) * q_len > kMaxRows) return KVS_EUNSUPPORTED;
+  if (num_seqs > kMaxSeqs) return KVS_EUNSUPPORTED;
+  if ((int64_t)table_stride * block_size > INT_MAX / 2) return KVS_EUNSUPPORTED;
+  // the batch's 16-token tiles are counted in 32 bits, with headroom
+  if ((int64_t)num_seqs * (walk_blocks * (int64_t)(block_size / 16) + 1) > INT_MAX / 2)
+    return KVS_EUNSUPPORTED;
+  if (num_seqs == 0) return KVS_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
+    return KVS_EINVAL;
+  const size_t need =
+      paged_decode_attention_workspace_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim);
+  if (workspace_bytes < need) return KVS_ENOSPACE;
+
+  kvs::DecodeParams p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.kv_pos_offset = kv_pos_offset;
+  p.out = out;
+  p.chunk_meta = (int32_t*)workspace;
+  p.partials = (float*)((char*)workspace + kvs::decode_meta_bytes(num_seqs));
+  p.total_blocks = total_blocks;
+  p.table_stride = table_stride;
+  p.walk_blocks = walk_blocks;
+  p.num_seqs = num_seqs;
+  p.q_len = q_len;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.window = window;
+  p.max_slices = kvs::decode_max_slices(num_kv_heads);
+  p.min_tiles = 8;  // 128 tokens: partial traffic stays a few percent of the KV a slice reads
+  p.start_tiles = 2;  // a segment start costs about two tiles' streaming time
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  p.flags = flags;
+  p.is_bf16 = dtype == KVS_BF16;
+  return launch_status(kvs::launch_paged_decode(p, (hipStream_t)stream));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* kvs_status_string(int status) {
@@ -183,52 +245,52 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
                            int32_t block_size, int64_t total_blocks, float scale,
                            kvs_dtype dtype, uint32_t flags, void* workspace,
                            size_t workspace_bytes, float* out, void* stream) {
-  if (num_seqs < 0 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
-      block_size < 1 || table_stride < 1 || walk_blocks < 0 || walk_blocks > table_stride ||
-      total_blocks < 1 || !isfinite(scale))
-    return KVS_EINVAL;
-  if (num_q_heads % num_kv_heads != 0) return KVS_EINVAL;
-  if (flags & ~KVS_WALK_TABLE) return KVS_EINVAL;
-  if (!elem_bytes(dtype)) return KVS_EUNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return KVS_EUNSUPPORTED;
-  if (!is_pow2(block_size) || block_size < 16 || block_size > 256) return KVS_EUNSUPPORTED;
-  if ((int64_t)(num_q_heads / num_kv_heads) * q_len > kMaxRows) return KVS_EUNSUPPORTED;
-  if (num_seqs > kMaxSeqs) return KVS_EUNSUPPORTED;
-  if ((int64_t)table_stride * block_size > INT_MAX / 2) return KVS_EUNSUPPORTED;
-  // the batch's 16-token tiles are counted in 32 bits, with headroom
-  if ((int64_t)num_seqs * walk_blocks * (block_size / 16) > INT_MAX / 2) return KVS_EUNSUPPORTED;
-  if (num_seqs == 0) return KVS_OK;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
-    return KVS_EINVAL;
-  const size_t need =
-      paged_decode_attention_workspace_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim);
-  if (workspace_bytes < need) return KVS_ENOSPACE;
+  return decode_common(q, k_cache, v_cache, block_table, table_stride, walk_blocks, seq_lens,
+                       nullptr, 0, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim,
+                       block_size, total_blocks, scale, dtype, flags, workspace,
+                       workspace_bytes, out, stream);
+}
 
-  kvs::DecodeParams p{};
-  p.q = q;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.block_table = block_table;
-  p.seq_lens = seq_lens;
-  p.out = out;
-  p.chunk_meta = (int32_t*)workspace;
-  p.partials = (float*)((char*)workspace + kvs::decode_meta_bytes(num_seqs));
-  p.total_blocks = total_blocks;
-  p.table_stride = table_stride;
-  p.walk_blocks = walk_blocks;
-  p.num_seqs = num_seqs;
-  p.q_len = q_len;
-  p.num_q_heads = num_q_heads;
-  p.num_kv_heads = num_kv_heads;
-  p.head_dim = head_dim;
-  p.block_size = block_size;
-  p.max_slices = kvs::decode_max_slices(num_kv_heads);
-  p.min_tiles = 8;  // 128 tokens: partial traffic stays a few percent of the KV a slice reads
-  p.start_tiles = 2;  // a segment start costs about two tiles' streaming time
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
-  p.flags = flags;
-  p.is_bf16 = dtype == KVS_BF16;
-  return launch_status(kvs::launch_paged_decode(p, (hipStream_t)stream));
+int paged_decode_attention_swa(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, int32_t table_stride,
+                               int32_t walk_blocks, const int32_t* seq_lens,
+                               const int32_t* kv_pos_offset, int32_t sliding_window,
+                               int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t total_blocks, float scale, kvs_dtype dtype,
+                               void* workspace, size_t workspace_bytes, float* out,
+                               void* stream) {
+  return decode_common(q, k_cache, v_cache, block_table, table_stride, walk_blocks, seq_lens,
+                       kv_pos_offset, sliding_window, num_seqs, q_len, num_q_heads,
+                       num_kv_heads, head_dim, block_size, total_blocks, scale, dtype, 0,
+                       workspace, workspace_bytes, out, stream);
+}
+
+int kv_swa_tail_trim(const int32_t* src, int32_t rows, int32_t src_stride,
+                     const int32_t* seq_lens, int32_t q_len, int32_t sliding_window,
+                     int32_t block_size, int32_t* dst, int32_t dst_stride, int32_t* kv_pos_offset,
+                     int32_t* width_out) {
+  if (rows < 0 || src_stride < 1 || q_len < 1 || sliding_window < 1 || block_size < 1 ||
+      !width_out)
+    return KVS_EINVAL;
+  const int64_t need = ((int64_t)sliding_window + q_len - 1 + block_size - 1) / block_size + 1;
+  const int32_t width = (int32_t)(need < src_stride ? need : src_stride);
+  *width_out = width;
+  if (dst_stride < width) return KVS_EINVAL;
+  if (rows == 0) return KVS_OK;
+  if (!src || !seq_lens || !dst || !kv_pos_offset) return KVS_EINVAL;
+  for (int32_t r = 0; r < rows; ++r) {
+    const int32_t L = seq_lens[r];
+    const int64_t last = L > 0 ? (int64_t)(L - 1) / block_size : 0;
+    const int64_t first = last - width + 1 > 0 ? last - width + 1 : 0;
+    if (first * block_size > INT_MAX) return KVS_EINVAL;
+    kv_pos_offset[r] = (int32_t)(first * block_size);
+    for (int32_t c = 0; c < width; ++c) {
+      const int64_t col = first + c;
+      dst[(int64_t)r * dst_stride + c] = col < src_stride ? src[(int64_t)r * src_stride + col] : -1;
+    }
+  }
+  return KVS_OK;
 }
 
 }  // extern "C"

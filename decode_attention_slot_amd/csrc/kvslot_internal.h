@@ -31,6 +31,7 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_table;
   const int32_t* seq_lens;
+  const int32_t* kv_pos_offset;  // per request, position of table column 0; null: 0
   float* out;
   float* partials;      // [slots][num_kv_heads][rows][head_dim + 4]
   int32_t* chunk_meta;  // [num_seqs][2]: first partial slot and partial count
@@ -43,6 +44,7 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t block_size;
+  int32_t window;  // sliding window in positions; 0: none
   int32_t max_slices;  // partial storage bound on the slices (per head group)
   int32_t slices;      // set by the launcher: slices the batch's tiles are cut into
   int32_t min_tiles;   // never cut a slice shorter than this many 16-token tiles

@@ -8,6 +8,11 @@
 // position p below walk_blocks * block_size whose block-table entry is
 // active; q head h reads KV head h / (Hq / Hkv). The result is the softmax of
 // scale * <q, k> over those keys applied to the values, in fp32.
+// A sliding-window layer ("KV Caching with vLLM", section "Attention Type";
+// "Decode Context-Length Bucketing", the SWA tail trim) adds two things: a
+// window, so the query at qpos sees keys from qpos - window + 1 only, and a
+// per-request kv_pos_offset, the absolute position of the (tail-trimmed)
+// table's column 0; positions stay absolute.
 //
 // How, on CDNA4:
 // * Work split: the 16-token tiles of every request's context, laid end to
@@ -73,6 +78,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kFlagWalkTable = 0x1u;
 // Never set by the host. Testing it keeps the table-walk loads alive.
 constexpr uint32_t kFlagSink = 0x80000000u;
+constexpr int kContextWalk = 0, kTableWalk = 1, kWindow = 2;  // pass-1 modes
 constexpr int kTile = 16;
 constexpr int kStage = 256;  // block ids staged in LDS at a time
 constexpr int kDepth = 2;    // tiles in flight per wave
@@ -116,15 +122,38 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Context positions of a request that a walk of walk_tok positions can see.
-__device__ __forceinline__ int visible_len(int L, int walk_tok) {
-  return L <= 0 ? 0 : (L < walk_tok ? L : walk_tok);
+// The tiles request r walks: absolute positions [16 * t_lo, E) in 16-token
+// tiles, n of them. off is the absolute position of table column 0 (a
+// tail-trimmed table; 0 for a whole table), rounded down to a block. E ends
+// the visible context: the request's length, cut at the walked columns. With
+// a sliding window the walk starts at the earliest key a query of this step
+// sees (L - q_len - window + 1). Positions stay below 2^31 - 64.
+struct ReqSpan {
+  int off, E, t_lo, n;
+};
+
+template <bool SWA>
+__device__ __forceinline__ ReqSpan request_span(const int32_t* kv_pos_offset, int32_t window,
+                                                int r, int L, int walk_tok, int bs, int Sq) {
+  ReqSpan sp;
+  const int off = SWA && kv_pos_offset ? kv_pos_offset[r] : 0;
+  sp.off = max(off, 0) & ~(bs - 1);
+  int64_t E = min((int64_t)L, (int64_t)sp.off + walk_tok);
+  E = min(E, (int64_t)INT32_MAX - 64);
+  sp.E = L <= 0 ? 0 : (int)E;
+  int64_t start = sp.off;
+  if (SWA && window > 0) start = max(start, (int64_t)L - Sq - window + 1);
+  sp.t_lo = (int)(start / 16);
+  sp.n = sp.E > start ? (sp.E + 15) / 16 - sp.t_lo : 0;
+  return sp;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-template <bool BF16, int D, int NW, bool TW>
+// MODE: kContextWalk, kTableWalk (the fixed-shape walk) or kWindow (a
+// sliding window over a possibly tail-trimmed table).
+template <bool BF16, int D, int NW, int MODE>
 __global__ void __launch_bounds__(NW * 64, 2)
 paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int ES = BF16 ? 2 : 4;       // bytes per element
@@ -134,6 +163,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int NVW = NT * ES / 4;       // V dwords per lane per token
   constexpr int PSTRIDE = D + 4;         // floats per partial row (acc, m, l, pad)
   constexpr int NTHR = NW * 64;
+  constexpr bool TW = MODE == kTableWalk;
+  constexpr bool SWA = MODE == kWindow;
   constexpr uint32_t kNegZero = BF16 ? 0x80008000u : 0x80000000u;
   static_assert(NP >= 1 && NVW >= 2, "unsupported head_dim");
   struct TileBuf {
@@ -179,7 +210,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // request carries that many fewer tiles. s_pref holds these units.
   const int X = p.start_tiles;
   for (int rr = threadIdx.x; rr < B; rr += NTHR)
-    s_pref[rr] = (visible_len(p.seq_lens[rr], walk_tok) + kTile - 1) / kTile;
+    s_pref[rr] = request_span<SWA>(p.kv_pos_offset, p.window, rr, p.seq_lens[rr], walk_tok, bs, Sq).n;
   if (threadIdx.x == 0) {
     s_first[0] = 0;
     s_first[1] = 0;
@@ -244,14 +275,15 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
   const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
 
-  // Tiles [tok_a, tok_b) (multiples of kTile) of table row trow, through
-  // fn(token of the tile, its loads). Block ids are staged in LDS in pieces
+  // Tiles [tok_a, tok_b) (absolute positions, multiples of kTile) of table
+  // row trow, whose column 0 holds position off, through fn(position of the
+  // tile, its loads). Block ids are staged in LDS in pieces
   // of kStage; a ring of kDepth tile buffers keeps tiles t+1 .. t+kDepth-1
   // in flight while tile t is used. Loads past the last tile re-load the
   // last tile (a cache hit), so no load depends on a branch.
-  auto walk_tiles_of = [&](const int32_t* trow, int tok_a, int tok_b, auto&& fn) {
-    const int blk_first = tok_a >> bs_shift;
-    const int blk_end = ((tok_b - 1) >> bs_shift) + 1;
+  auto walk_tiles_of = [&](const int32_t* trow, int off, int tok_a, int tok_b, auto&& fn) {
+    const int blk_first = (tok_a - off) >> bs_shift;
+    const int blk_end = ((tok_b - 1 - off) >> bs_shift) + 1;
     for (int pb = blk_first; pb < blk_end; pb += kStage) {
       const int pn = min(kStage, blk_end - pb);
       __syncthreads();  // the previous piece is consumed by every wave
@@ -260,14 +292,14 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         s_blk[i] = col < p.table_stride ? trow[col] : 0;
       }
       __syncthreads();
-      const int t_begin = max(tok_a, pb << bs_shift);
-      const int t_end = min(tok_b, (pb + pn) << bs_shift);
+      const int t_begin = max(tok_a, off + (pb << bs_shift));
+      const int t_end = min(tok_b, off + ((pb + pn) << bs_shift));
       const int nt = (t_end - t_begin) / kTile;
 
       // K as the score MFMA's A operand, V in row layout. An inactive
       // entry reads null block 0 and is masked by the caller.
       auto load = [&](int tt, TileBuf& bf) {
-        const int bid = uniform(s_blk[(tt >> bs_shift) - pb]);
+        const int bid = uniform(s_blk[((tt - off) >> bs_shift) - pb]);
         const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
         const int64_t base = (int64_t)(active ? bid : 0) * block_bytes;
         const char* kb = (const char*)p.k_cache + base;
@@ -313,13 +345,23 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // ---- one segment: tiles [t0, t1) of request r (nr tiles, tile 0 at unit pr) --
   auto segment = [&](int r, int t0, int t1, int nr, int pr) {
     const int L = uniform(p.seq_lens[r]);
-    const int E = visible_len(L, walk_tok);
+    const ReqSpan sp = request_span<SWA>(p.kv_pos_offset, p.window, r, L, walk_tok, bs, Sq);
+    const int E = uniform(sp.E);
+    const int off = uniform(sp.off);
+    const int t_lo = uniform(sp.t_lo);
 
     // query operand (B operand of the score MFMA)
     const int jrow = rho / G;
     const int hh = rho - jrow * G;
     const int qpos = rho < nrows ? L - Sq + jrow : -1;
     const int qpos_min = L - Sq;
+    // sliding window: row rho sees keys from qpos - window + 1; every row
+    // does from L - window on
+    const int qlo = SWA && p.window > 0
+                        ? (int)max((int64_t)qpos - p.window + 1, (int64_t)INT32_MIN)
+                        : INT32_MIN;
+    const int all_lo =
+        SWA && p.window > 0 ? (int)max((int64_t)L - p.window, (int64_t)INT32_MIN) : INT32_MIN;
     u32x4 qp[NP];
     {
       const char* qrow = (const char*)p.q +
@@ -359,13 +401,14 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       float sx[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sx[i] = s[i] * p.scale_log2;
-      const bool full = active && (tt + kTile <= E) && (tt + kTile - 1 <= qpos_min);
+      const bool full = active && (tt + kTile <= E) && (tt + kTile - 1 <= qpos_min) &&
+                        (!SWA || tt >= all_lo);
       if (!full) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = tt + 4 * jg + i;
           const bool kv_ok = active && pos < E;
-          if (!(kv_ok && pos <= qpos)) sx[i] = -INFINITY;
+          if (!(kv_ok && pos <= qpos && (!SWA || pos >= qlo))) sx[i] = -INFINITY;
           if (!kv_ok) {
 #pragma unroll
             for (int w = 0; w < NVW; ++w) bf.v[i][w] = kNegZero;
@@ -404,7 +447,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         }
       }
     };
-    walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, t0 * kTile, t1 * kTile, consume);
+    walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, off, (t_lo + t0) * kTile,
+                  (t_lo + t1) * kTile, consume);
 
     // acc[n][i] holds dimension (4*jg + i) * NT + n of query row rho.
     const float l_tot = sum_over_groups(l_run);
@@ -495,7 +539,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       const int pn = pr + (walk_tiles - n);
       if (pn > pos) {
         const int e = min(pbnd, pn);
-        walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, (n + pos - pr) * kTile,
+        walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, 0, (n + pos - pr) * kTile,
                       (n + e - pr) * kTile, drain);
         pos = e;
       }
@@ -647,7 +691,8 @@ hipError_t resident_workgroups(int* out) {
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, false>), NW * 64,
+      &per_cu, reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, kContextWalk>),
+      NW * 64,
       decode_lds_bytes(kDecodeMaxSeqs));
   if (e != hipSuccess) return e;
   *out = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
@@ -669,9 +714,11 @@ hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t strea
   const dim3 grid((unsigned)p.slices * (unsigned)HG);
   const size_t lds = decode_lds_bytes(p.num_seqs);
   if (p.flags & kFlagWalkTable)
-    paged_decode_kernel<BF16, D, NW, true><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+    paged_decode_kernel<BF16, D, NW, kTableWalk><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+  else if (p.window > 0 || p.kv_pos_offset)
+    paged_decode_kernel<BF16, D, NW, kWindow><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
   else
-    paged_decode_kernel<BF16, D, NW, false><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+    paged_decode_kernel<BF16, D, NW, kContextWalk><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   int64_t cgrid = (int64_t)p.num_seqs * p.num_kv_heads;

@@ -230,7 +230,7 @@ size_t paged_decode_attention_workspace_bytes(int32_t num_seqs, int32_t q_len,
  * decides the fp32 summation order.)
  * Supported: head_dim 64 or 128; block_size 16, 32, 64, 128 or 256;
  * (num_q_heads / num_kv_heads) * q_len <= 16; num_seqs <= 8192;
- * num_seqs * walk_blocks * block_size / 16 <= 2^30 - 1.
+ * num_seqs * (walk_blocks * block_size / 16 + 1) <= 2^30 - 1.
  * Errors: KVS_EINVAL (null pointers, non-positive sizes, num_q_heads not a
  * multiple of num_kv_heads, walk_blocks outside [0, table_stride]),
  * KVS_EUNSUPPORTED (outside the supported set), KVS_ENOSPACE (workspace
@@ -243,6 +243,70 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
                            int32_t block_size, int64_t total_blocks, float scale,
                            kvs_dtype dtype, uint32_t flags, void* workspace,
                            size_t workspace_bytes, float* out, void* stream);
+
+/*
+ * paged_decode_attention_swa - decode attention for a sliding-window layer
+ * over a tail-trimmed block table ([KVC] "Attention Type": a sliding-window
+ * layer keeps only the recent tokens within its window; [CLB] "Block-table
+ * head-trim vs. SWA tail-trim": the trimmed table keeps a request's last
+ * blocks and swa_kv_pos_offset gives the position of its first one, so
+ * positions stay absolute).
+ *
+ * As paged_decode_attention (flags 0), except that:
+ *   - column c of request r's table row holds the block of absolute
+ *     positions kv_pos_offset[r] + c * block_size onward, and only positions
+ *     kv_pos_offset[r] .. kv_pos_offset[r] + walk_blocks * block_size - 1
+ *     are visible;
+ *   - with sliding_window > 0, the query at position qpos sees only keys at
+ *     positions qpos - sliding_window + 1 .. qpos (the window counts the
+ *     query's own position); 0 means no window.
+ * Only the blocks those keys sit in are read.
+ *
+ *   kv_pos_offset  int32 [num_seqs], device, each >= 0 and a multiple of
+ *                  block_size (kv_swa_tail_trim writes them); NULL means 0
+ *                  for every request (a whole table with a window)
+ * On one device the output does not depend on whether the table is whole
+ * (offsets 0) or trimmed, as long as the trim keeps every block a window of
+ * the step touches: the two are bitwise identical.
+ * Errors: as paged_decode_attention, and KVS_EINVAL for sliding_window < 0.
+ */
+int paged_decode_attention_swa(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, int32_t table_stride,
+                               int32_t walk_blocks, const int32_t* seq_lens,
+                               const int32_t* kv_pos_offset, int32_t sliding_window,
+                               int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t total_blocks, float scale, kvs_dtype dtype,
+                               void* workspace, size_t workspace_bytes, float* out,
+                               void* stream);
+
+/*
+ * kv_swa_tail_trim - tail-trim a block table for a sliding-window layer
+ * ([CLB] "Block-table head-trim vs. SWA tail-trim"). Host only; every
+ * pointer is a host pointer; no GPU work.
+ *
+ * width = min(src_stride, ceil((sliding_window + q_len - 1) / block_size)
+ * + 1): the blocks the windows of a step's q_len queries can touch at any
+ * alignment (the page's window / block_size assumes one query and an
+ * aligned window). Row r keeps the width columns ending at its last
+ * context block (seq_lens[r] - 1) / block_size, starting no earlier than
+ * column 0: dst[r][c] = src[r][first + c], -1 past the source width, and
+ * kv_pos_offset[r] = first * block_size. A row with seq_lens[r] <= 0 keeps
+ * columns from 0.
+ *
+ *   src            int32 [rows][src_stride]
+ *   seq_lens       int32 [rows]
+ *   dst            int32 [rows][dst_stride], dst_stride >= width, written
+ *   kv_pos_offset  int32 [rows], written
+ *   width_out      written with width (also on KVS_EINVAL for a short dst)
+ * Errors: KVS_EINVAL for null pointers, rows < 0, src_stride < 1,
+ * q_len < 1, sliding_window < 1, block_size < 1, dst_stride < width, or an
+ * offset beyond int32.
+ */
+int kv_swa_tail_trim(const int32_t* src, int32_t rows, int32_t src_stride,
+                     const int32_t* seq_lens, int32_t q_len, int32_t sliding_window,
+                     int32_t block_size, int32_t* dst, int32_t dst_stride, int32_t* kv_pos_offset,
+                     int32_t* width_out);
 
 #ifdef __cplusplus
 }

@@ -71,9 +71,9 @@ class OracleStep:
         O.reshape_and_cache(k[mine], v[mine], slots[: len(req)][mine], self.k_cache, self.v_cache)
         return slots
 
-    def attention(self, q, walk_blocks=None, requests=None):
+    def attention(self, q, walk_blocks=None, requests=None, window=0):
         w = self.w
         walk = self.table.shape[1] if walk_blocks is None else walk_blocks
         rows = self.rows if requests is None else requests
         return O.paged_decode_attention(q, self.k_cache, self.v_cache, self.table, w.seq_lens,
-                                        walk, w.scale, w.dtype, requests=rows)
+                                        walk, w.scale, w.dtype, requests=rows, window=window)

@@ -153,6 +153,48 @@ def test_gpu_entry_points_reject_bad_scalars(K):
     assert lib.paged_decode_attention_workspace_bytes(12, 1, 32, 8, 128) > 0
 
 
+def test_swa_tail_trim_matches_oracle(K):
+    rng = np.random.default_rng(5)
+    for bs, q_len, window in [(16, 1, 1), (64, 4, 4096), (32, 2, 100), (256, 1, 5000), (16, 3, 17)]:
+        lens = rng.integers(-3, 20000, size=11).astype(np.int32)
+        lens[0], lens[1] = 0, 1
+        width = int(-(-int(lens.max()) // bs)) + 3
+        table = rng.integers(-1, 9999, size=(11, width)).astype(np.int32)
+        got_t, got_o = K.kv_swa_tail_trim(table, lens, q_len, window, bs)
+        want_t, want_o = O.swa_tail_trim(table, lens, q_len, window, bs)
+        assert np.array_equal(got_t, want_t) and np.array_equal(got_o, want_o)
+
+
+def test_swa_entry_points_reject_bad_scalars(K):
+    lib = K.load()
+    null = None
+    import ctypes
+    w = ctypes.c_int32()
+    # kv_swa_tail_trim: bad window / q_len / block size, short destination, null pointers
+    assert lib.kv_swa_tail_trim(null, 1, 4, null, 1, 0, 16, null, 4, null, ctypes.byref(w)) == -1
+    assert lib.kv_swa_tail_trim(null, 1, 4, null, 0, 10, 16, null, 4, null, ctypes.byref(w)) == -1
+    assert lib.kv_swa_tail_trim(null, 1, 40, null, 1, 100, 16, null, 2, null, ctypes.byref(w)) == -1
+    assert w.value == 8  # ceil(100 / 16) + 1
+    assert lib.kv_swa_tail_trim(null, 1, 40, null, 1, 100, 16, null, 8, null, ctypes.byref(w)) == -1
+    assert lib.kv_swa_tail_trim(null, 0, 40, null, 1, 100, 16, null, 8, null, ctypes.byref(w)) == 0
+
+    def swa(**kw):
+        a = dict(q=null, k=null, v=null, bt=null, stride=4, walk=4, sl=null, off=null, win=8, B=1,
+                 sq=1, hq=8, hkv=2, d=128, bs=64, nb=10, scale=0.1, dtype=1, ws=null,
+                 wsb=1 << 30, out=null)
+        a.update(kw)
+        return lib.paged_decode_attention_swa(a["q"], a["k"], a["v"], a["bt"], a["stride"],
+                                              a["walk"], a["sl"], a["off"], a["win"], a["B"],
+                                              a["sq"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
+                                              a["scale"], a["dtype"], a["ws"], a["wsb"], a["out"],
+                                              null)
+
+    assert swa() == -1          # null pointers
+    assert swa(win=-1) == -1    # negative window
+    assert swa(B=0) == 0
+    assert swa(d=96) == -2
+
+
 def test_no_fallback_when_library_missing(K, tmp_path, monkeypatch):
     from decode_attention_slot_amd import _lib
 

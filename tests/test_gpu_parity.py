@@ -367,6 +367,101 @@ def test_cache_write_image_vs_oracle(cuda, dtype):
     assert np.array_equal(host_bits(dkc), bits(kc)) and np.array_equal(host_bits(dvc), bits(vc))
 
 
+# ---------------------------------------------------------------------------
+# sliding window over a tail-trimmed table
+# ---------------------------------------------------------------------------
+SWA_SHAPES = [
+    # (dtype, d, bs, hkv, g, sq, window, lens)
+    ("f32", 64, 16, 2, 2, 1, 1, [1, 5, 40]),
+    ("f32", 128, 64, 1, 4, 3, 70, [3, 64, 65, 700]),
+    ("bf16", 128, 64, 8, 4, 1, 4096, [1, 100, 4095, 4096, 4097, 9000]),
+    ("bf16", 128, 16, 8, 8, 1, 1000, [17, 999, 1000, 1001, 5000]),
+    ("bf16", 128, 64, 8, 4, 4, 333, [4, 5, 336, 337, 2000, 6000]),
+    ("bf16", 64, 256, 2, 2, 2, 600, [2, 255, 600, 601, 3000]),
+    ("bf16", 128, 32, 4, 1, 16, 50, [16, 40, 66, 2100]),
+]
+
+
+def swa_case(cuda, shape, seed=7):
+    dtype, d, bs, hkv, g, sq, window, lens = shape
+    c = small_case(cuda, seed, lens, bs, hkv, g, sq, d, dtype)
+    trimmed, off = K.kv_swa_tail_trim(c["table"], lens, sq, window, bs)
+    c.update(window=window, trimmed=trimmed, off=off, d_tt=torch.from_numpy(trimmed).to(cuda),
+             d_off=torch.from_numpy(off).to(cuda))
+    return c
+
+
+def swa_gpu(c, table=None, off=None):
+    return K.paged_decode_attention_swa(c["d_q"], c["d_kc"], c["d_vc"],
+                                        c["d_tt"] if table is None else table, c["d_sl"],
+                                        c["w"].scale, c["window"],
+                                        kv_pos_offset=c["d_off"] if off is None else off)
+
+
+@pytest.mark.parametrize("shape", SWA_SHAPES,
+                         ids=lambda s: f"{s[0]}-d{s[1]}-bs{s[2]}-h{s[3]}x{s[4]}-q{s[5]}-w{s[6]}")
+def test_swa_trimmed_vs_oracle(cuda, shape):
+    c = swa_case(cuda, shape)
+    w = c["w"]
+    out = swa_gpu(c)
+    torch.cuda.synchronize()
+    # the oracle walks the whole table with the window
+    want = O.paged_decode_attention(c["q"], c["kc"], c["vc"], c["table"], w.seq_lens,
+                                    c["table"].shape[1], w.scale, w.dtype, window=c["window"])
+    assert max_err(out, want) <= TOL[w.dtype]
+    # ... and equals its own run over the trimmed frame
+    want_t = O.paged_decode_attention(c["q"], c["kc"], c["vc"], c["trimmed"], w.seq_lens,
+                                      c["trimmed"].shape[1], w.scale, w.dtype, window=c["window"],
+                                      kv_pos_offset=c["off"])
+    np.testing.assert_array_equal(want, want_t)
+
+
+def test_swa_trimmed_equals_whole_table_bitwise(cuda):
+    c = swa_case(cuda, SWA_SHAPES[4])
+    trimmed = swa_gpu(c)
+    whole = swa_gpu(c, table=c["d_bt"], off=torch.zeros_like(c["d_off"]))
+    no_off = K.paged_decode_attention_swa(c["d_q"], c["d_kc"], c["d_vc"], c["d_bt"], c["d_sl"],
+                                          c["w"].scale, c["window"])
+    torch.cuda.synchronize()
+    assert torch.equal(trimmed.view(torch.int32), whole.view(torch.int32))
+    assert torch.equal(trimmed.view(torch.int32), no_off.view(torch.int32))
+
+
+def test_swa_window_wider_than_context_is_plain_decode(cuda):
+    c = small_case(cuda, 8, [1, 64, 65, 700, 3000], 64, 8, 4, 2, 128, "bf16")
+    plain = gpu_attn(c)
+    wide = K.paged_decode_attention_swa(c["d_q"], c["d_kc"], c["d_vc"], c["d_bt"], c["d_sl"],
+                                        c["w"].scale, 3001)
+    off0 = K.paged_decode_attention_swa(c["d_q"], c["d_kc"], c["d_vc"], c["d_bt"], c["d_sl"],
+                                        c["w"].scale, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int32), wide.view(torch.int32))
+    assert torch.equal(plain.view(torch.int32), off0.view(torch.int32))
+
+
+def test_swa_workload_scale(cuda):
+    """Ragged + speculative workload (S_q 4, 64 requests up to ~24K tokens) with
+    a 4096-token window over the trimmed table; sampled rows vs the oracle."""
+    w = W.make_workload(4)
+    s = dev.build(w, cuda)
+    dev.run_step(s)
+    window = 4096
+    lens = w.seq_lens[: w.num_rows]
+    trimmed, off = K.kv_swa_tail_trim(s.host_table, lens, w.q_len, window, w.block_size)
+    assert trimmed.shape[1] == -(-(window + w.q_len - 1) // w.block_size) + 1
+    out = K.paged_decode_attention_swa(s.q, s.k_cache, s.v_cache,
+                                       torch.from_numpy(trimmed).to(cuda), s.seq_lens, w.scale,
+                                       window, kv_pos_offset=torch.from_numpy(off).to(cuda))
+    torch.cuda.synchronize()
+    ref = OracleStep(w, s.host_table)
+    ref.write_step()
+    rows = [0, 1, int(np.argmax(lens)), int(np.argmin(lens)), w.num_rows - 1]
+    want = O.paged_decode_attention(w.q(), ref.k_cache, ref.v_cache, s.host_table, lens,
+                                    s.host_table.shape[1], w.scale, w.dtype, requests=rows,
+                                    window=window)
+    assert max_err(out, want, rows) <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("bs,dtype", [(16, "bf16"), (64, "f32"), (3, "bf16")])
 def test_fused_slot_write_vs_oracle(cuda, bs, dtype):
     """One-launch slot mapping + write: slots and byte images equal the oracle's
