@@ -10,9 +10,14 @@ from .kvslot_oracle import (  # noqa: F401
     PAD_SLOT_ID,
     OracleError,
     compute_slot_mapping,
+    compute_slot_mapping_dcp,
+    dcp_local_position,
+    dcp_owner,
     kv_cache_tensor_bytes,
     map_to_kernel_blocks,
+    merge_lse,
     paged_decode_attention,
+    paged_decode_attention_dcp,
     remap_null_block_to_sentinel,
     reshape_and_cache,
     select_ctx_bucket,

@@ -241,6 +241,127 @@ def swa_tail_trim(block_table, seq_lens, q_len, window, block_size):
 
 
 # ---------------------------------------------------------------------------
+# Decode context parallelism (one rank's share)
+# ---------------------------------------------------------------------------
+def dcp_owner(position, world_size, interleave):
+    """Rank that stores the KV of a position under decode context parallelism.
+
+    [BT] design motivation ("DCP / PCP interleave"): with TOTAL_CP_WORLD_SIZE,
+    TOTAL_CP_RANK and CP_KV_CACHE_INTERLEAVE_SIZE the slot-mapping kernel
+    writes a real slot only for the positions its own rank stores and PAD_ID
+    for the others. The page prints no formula. Reading: positions go to the
+    ranks round-robin in runs of ``interleave`` consecutive tokens.
+    """
+    return (np.asarray(position) // interleave) % world_size
+
+
+def dcp_local_position(position, world_size, interleave):
+    """Position of a token inside its owner's cache (same reading).
+
+    Each rank packs its own runs densely and in order: run k of the rank
+    holds global runs k * world + rank. With ``interleave`` dividing the
+    block size, the rank-local position's block index equals the global
+    position // (world * block_size): every rank shares the request's table
+    row, a table column standing for world * block_size consecutive
+    positions (a "virtual" block), of which each rank stores block_size.
+    """
+    p = np.asarray(position)
+    return (p // (world_size * interleave)) * interleave + p % interleave
+
+
+def compute_slot_mapping_dcp(req_indices, positions, block_table, block_size, world_size, rank,
+                             interleave, max_num_tokens=None):
+    """Slot mapping on one context-parallel rank ([BT], as dcp_owner).
+
+    A token this rank stores gets the slot of its rank-local position
+    (table[r, lp // bs] * bs + lp % bs, with the padding, table-bounds and
+    inactive-entry rules of compute_slot_mapping); every other token, and
+    the tail of the buffer, gets PAD_SLOT_ID.
+    """
+    req = np.asarray(req_indices, dtype=np.int64)
+    pos = np.asarray(positions, dtype=np.int64)
+    assert block_size % interleave == 0 and 0 <= rank < world_size
+    local = np.where(pos >= 0, dcp_local_position(np.maximum(pos, 0), world_size, interleave), -1)
+    mine = (pos >= 0) & (dcp_owner(np.maximum(pos, 0), world_size, interleave) == rank)
+    slots = compute_slot_mapping(req, local, block_table, block_size, max_num_tokens)
+    n = len(req)
+    slots[:n] = np.where(mine, slots[:n], PAD_SLOT_ID)
+    return slots
+
+
+def paged_decode_attention_dcp(q, k_cache, v_cache, block_table, seq_lens, walk_blocks, scale,
+                               dtype, world_size, rank, interleave, requests=None):
+    """One context-parallel rank's decode attention over the keys it stores.
+
+    Queries are those of paged_decode_attention (global positions, causal);
+    the keys are the positions p < L this rank owns (dcp_owner), read from
+    this rank's cache at their rank-local position, with the head trim
+    counted in table columns (p < walk_blocks * world * bs). Returns (out,
+    lse): out normalised over this rank's keys, and the natural-log
+    sum of exp(scores) over them (-inf and zeros where the rank sees no
+    key), the partial state that ranks exchange and merge (merge_lse).
+    """
+    q64 = widen(q, dtype)
+    B, S_q, Hq, D = q64.shape
+    _, bs, Hkv, _ = k_cache.shape
+    G = Hq // Hkv
+    assert block_size_ok(bs, interleave)
+    table = np.asarray(block_table, dtype=np.int64)
+    out = np.zeros((B, S_q, Hq, D), dtype=np.float64)
+    lse = np.full((B, S_q, Hq), -np.inf, dtype=np.float64)
+    rows = range(B) if requests is None else requests
+    for r in rows:
+        L = int(seq_lens[r])
+        if L <= 0:
+            continue
+        visible = min(L, int(walk_blocks) * world_size * bs)
+        gpos = np.arange(visible)
+        gpos = gpos[dcp_owner(gpos, world_size, interleave) == rank]
+        lpos = dcp_local_position(gpos, world_size, interleave)
+        blocks = table[r, lpos // bs]
+        active = blocks > 0
+        gpos, lpos, blocks = gpos[active], lpos[active], blocks[active]
+        K = widen(k_cache[blocks, lpos % bs], dtype)
+        V = widen(v_cache[blocks, lpos % bs], dtype)
+        for j in range(S_q):
+            qpos = L - S_q + j
+            seen = gpos <= qpos
+            if not seen.any():
+                continue
+            Kj, Vj = K[seen], V[seen]
+            for h in range(Hq):
+                g = h // G
+                s = scale * (Kj[:, g, :] @ q64[r, j, h])
+                mx = s.max()
+                p = np.exp(s - mx)
+                out[r, j, h] = (p @ Vj[:, g, :]) / p.sum()
+                lse[r, j, h] = mx + np.log(p.sum())
+    return out, lse
+
+
+def block_size_ok(block_size, interleave):
+    """The reading of dcp_local_position needs the interleave to divide the block."""
+    return interleave >= 1 and block_size % interleave == 0
+
+
+def merge_lse(outs, lses):
+    """Merge per-rank (out, lse) partial states into the full attention.
+
+    The softmax over the union of the ranks' disjoint key sets: weight each
+    rank's normalised output by exp(lse_rank - lse_total). Rows no rank saw
+    stay zero.
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    mx = lses.max(axis=0)
+    safe = np.where(np.isfinite(mx), mx, 0.0)
+    w = np.exp(lses - safe[None])  # exp(-inf) = 0 for ranks that saw nothing
+    tot = w.sum(axis=0)
+    merged = (w[..., None] * outs).sum(axis=0) / np.where(tot > 0, tot, 1.0)[..., None]
+    return np.where((tot > 0)[..., None], merged, 0.0)
+
+
+# ---------------------------------------------------------------------------
 # Context-length bucket selection
 # ---------------------------------------------------------------------------
 def smallest_bucket_at_least(n, buckets):

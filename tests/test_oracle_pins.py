@@ -427,6 +427,104 @@ def test_tail_trimmed_frame_equals_full_table_with_window():
     assert trimmed.shape[1] == 5 and off.tolist() == [224, 0, 64, 0]
 
 
+# ---------------------------------------------------------------------------
+# decode context parallelism: one rank's share
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("world,interleave,bs", [(1, 1, 16), (2, 1, 16), (2, 16, 16), (4, 8, 64),
+                                                 (3, 4, 32), (8, 64, 64)])
+def test_dcp_positions_partition_and_pack(world, interleave, bs):
+    p = np.arange(0, 5 * world * bs + 7)
+    owner = O.dcp_owner(p, world, interleave)
+    local = O.dcp_local_position(p, world, interleave)
+    assert set(owner.tolist()) <= set(range(world))
+    for k in range(world):
+        lp = local[owner == k]
+        # each rank packs its own positions densely and in order
+        assert lp.tolist() == list(range(len(lp)))
+    # the rank-local block is the global "virtual" block of world * bs positions
+    assert (local // bs == p // (world * bs)).all()
+    # runs of interleave consecutive positions stay on one rank
+    assert (owner == O.dcp_owner((p // interleave) * interleave, world, interleave)).all()
+
+
+def test_dcp_slot_mapping_with_one_rank_is_plain():
+    rng = np.random.default_rng(21)
+    table = rng.permutation(np.arange(1, 41)).reshape(4, 10).astype(np.int32)
+    table[1, 3] = -1
+    req = rng.integers(-1, 5, size=300).astype(np.int32)
+    pos = rng.integers(-2, 12 * 16, size=300)
+    np.testing.assert_array_equal(O.compute_slot_mapping_dcp(req, pos, table, 16, 1, 0, 16, 333),
+                                  O.compute_slot_mapping(req, pos, table, 16, 333))
+
+
+def dcp_caches(rng, lens, bs, world, interleave, Hkv, D, dtype="f32"):
+    """Every rank's cache, written through the DCP slot mapping of each rank."""
+    B = len(lens)
+    vblocks = [-(-L // (world * bs)) for L in lens]
+    width = max(vblocks) + 1
+    total = sum(vblocks) + 2
+    table = random_tables(rng, B, width, [n * bs for n in vblocks], bs, total)
+    ks = [W.to_storage(rng.standard_normal((L, Hkv, D)).astype(np.float32), dtype) for L in lens]
+    vs = [W.to_storage(rng.standard_normal((L, Hkv, D)).astype(np.float32), dtype) for L in lens]
+    req = np.concatenate([np.full(L, r, np.int32) for r, L in enumerate(lens)])
+    pos = np.concatenate([np.arange(L) for L in lens])
+    knew, vnew = np.concatenate(ks), np.concatenate(vs)
+    wl = W.Workload(name="", index=0, seed=0, dtype=dtype, block_size=bs, total_blocks=total,
+                    num_kv_heads=Hkv, num_q_heads=Hkv, head_dim=D, q_len=1, num_reqs=0,
+                    computed=None, chunk_lens=None, seq_lens=np.zeros(1), block_table=None)
+    caches = []
+    for k in range(world):
+        slots = O.compute_slot_mapping_dcp(req, pos, table, bs, world, k, interleave)
+        kc, vc = wl.canary_cache(), wl.canary_cache()
+        O.reshape_and_cache(knew, vnew, slots, kc, vc)
+        caches.append((kc, vc, slots))
+    return table, ks, vs, caches, width
+
+
+@pytest.mark.parametrize("world,interleave", [(2, 1), (2, 16), (4, 8), (3, 16)])
+def test_dcp_every_token_stored_once_and_found(world, interleave):
+    rng = np.random.default_rng(22)
+    lens, bs = [1, 40, 200], 16
+    table, ks, _, caches, _ = dcp_caches(rng, lens, bs, world, interleave, 2, 4)
+    stored = sum((c[2] >= 0).sum() for c in caches)
+    assert stored == sum(lens)
+    for r, L in enumerate(lens):
+        for p in range(L):
+            k = int(O.dcp_owner(p, world, interleave))
+            lp = int(O.dcp_local_position(p, world, interleave))
+            row = caches[k][0][table[r, lp // bs], lp % bs]
+            np.testing.assert_array_equal(row, ks[r][p])
+
+
+@pytest.mark.parametrize("world,interleave,S_q", [(2, 1, 1), (2, 16, 3), (4, 8, 2), (3, 4, 1)])
+def test_dcp_merged_ranks_equal_full_attention(world, interleave, S_q):
+    rng = np.random.default_rng(23)
+    lens, bs, Hkv, G, D = [S_q, 37, 150, 301], 16, 2, 2, 8
+    table, ks, vs, caches, width = dcp_caches(rng, lens, bs, world, interleave, Hkv, D)
+    q = rng.standard_normal((len(lens), S_q, Hkv * G, D)).astype(np.float32)
+    parts = [O.paged_decode_attention_dcp(q, kc, vc, table, np.array(lens), width, 0.35, "f32",
+                                          world, k, interleave)
+             for k, (kc, vc, _) in enumerate(caches)]
+    merged = O.merge_lse([o for o, _ in parts], [l for _, l in parts])
+    for r, L in enumerate(lens):
+        want = sdpa_reference(O.widen(q[r], "f32"), O.widen(ks[r], "f32"), O.widen(vs[r], "f32"),
+                              L, S_q, 0.35, G)
+        np.testing.assert_allclose(merged[r], want, rtol=0, atol=1e-12)
+
+
+def test_dcp_lse_of_a_single_key_is_its_score():
+    rng = np.random.default_rng(24)
+    table, ks, _, caches, width = dcp_caches(rng, [1], 16, 2, 1, 1, 4)
+    q = rng.standard_normal((1, 1, 1, 4)).astype(np.float32)
+    out, lse = O.paged_decode_attention_dcp(q, caches[0][0], caches[0][1], table, np.array([1]),
+                                            width, 0.5, "f32", 2, 0, 1)
+    score = 0.5 * float(ks[0][0, 0].astype(np.float64) @ q[0, 0, 0].astype(np.float64))
+    assert abs(lse[0, 0, 0] - score) < 1e-12
+    _, lse1 = O.paged_decode_attention_dcp(q, caches[1][0], caches[1][1], table, np.array([1]),
+                                           width, 0.5, "f32", 2, 1, 1)
+    assert lse1[0, 0, 0] == -np.inf  # rank 1 stores nothing of a 1-token request
+
+
 def test_bf16_widening_matches_torch():
     bits = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x7F7F, 0x0001, 0x4049, 0xC2F7], np.uint16)
     rng = np.random.default_rng(0)
