@@ -79,6 +79,26 @@ def attention_bytes(w, walk_blocks: int, table_walk: bool) -> int:
     return blocks * per_block + q_out + 4 * w.num_rows
 
 
+def dcp_attention_bytes(w, world: int, rank: int, interleave: int) -> int:
+    """Algorithmic bytes of one rank's decode attention under context parallelism.
+
+    Per request: the whole blocks of this rank's cache holding its share of
+    the context (the positions below L it stores, packed densely), plus a
+    table entry each; q in; fp32 out and lse; seq_len.
+    """
+    per_block = 2 * w.block_size * w.num_kv_heads * w.head_dim * w.es + 4
+    span = world * interleave
+    blocks = 0
+    for r in range(w.num_rows):
+        L = int(w.seq_lens[r])
+        if L <= 0:
+            continue
+        local = (L // span) * interleave + min(max(L % span - rank * interleave, 0), interleave)
+        blocks += -(-local // w.block_size)
+    rows = w.num_rows * w.q_len * w.num_q_heads
+    return blocks * per_block + rows * w.head_dim * (w.es + 4) + 4 * rows + 4 * w.num_rows
+
+
 def window_attention_bytes(w, window: int, kv_off, width: int) -> int:
     """Algorithmic bytes of one sliding-window launch over a tail-trimmed table.
 
@@ -131,6 +151,10 @@ def main(argv=None) -> int:
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window layer: attend over a tail-trimmed table with this window "
                          "(paged_decode_attention_swa); the trim is host metadata built untimed")
+    ap.add_argument("--dcp", type=int, default=1,
+                    help="decode context parallelism over this many ranks: measure rank 0's share "
+                         "(its cache holds only its tokens; paged_decode_attention_dcp)")
+    ap.add_argument("--dcp-interleave", type=int, default=1)
     ap.add_argument("--separate-write", action="store_true",
                     help="step uses kv_slot_mapping + kv_cache_write (two launches) instead of "
                          "kv_slot_mapping_cache_write")
@@ -162,7 +186,10 @@ def main(argv=None) -> int:
 
     # ---- set-up (untimed): caches, prefill, rotation copies ---------------
     t_setup = time.time()
-    s = dev.build(w, cuda, threads=16)
+    dcp = (args.dcp, 0, args.dcp_interleave) if args.dcp > 1 else None
+    if dcp and (args.window or args.walk != "context"):
+        raise SystemExit("--dcp takes the context walk without a window")
+    s = dev.build(w, cuda, threads=16, dcp=dcp)
     table_walk = args.walk != "context"
     # tokens each request holds before its decode tokens (prior context + ragged chunk)
     before = (w.computed + w.chunk_lens)[: w.num_reqs]
@@ -181,6 +208,9 @@ def main(argv=None) -> int:
     T = int(step_req.numel())
     T_live = int((step_req >= 0).sum().item())
     a_bytes = attention_bytes(w, walk_blocks, table_walk)
+    if dcp:
+        a_bytes = dcp_attention_bytes(w, *dcp)
+        walk_blocks = int(s.block_table.shape[1])
     if args.window:
         if table_walk:
             raise SystemExit("--window takes the context walk")
@@ -212,7 +242,15 @@ def main(argv=None) -> int:
     write_args = [(step_k.data_ptr(), step_v.data_ptr(), slots.data_ptr(), T, kc.data_ptr(),
                    vc.data_ptr(), w.total_blocks, w.block_size, w.num_kv_heads, w.head_dim, dt, sp)
                   for kc, vc in caches]
-    if args.window:
+    if dcp:
+        lse = torch.empty((w.num_rows, w.q_len, w.num_q_heads), dtype=torch.float32, device=cuda)
+        f_attn = lib.paged_decode_attention_dcp
+        attn_args = [(s.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), s.block_table.data_ptr(),
+                      int(stride), int(walk_blocks), s.seq_lens.data_ptr(), w.num_rows, w.q_len,
+                      w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.total_blocks,
+                      w.scale, dt, dcp[0], dcp[1], dcp[2], ws.data_ptr(), int(ws.numel()),
+                      out.data_ptr(), lse.data_ptr(), sp) for kc, vc in caches]
+    elif args.window:
         f_attn = lib.paged_decode_attention_swa
         wt = int(trimmed.shape[1])
         attn_args = [(s.q.data_ptr(), kc.data_ptr(), vc.data_ptr(), d_trim.data_ptr(), wt, wt,
@@ -232,6 +270,9 @@ def main(argv=None) -> int:
 
     f_slot, f_write = lib.kv_slot_mapping, lib.kv_cache_write
     f_fused = lib.kv_slot_mapping_cache_write
+    f_slot_dcp = lib.kv_slot_mapping_dcp
+    if dcp:
+        slot_dcp_args = slot_args[:8] + tuple(dcp) + slot_args[8:]
     fused_args = [slot_args[:9] + (step_k.data_ptr(), step_v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
                                    w.total_blocks, w.num_kv_heads, w.head_dim, dt, sp)
                   for kc, vc in caches]
@@ -241,7 +282,10 @@ def main(argv=None) -> int:
         # host: the per-step bucket pick the pages describe (feature off unless bucketed)
         f_select(max_ctx, num_spec, buckets, max_model_len, w.block_size)
         j = i % R
-        if args.separate_write:
+        if dcp:
+            st = f_slot_dcp(*slot_dcp_args)
+            st |= f_write(*write_args[j])
+        elif args.separate_write:
             st = f_slot(*slot_args)
             st |= f_write(*write_args[j])
         else:
@@ -298,7 +342,7 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
 
     write_bytes = cache_write_bytes(w, T_live, T)
-    if not args.separate_write:
+    if not (args.separate_write or dcp):
         write_bytes -= 8 * T  # the one-launch write keeps the slots in registers
     step_bytes = slot_map_bytes(T) + write_bytes + a_bytes
     decode_tokens = w.num_reqs * w.q_len
@@ -327,7 +371,8 @@ def main(argv=None) -> int:
             "bucket_len": int(bucket_len),
             "step_tokens": T,
             "cache_copies_rotated": R,
-            "step_write": "separate" if args.separate_write else "fused",
+            "step_write": "separate" if (args.separate_write or dcp) else "fused",
+            "dcp": {"world": dcp[0], "rank": dcp[1], "interleave": dcp[2]} if dcp else None,
             "parallelism": "single GPU",
         },
         "attention_gbps": round(attn_gbps, 2),
@@ -349,11 +394,12 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(args.workload,
-                                        f"window{args.window}" if args.window else args.walk),
+                                        f"window{args.window}" if args.window else
+                                        (f"dcp{dcp[0]}" if dcp else args.walk)),
         },
         "setup_s": round(t_setup, 2),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not dcp:
         result["cpu_baseline"] = cpu_baseline(w, s.host_table, walk_blocks, args.cpu_seconds,
                                               window=args.window)
     print(json.dumps(result), flush=True)

@@ -19,6 +19,9 @@ from ._lib import (  # noqa: F401
     kv_map_to_kernel_blocks,
     kv_slot_mapping,
     kv_slot_mapping_cache_write,
+    kv_slot_mapping_dcp,
+    paged_decode_attention_dcp,
+    decode_lse_merge,
     load,
     make_workspace,
     paged_decode_attention,

@@ -38,6 +38,9 @@ EXPORTS = (
     "paged_decode_attention",
     "paged_decode_attention_swa",
     "kv_swa_tail_trim",
+    "kv_slot_mapping_dcp",
+    "paged_decode_attention_dcp",
+    "decode_lse_merge",
 )
 
 
@@ -83,9 +86,16 @@ def _lib():
             ctypes.c_int, vp, sz, vp, vp,
         ]
         lib.kv_swa_tail_trim.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, i32, vp, vp]
+        lib.kv_slot_mapping_dcp.argtypes = [vp, vp, i64, i64, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+        lib.paged_decode_attention_dcp.argtypes = [
+            vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32, i64, f32, ctypes.c_int,
+            i32, i32, i32, vp, sz, vp, vp, vp,
+        ]
+        lib.decode_lse_merge.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp]
         for name in ("kv_slot_mapping", "kv_cache_write", "kv_slot_mapping_cache_write",
                      "select_ctx_bucket", "kv_map_to_kernel_blocks", "paged_decode_attention",
-                     "paged_decode_attention_swa", "kv_swa_tail_trim"):
+                     "paged_decode_attention_swa", "kv_swa_tail_trim", "kv_slot_mapping_dcp",
+                     "paged_decode_attention_dcp", "decode_lse_merge"):
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -299,6 +309,78 @@ def paged_decode_attention_swa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
         _dev(out, "out", torch.float32), _stream(q, stream))
     _check(st, "paged_decode_attention_swa")
     return out
+
+
+def kv_slot_mapping_dcp(req_indices: torch.Tensor, positions: torch.Tensor,
+                        block_table: torch.Tensor, block_size: int, cp_world_size: int,
+                        cp_rank: int, cp_interleave: int, slot_mapping: Optional[torch.Tensor] = None,
+                        max_num_tokens: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Slots on one context-parallel rank (others' tokens -1); see kvslot.h."""
+    T = int(req_indices.numel())
+    if slot_mapping is None:
+        n = T if max_num_tokens is None else int(max_num_tokens)
+        slot_mapping = torch.empty(n, dtype=torch.int64, device=block_table.device)
+    rows, stride = block_table.shape
+    st = _lib().kv_slot_mapping_dcp(
+        _dev(req_indices, "req_indices", torch.int32, 1), _dev(positions, "positions", torch.int64, 1),
+        T, int(slot_mapping.numel()), _dev(block_table, "block_table", torch.int32, 2),
+        int(rows), int(stride), int(block_size), int(cp_world_size), int(cp_rank), int(cp_interleave),
+        _dev(slot_mapping, "slot_mapping", torch.int64, 1), _stream(block_table, stream))
+    _check(st, "kv_slot_mapping_dcp")
+    return slot_mapping
+
+
+def paged_decode_attention_dcp(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                               cp_world_size: int, cp_rank: int, cp_interleave: int,
+                               walk_blocks: Optional[int] = None,
+                               workspace: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                               stream=None):
+    """One rank's attention over its keys; returns (out, lse). See kvslot.h."""
+    B, Sq, Hq, D = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != D or q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype \
+            or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("paged_decode_attention_dcp: shape or dtype mismatch")
+    if block_table.shape[0] < B or seq_lens.numel() < B:
+        raise ValueError("paged_decode_attention_dcp: too few rows")
+    stride = int(block_table.shape[1])
+    walk = stride if walk_blocks is None else int(walk_blocks)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Sq, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(B, Sq, Hq, hkv, D, q.device)
+    st = _lib().paged_decode_attention_dcp(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table", torch.int32, 2), stride, walk,
+        _dev(seq_lens, "seq_lens", torch.int32), int(B), int(Sq), int(Hq), int(hkv), int(D), int(bs),
+        int(nb), float(scale), _kvs_dtype(k_cache), int(cp_world_size), int(cp_rank),
+        int(cp_interleave), _dev(workspace, "workspace", torch.uint8), int(workspace.numel()),
+        _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32), _stream(q, stream))
+    _check(st, "paged_decode_attention_dcp")
+    return out, lse
+
+
+def decode_lse_merge(outs: torch.Tensor, lses: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, stream=None):
+    """Merge [world, ..., D] outputs and [world, ...] lse into (out, lse); see kvslot.h."""
+    world = int(outs.shape[0])
+    D = int(outs.shape[-1])
+    rows = int(outs[0].numel()) // D if world else 0
+    if tuple(lses.shape) != tuple(outs.shape[:-1]):
+        raise ValueError("decode_lse_merge: lses must match outs without the last dim")
+    if out is None:
+        out = torch.empty(outs.shape[1:], dtype=torch.float32, device=outs.device)
+    if lse is None:
+        lse = torch.empty(lses.shape[1:], dtype=torch.float32, device=outs.device)
+    st = _lib().decode_lse_merge(_dev(outs, "outs", torch.float32), _dev(lses, "lses", torch.float32),
+                                 world, rows, D, _dev(out, "out", torch.float32),
+                                 _dev(lse, "lse", torch.float32), _stream(outs, stream))
+    _check(st, "decode_lse_merge")
+    return out, lse
 
 
 def kv_swa_tail_trim(block_table: np.ndarray, seq_lens, q_len: int, sliding_window: int,

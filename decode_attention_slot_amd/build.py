@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvslot.so")
 
-SOURCES = ["abi.cpp", "slot_mapping.hip", "cache_write.hip", "slot_write.hip", "paged_decode.hip"]
+SOURCES = ["abi.cpp", "slot_mapping.hip", "cache_write.hip", "slot_write.hip", "paged_decode.hip", "lse_merge.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

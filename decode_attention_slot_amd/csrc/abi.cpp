@@ -31,13 +31,17 @@ namespace {
 int decode_common(const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_table, int32_t table_stride, int32_t walk_blocks,
                   const int32_t* seq_lens, const int32_t* kv_pos_offset, int32_t window,
+                  int32_t cp_world, int32_t cp_rank, int32_t cp_interleave,
                   int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                   int32_t head_dim, int32_t block_size, int64_t total_blocks, float scale,
                   kvs_dtype dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
-                  float* out, void* stream) {
+                  float* out, float* lse, void* stream) {
   if (num_seqs < 0 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
       block_size < 1 || table_stride < 1 || walk_blocks < 0 || walk_blocks > table_stride ||
-      total_blocks < 1 || !isfinite(scale) || window < 0)
+      total_blocks < 1 || !isfinite(scale) || window < 0 || cp_world < 1 || cp_rank < 0 ||
+      cp_rank >= cp_world || cp_interleave < 1)
+    return KVS_EINVAL;
+  if (!is_pow2(cp_interleave) || (block_size > 0 && block_size % cp_interleave != 0))
     return KVS_EINVAL;
   if (num_q_heads % num_kv_heads != 0) return KVS_EINVAL;
   if (flags & ~KVS_WALK_TABLE) return KVS_EINVAL;
@@ -46,7 +50,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
   if (!is_pow2(block_size) || block_size < 16 || block_size > 256) return KVS_EUNSUPPORTED;
   if ((int64_t)(num_q_heads / num_kv_heads) * q_len > kMaxRows) return KVS_EUNSUPPORTED;
   if (num_seqs > kMaxSeqs) return KVS_EUNSUPPORTED;
-  if ((int64_t)table_stride * block_size > INT_MAX / 2) return KVS_EUNSUPPORTED;
+  if ((int64_t)table_stride * block_size * cp_world > INT_MAX / 2) return KVS_EUNSUPPORTED;
   // the batch's 16-token tiles are counted in 32 bits, with headroom
   if ((int64_t)num_seqs * (walk_blocks * (int64_t)(block_size / 16) + 1) > INT_MAX / 2)
     return KVS_EUNSUPPORTED;
@@ -65,6 +69,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
   p.seq_lens = seq_lens;
   p.kv_pos_offset = kv_pos_offset;
   p.out = out;
+  p.lse_out = lse;
   p.chunk_meta = (int32_t*)workspace;
   p.partials = (float*)((char*)workspace + kvs::decode_meta_bytes(num_seqs));
   p.total_blocks = total_blocks;
@@ -77,6 +82,9 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
   p.head_dim = head_dim;
   p.block_size = block_size;
   p.window = window;
+  p.cp_world = cp_world;
+  p.cp_rank = cp_rank;
+  p.cp_ishift = __builtin_ctz((unsigned)cp_interleave);
   p.max_slices = kvs::decode_max_slices(num_kv_heads);
   p.min_tiles = 8;  // 128 tokens: partial traffic stays a few percent of the KV a slice reads
   p.start_tiles = 2;  // a segment start costs about two tiles' streaming time
@@ -135,6 +143,25 @@ int kv_cache_write(const void* k_new, const void* v_new, const int64_t* slot_map
   return launch_status(kvs::launch_cache_write(k_new, v_new, slot_mapping, num_tokens, k_cache,
                                                v_cache, total_blocks * block_size,
                                                (int32_t)row_bytes, (hipStream_t)stream));
+}
+
+int kv_slot_mapping_dcp(const int32_t* req_indices, const int64_t* positions, int64_t num_tokens,
+                        int64_t max_num_tokens, const int32_t* block_table, int32_t table_rows,
+                        int32_t table_stride, int32_t block_size, int32_t cp_world_size,
+                        int32_t cp_rank, int32_t cp_interleave, int64_t* slot_mapping,
+                        void* stream) {
+  if (num_tokens < 0 || max_num_tokens < num_tokens || table_rows < 0 || table_stride < 1 ||
+      block_size < 1 || cp_world_size < 1 || cp_rank < 0 || cp_rank >= cp_world_size ||
+      cp_interleave < 1)
+    return KVS_EINVAL;
+  if (!is_pow2(block_size) || !is_pow2(cp_interleave) || block_size % cp_interleave != 0)
+    return KVS_EINVAL;
+  if (max_num_tokens > 0 && !slot_mapping) return KVS_EINVAL;
+  if (num_tokens > 0 && (!req_indices || !positions)) return KVS_EINVAL;
+  if (table_rows > 0 && !block_table) return KVS_EINVAL;
+  return launch_status(kvs::launch_slot_mapping_dcp(
+      req_indices, positions, num_tokens, max_num_tokens, block_table, table_rows, table_stride,
+      block_size, cp_world_size, cp_rank, cp_interleave, slot_mapping, (hipStream_t)stream));
 }
 
 int kv_slot_mapping_cache_write(const int32_t* req_indices, const int64_t* positions,
@@ -246,9 +273,9 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
                            kvs_dtype dtype, uint32_t flags, void* workspace,
                            size_t workspace_bytes, float* out, void* stream) {
   return decode_common(q, k_cache, v_cache, block_table, table_stride, walk_blocks, seq_lens,
-                       nullptr, 0, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim,
+                       nullptr, 0, 1, 0, 1, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim,
                        block_size, total_blocks, scale, dtype, flags, workspace,
-                       workspace_bytes, out, stream);
+                       workspace_bytes, out, nullptr, stream);
 }
 
 int paged_decode_attention_swa(const void* q, const void* k_cache, const void* v_cache,
@@ -261,9 +288,33 @@ int paged_decode_attention_swa(const void* q, const void* k_cache, const void* v
                                void* workspace, size_t workspace_bytes, float* out,
                                void* stream) {
   return decode_common(q, k_cache, v_cache, block_table, table_stride, walk_blocks, seq_lens,
-                       kv_pos_offset, sliding_window, num_seqs, q_len, num_q_heads,
+                       kv_pos_offset, sliding_window, 1, 0, 1, num_seqs, q_len, num_q_heads,
                        num_kv_heads, head_dim, block_size, total_blocks, scale, dtype, 0,
-                       workspace, workspace_bytes, out, stream);
+                       workspace, workspace_bytes, out, nullptr, stream);
+}
+
+int paged_decode_attention_dcp(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, int32_t table_stride,
+                               int32_t walk_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t total_blocks,
+                               float scale, kvs_dtype dtype, int32_t cp_world_size,
+                               int32_t cp_rank, int32_t cp_interleave, void* workspace,
+                               size_t workspace_bytes, float* out, float* lse, void* stream) {
+  if (num_seqs > 0 && !lse) return KVS_EINVAL;
+  return decode_common(q, k_cache, v_cache, block_table, table_stride, walk_blocks, seq_lens,
+                       nullptr, 0, cp_world_size, cp_rank, cp_interleave, num_seqs, q_len,
+                       num_q_heads, num_kv_heads, head_dim, block_size, total_blocks, scale,
+                       dtype, 0, workspace, workspace_bytes, out, lse, stream);
+}
+
+int decode_lse_merge(const float* outs, const float* lses, int32_t world, int64_t rows,
+                     int32_t head_dim, float* out, float* lse, void* stream) {
+  if (world < 1 || rows < 0 || head_dim < 4 || head_dim % 4 != 0) return KVS_EINVAL;
+  if (rows > 0 && (!outs || !lses || !out)) return KVS_EINVAL;
+  if (rows > INT64_MAX / head_dim / world) return KVS_EINVAL;
+  return launch_status(
+      kvs::launch_lse_merge(outs, lses, world, rows, head_dim, out, lse, (hipStream_t)stream));
 }
 
 int kv_swa_tail_trim(const int32_t* src, int32_t rows, int32_t src_stride,

@@ -17,6 +17,16 @@ hipError_t launch_cache_write(const void* k_new, const void* v_new, const int64_
                               int64_t num_tokens, void* k_cache, void* v_cache,
                               int64_t total_slots, int32_t row_bytes, hipStream_t stream);
 
+hipError_t launch_slot_mapping_dcp(const int32_t* req_indices, const int64_t* positions,
+                                   int64_t num_tokens, int64_t max_num_tokens,
+                                   const int32_t* block_table, int32_t table_rows,
+                                   int32_t table_stride, int32_t block_size, int32_t world,
+                                   int32_t rank, int32_t interleave, int64_t* slot_mapping,
+                                   hipStream_t stream);
+
+hipError_t launch_lse_merge(const float* outs, const float* lses, int32_t world, int64_t rows,
+                            int32_t head_dim, float* out, float* lse, hipStream_t stream);
+
 hipError_t launch_slot_write(const int32_t* req_indices, const int64_t* positions,
                              int64_t num_tokens, int64_t max_num_tokens,
                              const int32_t* block_table, int32_t table_rows,
@@ -33,6 +43,7 @@ struct DecodeParams {
   const int32_t* seq_lens;
   const int32_t* kv_pos_offset;  // per request, position of table column 0; null: 0
   float* out;
+  float* lse_out;  // optional [num_seqs][q_len][num_q_heads]: natural-log sum of exp(scores)
   float* partials;      // [slots][num_kv_heads][rows][head_dim + 4]
   int32_t* chunk_meta;  // [num_seqs][2]: first partial slot and partial count
   int64_t total_blocks;
@@ -45,6 +56,7 @@ struct DecodeParams {
   int32_t head_dim;
   int32_t block_size;
   int32_t window;  // sliding window in positions; 0: none
+  int32_t cp_world, cp_rank, cp_ishift;  // context parallelism (1, 0, 0: none)
   int32_t max_slices;  // partial storage bound on the slices (per head group)
   int32_t slices;      // set by the launcher: slices the batch's tiles are cut into
   int32_t min_tiles;   // never cut a slice shorter than this many 16-token tiles

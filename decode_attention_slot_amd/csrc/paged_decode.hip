@@ -78,7 +78,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kFlagWalkTable = 0x1u;
 // Never set by the host. Testing it keeps the table-walk loads alive.
 constexpr uint32_t kFlagSink = 0x80000000u;
-constexpr int kContextWalk = 0, kTableWalk = 1, kWindow = 2;  // pass-1 modes
+// pass-1 modes: context walk, fixed-shape table walk, and the general walk
+// (sliding window, tail-trimmed table, context-parallel share)
+constexpr int kContextWalk = 0, kTableWalk = 1, kGeneral = 2;
 constexpr int kTile = 16;
 constexpr int kStage = 256;  // block ids staged in LDS at a time
 constexpr int kDepth = 2;    // tiles in flight per wave
@@ -132,27 +134,51 @@ struct ReqSpan {
   int off, E, t_lo, n;
 };
 
-template <bool SWA>
-__device__ __forceinline__ ReqSpan request_span(const int32_t* kv_pos_offset, int32_t window,
-                                                int r, int L, int walk_tok, int bs, int Sq) {
+// Under context parallelism the walk runs over this rank's own positions
+// (its cache's local positions, 0 .. E - 1): the global positions below
+// min(L, walk_blocks * world * bs) that this rank stores.
+template <bool GEN>
+__device__ __forceinline__ ReqSpan request_span(const DecodeParams& p, int r, int L, int walk_tok,
+                                                int bs, int Sq) {
   ReqSpan sp;
-  const int off = SWA && kv_pos_offset ? kv_pos_offset[r] : 0;
+  if (GEN && p.cp_world > 1) {
+    const int64_t eg = min((int64_t)L, (int64_t)walk_tok * p.cp_world);
+    const int64_t run = (int64_t)1 << p.cp_ishift;
+    const int64_t span = run * p.cp_world;
+    const int64_t rem = eg > 0 ? eg % span - (int64_t)p.cp_rank * run : 0;
+    const int64_t e_loc = eg > 0 ? (eg / span) * run + min(max(rem, (int64_t)0), run) : 0;
+    sp.off = 0;
+    sp.E = (int)min(e_loc, (int64_t)INT32_MAX - 64);
+    sp.t_lo = 0;
+    sp.n = (sp.E + 15) / 16;
+    return sp;
+  }
+  const int32_t* kv_pos_offset = p.kv_pos_offset;
+  const int32_t window = p.window;
+  const int off = GEN && kv_pos_offset ? kv_pos_offset[r] : 0;
   sp.off = max(off, 0) & ~(bs - 1);
   int64_t E = min((int64_t)L, (int64_t)sp.off + walk_tok);
   E = min(E, (int64_t)INT32_MAX - 64);
   sp.E = L <= 0 ? 0 : (int)E;
   int64_t start = sp.off;
-  if (SWA && window > 0) start = max(start, (int64_t)L - Sq - window + 1);
+  if (GEN && window > 0) start = max(start, (int64_t)L - Sq - window + 1);
   sp.t_lo = (int)(start / 16);
   sp.n = sp.E > start ? (sp.E + 15) / 16 - sp.t_lo : 0;
   return sp;
 }
 
+// Natural-log sum of exp(scores) of a row from its running state: max m
+// (log2 units) and sum l of exp2(score - m); -inf when the row saw no key.
+__device__ __forceinline__ float row_lse(float m, float l) {
+  return l > 0.0f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// MODE: kContextWalk, kTableWalk (the fixed-shape walk) or kWindow (a
-// sliding window over a possibly tail-trimmed table).
+// MODE: kContextWalk, kTableWalk (the fixed-shape walk) or kGeneral (a
+// sliding window over a possibly tail-trimmed table, or one rank's share
+// under context parallelism).
 template <bool BF16, int D, int NW, int MODE>
 __global__ void __launch_bounds__(NW * 64, 2)
 paged_decode_kernel(const DecodeParams p, int bs_shift) {
@@ -164,7 +190,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int PSTRIDE = D + 4;         // floats per partial row (acc, m, l, pad)
   constexpr int NTHR = NW * 64;
   constexpr bool TW = MODE == kTableWalk;
-  constexpr bool SWA = MODE == kWindow;
+  constexpr bool GEN = MODE == kGeneral;
   constexpr uint32_t kNegZero = BF16 ? 0x80008000u : 0x80000000u;
   static_assert(NP >= 1 && NVW >= 2, "unsupported head_dim");
   struct TileBuf {
@@ -210,7 +236,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // request carries that many fewer tiles. s_pref holds these units.
   const int X = p.start_tiles;
   for (int rr = threadIdx.x; rr < B; rr += NTHR)
-    s_pref[rr] = request_span<SWA>(p.kv_pos_offset, p.window, rr, p.seq_lens[rr], walk_tok, bs, Sq).n;
+    s_pref[rr] = request_span<GEN>(p, rr, p.seq_lens[rr], walk_tok, bs, Sq).n;
   if (threadIdx.x == 0) {
     s_first[0] = 0;
     s_first[1] = 0;
@@ -345,7 +371,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // ---- one segment: tiles [t0, t1) of request r (nr tiles, tile 0 at unit pr) --
   auto segment = [&](int r, int t0, int t1, int nr, int pr) {
     const int L = uniform(p.seq_lens[r]);
-    const ReqSpan sp = request_span<SWA>(p.kv_pos_offset, p.window, r, L, walk_tok, bs, Sq);
+    const ReqSpan sp = request_span<GEN>(p, r, L, walk_tok, bs, Sq);
     const int E = uniform(sp.E);
     const int off = uniform(sp.off);
     const int t_lo = uniform(sp.t_lo);
@@ -357,11 +383,21 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     const int qpos_min = L - Sq;
     // sliding window: row rho sees keys from qpos - window + 1; every row
     // does from L - window on
-    const int qlo = SWA && p.window > 0
+    const int qlo = GEN && p.window > 0
                         ? (int)max((int64_t)qpos - p.window + 1, (int64_t)INT32_MIN)
                         : INT32_MIN;
     const int all_lo =
-        SWA && p.window > 0 ? (int)max((int64_t)L - p.window, (int64_t)INT32_MIN) : INT32_MIN;
+        GEN && p.window > 0 ? (int)max((int64_t)L - p.window, (int64_t)INT32_MIN) : INT32_MIN;
+    // Global position of a walked position: itself, except under context
+    // parallelism, where the walk runs over this rank's local positions.
+    auto gpos = [&](int lp) -> int64_t {
+      if constexpr (GEN) {
+        const int64_t run = lp >> p.cp_ishift;
+        return (((run * p.cp_world) + p.cp_rank) << p.cp_ishift) + (lp & ((1 << p.cp_ishift) - 1));
+      } else {
+        return lp;
+      }
+    };
     u32x4 qp[NP];
     {
       const char* qrow = (const char*)p.q +
@@ -401,14 +437,14 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       float sx[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sx[i] = s[i] * p.scale_log2;
-      const bool full = active && (tt + kTile <= E) && (tt + kTile - 1 <= qpos_min) &&
-                        (!SWA || tt >= all_lo);
+      const bool full = active && (tt + kTile <= E) && (gpos(tt + kTile - 1) <= qpos_min) &&
+                        (!GEN || tt >= all_lo);
       if (!full) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = tt + 4 * jg + i;
           const bool kv_ok = active && pos < E;
-          if (!(kv_ok && pos <= qpos && (!SWA || pos >= qlo))) sx[i] = -INFINITY;
+          if (!(kv_ok && gpos(pos) <= qpos && (!GEN || pos >= qlo))) sx[i] = -INFINITY;
           if (!kv_ok) {
 #pragma unroll
             for (int w = 0; w < NVW; ++w) bf.v[i][w] = kNegZero;
@@ -472,6 +508,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
           *(f32x4*)(o + i * NT + n0) = v;
         }
       }
+      if (p.lse_out && jg == 0)
+        p.lse_out[((int64_t)r * Sq + jrow) * Hq + (int64_t)g * G + hh] = row_lse(m_run, l_tot);
       return;
     }
     // split: publish this segment's partial state
@@ -515,6 +553,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       const int row_floats = Sq * Hq * D;
       float* o = p.out + (int64_t)r * row_floats;
       for (int i = threadIdx.x; i < row_floats; i += NTHR) o[i] = 0.0f;
+      if (p.lse_out)
+        for (int i = threadIdx.x; i < Sq * Hq; i += NTHR) p.lse_out[(int64_t)r * Sq * Hq + i] = -INFINITY;
       if (threadIdx.x == 0) p.chunk_meta[2 * r + 1] = 0;
     }
   }
@@ -670,6 +710,8 @@ paged_decode_combine_kernel(const DecodeParams p) {
       const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
       float* orow = p.out + (((int64_t)r * Sq + jr) * Hq + (int64_t)g * G + hr) * D;
       *(f32x4*)(orow + (f - row * F4ROW) * 4) = ot * inv;
+      if (p.lse_out && f == row * F4ROW)
+        p.lse_out[((int64_t)r * Sq + jr) * Hq + (int64_t)g * G + hr] = row_lse(M, Lt);
     }
     __syncthreads();
   }
@@ -715,8 +757,8 @@ hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t strea
   const size_t lds = decode_lds_bytes(p.num_seqs);
   if (p.flags & kFlagWalkTable)
     paged_decode_kernel<BF16, D, NW, kTableWalk><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
-  else if (p.window > 0 || p.kv_pos_offset)
-    paged_decode_kernel<BF16, D, NW, kWindow><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+  else if (p.window > 0 || p.kv_pos_offset || p.cp_world > 1)
+    paged_decode_kernel<BF16, D, NW, kGeneral><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
   else
     paged_decode_kernel<BF16, D, NW, kContextWalk><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
   e = hipGetLastError();

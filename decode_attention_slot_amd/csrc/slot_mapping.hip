@@ -31,7 +31,40 @@ slot_mapping_kernel(const int32_t* __restrict__ req_indices, const int64_t* __re
   }
 }
 
+__global__ void __launch_bounds__(256)
+slot_mapping_dcp_kernel(const int32_t* __restrict__ req_indices,
+                        const int64_t* __restrict__ positions, int64_t num_tokens,
+                        int64_t max_num_tokens, const int32_t* __restrict__ block_table,
+                        int32_t table_rows, int32_t table_stride, int32_t block_size,
+                        int32_t block_shift, int32_t world, int32_t rank, int32_t interleave_shift,
+                        int64_t* __restrict__ slot_mapping) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < max_num_tokens; t += stride) {
+    slot_mapping[t] = t < num_tokens
+                          ? token_slot_dcp(req_indices[t], positions[t], block_table, table_rows,
+                                           table_stride, block_size, block_shift, world, rank,
+                                           interleave_shift)
+                          : -1;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_slot_mapping_dcp(const int32_t* req_indices, const int64_t* positions,
+                                   int64_t num_tokens, int64_t max_num_tokens,
+                                   const int32_t* block_table, int32_t table_rows,
+                                   int32_t table_stride, int32_t block_size, int32_t world,
+                                   int32_t rank, int32_t interleave, int64_t* slot_mapping,
+                                   hipStream_t stream) {
+  if (max_num_tokens == 0) return hipSuccess;
+  int64_t blocks = (max_num_tokens + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  slot_mapping_dcp_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+      req_indices, positions, num_tokens, max_num_tokens, block_table, table_rows, table_stride,
+      block_size, __builtin_ctz((unsigned)block_size), world, rank,
+      __builtin_ctz((unsigned)interleave), slot_mapping);
+  return hipGetLastError();
+}
 
 hipError_t launch_slot_mapping(const int32_t* req_indices, const int64_t* positions,
                                int64_t num_tokens, int64_t max_num_tokens,

@@ -308,6 +308,79 @@ int kv_swa_tail_trim(const int32_t* src, int32_t rows, int32_t src_stride,
                      int32_t block_size, int32_t* dst, int32_t dst_stride, int32_t* kv_pos_offset,
                      int32_t* width_out);
 
+/*
+ * Decode context parallelism, one rank's part ("Block table: logical token
+ * -> physical KV block", design motivation: with TOTAL_CP_WORLD_SIZE,
+ * TOTAL_CP_RANK and CP_KV_CACHE_INTERLEAVE_SIZE the slot kernel writes a
+ * real slot only for the tokens its rank stores and PAD_ID for the others).
+ * The page prints no formula; the reading here: runs of cp_interleave
+ * consecutive positions go round-robin to the cp_world_size ranks (rank of
+ * position p: (p / cp_interleave) % cp_world_size), and each rank packs
+ * its runs densely, so position p lives in its rank's cache at local
+ * position lp = (p / (cp_world_size * cp_interleave)) * cp_interleave +
+ * p % cp_interleave. lp / block_size = p / (cp_world_size * block_size): the
+ * ranks share one table row, a column standing for cp_world_size *
+ * block_size consecutive positions of which each rank stores block_size.
+ * cp_interleave is a power of two dividing block_size.
+ */
+
+/*
+ * kv_slot_mapping_dcp - kv_slot_mapping on rank cp_rank: a token this rank
+ * stores gets table[r][lp / block_size] * block_size + lp % block_size
+ * (with every -1 rule of kv_slot_mapping), every other token -1, and the
+ * tail of the buffer -1. The cache write is then kv_cache_write.
+ * Errors: as kv_slot_mapping; KVS_EINVAL also for cp_world_size < 1,
+ * cp_rank outside [0, cp_world_size), a block_size that is not a power of
+ * two, or a cp_interleave that is not a power of two dividing block_size.
+ */
+int kv_slot_mapping_dcp(const int32_t* req_indices, const int64_t* positions, int64_t num_tokens,
+                        int64_t max_num_tokens, const int32_t* block_table, int32_t table_rows,
+                        int32_t table_stride, int32_t block_size, int32_t cp_world_size,
+                        int32_t cp_rank, int32_t cp_interleave, int64_t* slot_mapping,
+                        void* stream);
+
+/*
+ * paged_decode_attention_dcp - one rank's decode attention over the keys it
+ * stores: the positions p < seq_lens[r] (and below walk_blocks *
+ * cp_world_size * block_size) that rank cp_rank owns, read from this
+ * rank's caches at their local positions. Queries keep their global
+ * positions (L - q_len + j) and the causal rule. Writes out, normalised
+ * over this rank's keys, and lse[r][j][h], the natural-log sum of
+ * exp(scale * <q, k>) over them (-inf, with zero output, for a row that
+ * sees none of this rank's keys): the partial state the ranks exchange and
+ * decode_lse_merge combines.
+ *
+ *   lse  float [num_seqs][q_len][num_q_heads], device, written
+ * Other arguments, the workspace contract and the supported shapes: as
+ * paged_decode_attention (context walk).
+ * Errors: as paged_decode_attention; KVS_EINVAL also for a null lse and
+ * the cp_* rules of kv_slot_mapping_dcp.
+ */
+int paged_decode_attention_dcp(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, int32_t table_stride,
+                               int32_t walk_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t total_blocks,
+                               float scale, kvs_dtype dtype, int32_t cp_world_size,
+                               int32_t cp_rank, int32_t cp_interleave, void* workspace,
+                               size_t workspace_bytes, float* out, float* lse, void* stream);
+
+/*
+ * decode_lse_merge - combine the ranks' (out, lse) partial states into the
+ * attention over all their keys: out = sum_k exp(lse_k - lse) out_k with
+ * lse = log sum_k exp(lse_k); ranks with lse_k = -inf contribute nothing; a
+ * row no rank saw stays zero with lse -inf.
+ *
+ *   outs  float [world][rows][head_dim], device (rows = requests * q_len * heads)
+ *   lses  float [world][rows], device
+ *   out   float [rows][head_dim], device, written
+ *   lse   float [rows], device, written; may be NULL
+ * Errors: KVS_EINVAL for world < 1, rows < 0, head_dim not a positive
+ * multiple of 4, or null pointers when rows > 0.
+ */
+int decode_lse_merge(const float* outs, const float* lses, int32_t world, int64_t rows,
+                     int32_t head_dim, float* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -195,6 +195,33 @@ def test_swa_entry_points_reject_bad_scalars(K):
     assert swa(d=96) == -2
 
 
+def test_dcp_entry_points_reject_bad_scalars(K):
+    lib = K.load()
+    null = None
+
+    def sm(world=2, rank=0, il=16, bs=64):
+        return lib.kv_slot_mapping_dcp(null, null, 0, 0, null, 0, 1, bs, world, rank, il, null, null)
+
+    assert sm() == 0
+    assert sm(world=0) == -1 and sm(rank=2) == -1 and sm(rank=-1) == -1
+    assert sm(il=3) == -1 and sm(il=128) == -1 and sm(il=0) == -1 and sm(bs=48) == -1
+
+    def att(**kw):
+        a = dict(B=1, world=2, rank=0, il=16, lse=null)
+        a.update(kw)
+        return lib.paged_decode_attention_dcp(null, null, null, null, 4, 4, null, a["B"], 1, 8, 2, 128,
+                                              64, 10, 0.1, 1, a["world"], a["rank"], a["il"], null,
+                                              1 << 30, null, a["lse"], null)
+
+    assert att() == -1                # null lse / pointers
+    assert att(B=0) == 0
+    assert att(B=0, rank=3) == -1
+    assert lib.decode_lse_merge(null, null, 0, 1, 128, null, null, null) == -1
+    assert lib.decode_lse_merge(null, null, 2, 1, 6, null, null, null) == -1
+    assert lib.decode_lse_merge(null, null, 2, 1, 128, null, null, null) == -1
+    assert lib.decode_lse_merge(null, null, 2, 0, 128, null, null, null) == 0
+
+
 def test_no_fallback_when_library_missing(K, tmp_path, monkeypatch):
     from decode_attention_slot_amd import _lib
 

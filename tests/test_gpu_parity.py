@@ -462,6 +462,154 @@ def test_swa_workload_scale(cuda):
     assert max_err(out, want, rows) <= TOL[w.dtype]
 
 
+# ---------------------------------------------------------------------------
+# decode context parallelism: every rank's share on one GPU, then the merge
+# ---------------------------------------------------------------------------
+LSE_TOL = 1e-4  # fp32 log2/exp2 of scores up to ~50 in magnitude, relative to max(1, |lse|)
+
+
+@pytest.mark.parametrize("world,interleave,bs", [(2, 1, 16), (2, 16, 16), (4, 8, 64), (3, 64, 64),
+                                                 (8, 16, 32)])
+def test_dcp_slot_mapping_vs_oracle(cuda, world, interleave, bs):
+    rng = np.random.default_rng(31 + world)
+    rows, width, T = 5, 9, 2000
+    table = rng.permutation(np.arange(1, rows * width + 1)).reshape(rows, width).astype(np.int32)
+    table = np.where(rng.random((rows, width)) < 0.15, -1, table).astype(np.int32)
+    req = rng.integers(-1, rows + 1, size=T).astype(np.int32)
+    pos = rng.integers(-2, (width + 1) * world * bs, size=T).astype(np.int64)
+    d_req, d_pos, d_tab = (torch.from_numpy(x).to(cuda) for x in (req, pos, table))
+    for k in range(world):
+        got = K.kv_slot_mapping_dcp(d_req, d_pos, d_tab, bs, world, k, interleave,
+                                    max_num_tokens=T + 9)
+        torch.cuda.synchronize()
+        want = O.compute_slot_mapping_dcp(req, pos, table, bs, world, k, interleave, T + 9)
+        assert np.array_equal(got.cpu().numpy(), want), k
+
+
+def dcp_gpu_case(cuda, seed, lens, bs, world, interleave, hkv, g, sq, d, dtype):
+    """Every rank's caches, written on the GPU through kv_slot_mapping_dcp +
+    kv_cache_write, and the same caches built by the oracle."""
+    rng = np.random.default_rng(seed)
+    vblocks = [-(-L // (world * bs)) for L in lens]
+    width = max(vblocks) + 1
+    total = sum(vblocks) + 2
+    table = np.full((len(lens), width), -1, np.int32)
+    perm, off = rng.permutation(np.arange(1, total)), 0
+    for r, n in enumerate(vblocks):
+        table[r, :n] = perm[off:off + n]
+        off += n
+    T = sum(lens)
+    knew = W.to_storage(rng.standard_normal((T, hkv, d)).astype(np.float32), dtype)
+    vnew = W.to_storage(rng.standard_normal((T, hkv, d)).astype(np.float32), dtype)
+    req = np.concatenate([np.full(L, r, np.int32) for r, L in enumerate(lens)])
+    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.int64)
+    q = W.to_storage(rng.standard_normal((len(lens), sq, hkv * g, d)).astype(np.float32), dtype)
+    wl = W.Workload(name="", index=0, seed=seed, dtype=dtype, block_size=bs, total_blocks=total,
+                    num_kv_heads=hkv, num_q_heads=hkv * g, head_dim=d, q_len=sq, num_reqs=len(lens),
+                    computed=None, chunk_lens=None, seq_lens=np.array(lens, np.int32),
+                    block_table=table)
+    d_req, d_pos, d_tab = (torch.from_numpy(x).to(cuda) for x in (req, pos, table))
+    d_k, d_v = dev.upload_storage(knew, dtype, cuda), dev.upload_storage(vnew, dtype, cuda)
+    ranks = []
+    for k in range(world):
+        kc, vc = wl.canary_cache(), wl.canary_cache()
+        O.reshape_and_cache(knew, vnew, O.compute_slot_mapping_dcp(req, pos, table, bs, world, k,
+                                                                   interleave), kc, vc)
+        dkc, dvc = dev.canary_cache(wl, cuda), dev.canary_cache(wl, cuda)
+        slots = K.kv_slot_mapping_dcp(d_req, d_pos, d_tab, bs, world, k, interleave)
+        K.kv_cache_write(d_k, d_v, slots, dkc, dvc)
+        ranks.append((kc, vc, dkc, dvc))
+    return dict(table=table, q=q, ranks=ranks, lens=np.array(lens, np.int32), d_tab=d_tab,
+                d_q=dev.upload_storage(q, dtype, cuda), scale=1 / math.sqrt(d), dtype=dtype,
+                d_sl=torch.from_numpy(np.array(lens, np.int32)).to(cuda))
+
+
+@pytest.mark.parametrize("world,interleave,bs,dtype,sq,g,lens", [
+    (2, 1, 16, "f32", 1, 2, [1, 2, 33, 300]),
+    (2, 16, 64, "bf16", 4, 4, [4, 20, 129, 1500, 5000]),
+    (4, 8, 64, "bf16", 1, 4, [1, 5, 64, 700, 3000, 9000]),
+    (3, 64, 64, "bf16", 2, 8, [2, 191, 192, 193, 4000]),
+    (8, 16, 16, "bf16", 1, 8, [7, 128, 2049, 6000]),
+])
+def test_dcp_ranks_and_merge_vs_oracle(cuda, world, interleave, bs, dtype, sq, g, lens):
+    hkv, d = 2, 128
+    c = dcp_gpu_case(cuda, 40 + world, lens, bs, world, interleave, hkv, g, sq, d, dtype)
+    outs, lses, r_outs, r_lses = [], [], [], []
+    for k, (kc, vc, dkc, dvc) in enumerate(c["ranks"]):
+        # the GPU-written cache of this rank is the oracle's, byte for byte
+        assert np.array_equal(host_bits(dkc), bits(kc)) and np.array_equal(host_bits(dvc), bits(vc))
+        o, l = K.paged_decode_attention_dcp(c["d_q"], dkc, dvc, c["d_tab"], c["d_sl"], c["scale"],
+                                            world, k, interleave)
+        ro, rl = O.paged_decode_attention_dcp(c["q"], kc, vc, c["table"], c["lens"],
+                                              c["table"].shape[1], c["scale"], dtype, world, k,
+                                              interleave)
+        outs.append(o)
+        lses.append(l)
+        r_outs.append(ro)
+        r_lses.append(rl)
+    torch.cuda.synchronize()
+    for k in range(world):
+        assert max_err(outs[k], r_outs[k]) <= TOL[dtype], k
+        gl = lses[k].double().cpu().numpy()
+        assert np.array_equal(np.isneginf(gl), np.isneginf(r_lses[k])), k
+        fin = np.isfinite(r_lses[k])
+        assert (np.abs(gl[fin] - r_lses[k][fin]) <= LSE_TOL * np.maximum(1, np.abs(r_lses[k][fin]))).all()
+    merged, mlse = K.decode_lse_merge(torch.stack(outs), torch.stack(lses))
+    torch.cuda.synchronize()
+    want = O.merge_lse(r_outs, r_lses)
+    assert max_err(merged, want) <= TOL[dtype]
+
+
+def test_dcp_workload_scale(cuda):
+    """Ragged + speculative workload (64 requests, S_q 4) on rank 1 of 4: the
+    rank's cache built and stepped through the library; sampled rows vs the
+    oracle's share of the same rank."""
+    w = W.make_workload(4)
+    world, rank, il = 4, 1, 1
+    s = dev.build(w, cuda, dcp=(world, rank, il))
+    req = torch.cat([s.chunk_req, s.dec_req])
+    pos = torch.cat([s.chunk_pos, s.dec_pos])
+    slots = K.kv_slot_mapping_dcp(req, pos, s.block_table, w.block_size, world, rank, il)
+    K.kv_cache_write(torch.cat([s.chunk_k, s.dec_k]), torch.cat([s.chunk_v, s.dec_v]), slots,
+                     s.k_cache, s.v_cache)
+    out, lse = K.paged_decode_attention_dcp(s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens,
+                                            w.scale, world, rank, il)
+    torch.cuda.synchronize()
+    lens = w.seq_lens[: w.num_rows]
+    rows = [0, int(np.argmax(lens)), int(np.argmin(lens)), w.num_rows - 1]
+    kc, vc = w.canary_cache(), w.canary_cache()
+    for r in rows:
+        kr, vr = w.request_kv(r)
+        L = int(lens[r])
+        sl = O.compute_slot_mapping_dcp(np.full(L, r, np.int32), np.arange(L), s.host_table,
+                                        w.block_size, world, rank, il)
+        O.reshape_and_cache(kr, vr, sl, kc, vc)
+    want, want_lse = O.paged_decode_attention_dcp(w.q(), kc, vc, s.host_table, lens,
+                                                  s.host_table.shape[1], w.scale, w.dtype, world,
+                                                  rank, il, requests=rows)
+    assert max_err(out, want, rows) <= TOL[w.dtype]
+    gl = lse.double().cpu().numpy()[rows]
+    wl = want_lse[rows]
+    assert np.array_equal(np.isneginf(gl), np.isneginf(wl))
+    fin = np.isfinite(wl)
+    assert (np.abs(gl[fin] - wl[fin]) <= LSE_TOL * np.maximum(1, np.abs(wl[fin]))).all()
+
+
+def test_dcp_one_rank_is_plain_decode(cuda):
+    c = small_case(cuda, 9, [1, 64, 65, 700, 3000], 64, 8, 4, 2, 128, "bf16")
+    plain = gpu_attn(c)
+    one, lse = K.paged_decode_attention_dcp(c["d_q"], c["d_kc"], c["d_vc"], c["d_bt"], c["d_sl"],
+                                            c["w"].scale, 1, 0, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int32), one.view(torch.int32))
+    _, want = O.paged_decode_attention_dcp(c["q"], c["kc"], c["vc"], c["table"], c["w"].seq_lens,
+                                           c["table"].shape[1], c["w"].scale, "bf16", 1, 0, 64)
+    got = lse.double().cpu().numpy()
+    assert np.array_equal(np.isneginf(got), np.isneginf(want))  # query 0 of the 1-token request
+    fin = np.isfinite(want)
+    assert (np.abs(got[fin] - want[fin]) <= LSE_TOL * np.maximum(1, np.abs(want[fin]))).all()
+
+
 @pytest.mark.parametrize("bs,dtype", [(16, "bf16"), (64, "f32"), (3, "bf16")])
 def test_fused_slot_write_vs_oracle(cuda, bs, dtype):
     """One-launch slot mapping + write: slots and byte images equal the oracle's

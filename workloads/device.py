@@ -82,15 +82,31 @@ class DeviceStep:
         return torch.cat([self.chunk_pos, self.dec_pos])
 
 
+def dcp_block_table(w: Workload, world: int) -> np.ndarray:
+    """The table one context-parallel rank walks: request r keeps the first
+    ceil(L / (world * bs)) ids of its row, one per virtual block of world * bs
+    positions (every rank shares it); other entries are -1."""
+    table = kernel_block_table(w).copy()
+    bs = w.block_size
+    for r in range(table.shape[0]):
+        L = int(w.seq_lens[r])
+        n = -(-L // (world * bs)) if L > 0 else 0
+        table[r, n:] = np.where(table[r, n:] == 0, 0, -1)
+    return table
+
+
 def build(w: Workload, device="cuda", threads: int = 8, batch_tokens: int = 1 << 19,
-          prefill: bool = True, caches=None) -> DeviceStep:
+          prefill: bool = True, caches=None, dcp=None) -> DeviceStep:
     """Allocate, upload and prefill; returns the step's device tensors.
 
     ``caches`` reuses a (k_cache, v_cache) pair of the right shape (refilled
-    with the canary) instead of allocating new ones.
+    with the canary) instead of allocating new ones. ``dcp = (world, rank,
+    interleave)`` builds one context-parallel rank: its table
+    (dcp_block_table) and a cache holding only the tokens it stores, written
+    through kv_slot_mapping_dcp.
     """
     device = torch.device(device)
-    table = kernel_block_table(w)
+    table = kernel_block_table(w) if dcp is None else dcp_block_table(w, dcp[0])
     if caches is None:
         kc, vc = canary_cache(w, device), canary_cache(w, device)
     else:
@@ -118,7 +134,10 @@ def build(w: Workload, device="cuda", threads: int = 8, batch_tokens: int = 1 <<
         v = np.concatenate([p[3] for p in pending])
         d_req = torch.from_numpy(req).to(device)
         d_pos = torch.from_numpy(pos).to(device)
-        slots = K.kv_slot_mapping(d_req, d_pos, bt, w.block_size)
+        if dcp is None:
+            slots = K.kv_slot_mapping(d_req, d_pos, bt, w.block_size)
+        else:
+            slots = K.kv_slot_mapping_dcp(d_req, d_pos, bt, w.block_size, *dcp)
         K.kv_cache_write(upload_storage(k, w.dtype, device), upload_storage(v, w.dtype, device),
                          slots, kc, vc)
         pending, pending_tokens = [], 0
