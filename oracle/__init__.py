@@ -20,6 +20,7 @@ from .kvslot_oracle import (  # noqa: F401
     paged_decode_attention_dcp,
     remap_null_block_to_sentinel,
     reshape_and_cache,
+    select_batch_bucket,
     select_ctx_bucket,
     smallest_bucket_at_least,
     swa_tail_trim,

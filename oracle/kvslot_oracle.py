@@ -375,6 +375,28 @@ def smallest_bucket_at_least(n, buckets):
     return min(fits) if fits else None
 
 
+def select_batch_bucket(num_active, buckets):
+    """Padded batch size of a decode step ([BKV] "Decode Batch Padding").
+
+    The scheduler takes the smallest configured bucket that fits the active
+    requests; the rows past them are dummy requests. Readings: the list
+    must be non-empty, positive and strictly ascending (the page lists
+    ascending buckets and states no rule; the context-bucket rules of [CLB]
+    "Validation" minus its NKI tile rule), else code "bucket"; more active
+    requests than the largest bucket is code "range" (the scheduler never
+    schedules that many).
+    """
+    b = [int(x) for x in buckets]
+    if not b or any(x <= 0 for x in b) or any(y <= x for x, y in zip(b, b[1:])):
+        raise OracleError("bucket", "batch buckets must be positive and strictly ascending")
+    if num_active < 0:
+        raise OracleError("value", "negative request count")
+    used = smallest_bucket_at_least(num_active, b)
+    if used is None:
+        raise OracleError("range", "more active requests than the largest batch bucket")
+    return used
+
+
 def validate_buckets(buckets, max_model_len):
     """[CLB] "Validation": a set list must be non-empty, positive, strictly
     ascending, each value below max_model_len and divisible by P_MAX = 128."""

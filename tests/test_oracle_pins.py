@@ -697,3 +697,19 @@ def test_num_seqs_bucket_table():
         assert used - active == pad
     s = g["single_bucket"]
     assert O.smallest_bucket_at_least(s["active"], s["buckets"]) == s["bucket_used"]
+
+
+def test_batch_bucket_selection_follows_the_page():
+    g = gold("bkv_num_seqs_buckets.json")
+    for active, used, pad in g["rows"]:
+        assert O.select_batch_bucket(active, g["buckets"]) == used
+    s = g["single_bucket"]
+    for active in range(1, 9):  # a single bucket of 8 serves every batch size
+        assert O.select_batch_bucket(active, s["buckets"]) == s["bucket_used"]
+    for bad in ([], [0, 4], [4, 2], [2, 2]):
+        with pytest.raises(O.OracleError) as e:
+            O.select_batch_bucket(1, bad)
+        assert e.value.code == "bucket"
+    with pytest.raises(O.OracleError) as e:
+        O.select_batch_bucket(9, g["buckets"])
+    assert e.value.code == "range"
