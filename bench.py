@@ -151,6 +151,9 @@ def main(argv=None) -> int:
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window layer: attend over a tail-trimmed table with this window "
                          "(paged_decode_attention_swa); the trim is host metadata built untimed")
+    ap.add_argument("--batch-buckets", default=None,
+                    help="comma-separated num_seqs buckets: pad the batch with dummy requests to the "
+                         "smallest that fits (select_batch_bucket, called every step)")
     ap.add_argument("--dcp", type=int, default=1,
                     help="decode context parallelism over this many ranks: measure rank 0's share "
                          "(its cache holds only its tokens; paged_decode_attention_dcp)")
@@ -183,6 +186,10 @@ def main(argv=None) -> int:
     idx = WORKLOADS[args.workload]
     extra = {"forced_max_ctx": args.max_ctx} if (idx == 2 and args.max_ctx is not None) else {}
     w = W.make_workload(idx, seed=args.seed, **extra)
+    batch_buckets = [int(x) for x in args.batch_buckets.split(",")] if args.batch_buckets else None
+    num_active = w.num_rows
+    if batch_buckets:
+        w = W.pad_batch(w, K.select_batch_bucket(num_active, batch_buckets))
 
     # ---- set-up (untimed): caches, prefill, rotation copies ---------------
     t_setup = time.time()
@@ -281,6 +288,8 @@ def main(argv=None) -> int:
     def step(i, ev=None):
         # host: the per-step bucket pick the pages describe (feature off unless bucketed)
         f_select(max_ctx, num_spec, buckets, max_model_len, w.block_size)
+        if batch_buckets:
+            K.select_batch_bucket(num_active, batch_buckets)
         j = i % R
         if dcp:
             st = f_slot_dcp(*slot_dcp_args)
@@ -365,6 +374,7 @@ def main(argv=None) -> int:
             "seed": w.seed,
             "max_ctx": int((w.computed + w.chunk_lens)[: w.num_reqs].max()),
             "num_seqs": w.num_rows,
+            "batch_buckets": batch_buckets,
             "q_len": w.q_len,
             "walk": f"window {args.window} (tail-trimmed table)" if args.window else args.walk,
             "walk_blocks": int(walk_blocks),

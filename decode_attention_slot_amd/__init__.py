@@ -28,5 +28,6 @@ from ._lib import (  # noqa: F401
     paged_decode_attention_swa,
     kv_swa_tail_trim,
     paged_decode_attention_workspace_bytes,
+    select_batch_bucket,
     select_ctx_bucket,
 )

@@ -41,6 +41,7 @@ EXPORTS = (
     "kv_slot_mapping_dcp",
     "paged_decode_attention_dcp",
     "decode_lse_merge",
+    "select_batch_bucket",
 )
 
 
@@ -92,10 +93,11 @@ def _lib():
             i32, i32, i32, vp, sz, vp, vp, vp,
         ]
         lib.decode_lse_merge.argtypes = [vp, vp, i32, i64, i32, vp, vp, vp]
+        lib.select_batch_bucket.argtypes = [i32, vp, i32, vp]
         for name in ("kv_slot_mapping", "kv_cache_write", "kv_slot_mapping_cache_write",
                      "select_ctx_bucket", "kv_map_to_kernel_blocks", "paged_decode_attention",
                      "paged_decode_attention_swa", "kv_swa_tail_trim", "kv_slot_mapping_dcp",
-                     "paged_decode_attention_dcp", "decode_lse_merge"):
+                     "paged_decode_attention_dcp", "decode_lse_merge", "select_batch_bucket"):
             getattr(lib, name).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -213,6 +215,16 @@ def select_ctx_bucket(max_num_computed_tokens: int, num_speculative_tokens: int,
                                   ctypes.byref(out_w))
     _check(st, "select_ctx_bucket")
     return out_b.value, out_w.value
+
+
+def select_batch_bucket(num_active: int, buckets: Sequence[int]) -> int:
+    """Padded batch size: the smallest bucket >= num_active; host only. See kvslot.h."""
+    keep = (ctypes.c_int32 * max(len(buckets), 1))(*[int(b) for b in buckets])
+    out = ctypes.c_int32()
+    st = _lib().select_batch_bucket(int(num_active), ctypes.cast(keep, ctypes.c_void_p),
+                                    len(buckets), ctypes.byref(out))
+    _check(st, "select_batch_bucket")
+    return out.value
 
 
 def kv_map_to_kernel_blocks(block_table: np.ndarray, manager_block_size: int,

@@ -227,6 +227,23 @@ int select_ctx_bucket(int64_t max_num_computed_tokens, int32_t num_speculative_t
   return KVS_OK;
 }
 
+int select_batch_bucket(int32_t num_active, const int32_t* buckets, int32_t num_buckets,
+                        int32_t* padded_out) {
+  if (!padded_out || num_active < 0 || num_buckets < 0) return KVS_EINVAL;
+  if (num_buckets == 0 || !buckets) return KVS_EBUCKET;
+  for (int32_t i = 0; i < num_buckets; ++i) {
+    if (buckets[i] <= 0) return KVS_EBUCKET;
+    if (i > 0 && buckets[i] <= buckets[i - 1]) return KVS_EBUCKET;
+  }
+  for (int32_t i = 0; i < num_buckets; ++i) {
+    if (buckets[i] >= num_active) {  // ascending: the first that fits is the smallest
+      *padded_out = buckets[i];
+      return KVS_OK;
+    }
+  }
+  return KVS_ERANGE;
+}
+
 int kv_map_to_kernel_blocks(const int32_t* src, int32_t rows, int32_t src_stride,
                             int32_t manager_block_size, int32_t kernel_block_size, int32_t* dst,
                             int32_t dst_stride) {

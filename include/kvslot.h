@@ -184,6 +184,23 @@ int kv_map_to_kernel_blocks(const int32_t* src, int32_t rows, int32_t src_stride
                             int32_t dst_stride);
 
 /*
+ * select_batch_bucket - padded batch size of a decode step ([BKV] "Decode
+ * Batch Padding": the scheduler takes the smallest configured
+ * num_seqs_buckets entry that fits the active requests; the rows past them
+ * are dummy requests: request index -1 and position 0 for their tokens, so
+ * their slots are -1 and nothing is written, and seq_len 0 with null-block
+ * table rows, so decode attention reads nothing for them and writes zeros).
+ * Host only; pointers are host pointers.
+ *
+ * Writes the smallest buckets[i] >= num_active.
+ * Errors: KVS_EINVAL for a null padded_out or negative counts; KVS_EBUCKET
+ * for an empty, non-positive or not strictly ascending list; KVS_ERANGE
+ * when num_active exceeds the largest bucket.
+ */
+int select_batch_bucket(int32_t num_active, const int32_t* buckets, int32_t num_buckets,
+                        int32_t* padded_out);
+
+/*
  * paged_decode_attention_workspace_bytes - bytes of device workspace a
  * paged_decode_attention call with these sizes needs. Depends on these
  * arguments only (not on context lengths or walk_blocks), so one workspace

@@ -90,6 +90,25 @@ def test_select_ctx_bucket_validation_matches_oracle(K):
     assert e.value.name == "KVS_EINVAL"
 
 
+def test_select_batch_bucket_matches_oracle(K):
+    lists = [[1, 2, 4, 8], [8], [1, 3, 5, 64, 256], [16, 32]]
+    for b in lists:
+        for n in range(0, max(b) + 3):
+            try:
+                want = ("ok", O.select_batch_bucket(n, b))
+            except O.OracleError as e:
+                want = (e.code, None)
+            try:
+                got = ("ok", K.select_batch_bucket(n, b))
+            except K.KvslotError as e:
+                got = ({"KVS_ERANGE": "range", "KVS_EBUCKET": "bucket"}[e.name], None)
+            assert got == want, (b, n)
+    for bad in ([], [0, 4], [4, 2], [2, 2]):
+        with pytest.raises(K.KvslotError) as e:
+            K.select_batch_bucket(1, bad)
+        assert e.value.name == "KVS_EBUCKET"
+
+
 def test_map_to_kernel_blocks_matches_oracle(K):
     rng = np.random.default_rng(3)
     for mgr_bs, kern_bs in ((32, 16), (64, 16), (16, 16), (256, 64)):

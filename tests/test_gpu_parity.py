@@ -595,6 +595,37 @@ def test_dcp_workload_scale(cuda):
     assert (np.abs(gl[fin] - wl[fin]) <= LSE_TOL * np.maximum(1, np.abs(wl[fin]))).all()
 
 
+# ---------------------------------------------------------------------------
+# decode batch padding: dummy requests
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("index,buckets", [(1, [1, 2, 4, 8, 16]), (4, [8, 32, 96, 128]),
+                                           (0, [8])])
+def test_batch_padding_leaves_real_rows_bitwise(cuda, index, buckets):
+    """Padding the batch to its bucket with dummy requests changes nothing for
+    the real requests (bitwise: slots, cache image, attention), writes
+    nothing for the dummies and gives them zero outputs; the padded step
+    matches the oracle."""
+    w = W.make_workload(index)
+    rows = K.select_batch_bucket(w.num_rows, buckets)
+    assert rows == O.select_batch_bucket(w.num_rows, buckets) and rows > w.num_rows
+    wp = W.pad_batch(w, rows)
+    s0 = dev.build(w, cuda)
+    slots0, out0 = dev.run_step(s0)
+    s1 = dev.build(wp, cuda)
+    ref = OracleStep(wp, s1.host_table)
+    slots1, out1 = dev.run_step(s1)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots1.cpu().numpy(), ref.write_step())
+    assert np.array_equal(host_bits(s1.k_cache), bits(ref.k_cache))
+    assert max_err(out1, ref.attention(wp.q())) <= TOL[wp.dtype]
+    T0 = slots0.numel()
+    assert torch.equal(slots1[:T0], slots0) and (slots1[T0:] == -1).all()
+    assert torch.equal(s0.k_cache.view(torch.uint8), s1.k_cache.view(torch.uint8))
+    assert torch.equal(s0.v_cache.view(torch.uint8), s1.v_cache.view(torch.uint8))
+    assert torch.equal(out1[: w.num_rows].view(torch.int32), out0.view(torch.int32))
+    assert not out1[w.num_rows:].any()
+
+
 def test_dcp_one_rank_is_plain_decode(cuda):
     c = small_case(cuda, 9, [1, 64, 65, 700, 3000], 64, 8, 4, 2, 128, "bf16")
     plain = gpu_attn(c)

@@ -288,6 +288,33 @@ def _blocks_for(lengths: np.ndarray, block_size: int) -> np.ndarray:
     return np.array([-(-int(L) // block_size) for L in lengths], np.int64)
 
 
+def pad_batch(w: Workload, rows: int) -> Workload:
+    """The same step with the batch padded to ``rows`` rows by dummy requests.
+
+    [BKV] "Decode Batch Padding": dummy requests allocate no blocks and write
+    nothing; each contributes q_len tokens with request index -1 and position
+    0 (so their slots are -1), and here a null-block table row and context
+    length 0, so attention skips them. Real rows and their draws are
+    unchanged (q is drawn row-major, so the real rows keep their values).
+    """
+    extra = rows - w.num_rows
+    assert extra >= 0
+    z64, z32 = np.zeros(extra, np.int64), np.zeros(extra, np.int32)
+    kw = dict(
+        computed=np.concatenate([w.computed, z64]),
+        chunk_lens=np.concatenate([w.chunk_lens, z64]),
+        seq_lens=np.concatenate([w.seq_lens, z32]).astype(np.int32),
+        num_decode_pad_tokens=w.num_decode_pad_tokens + extra * w.q_len,
+    )
+    if w.block_table is not None:
+        kw["block_table"] = np.vstack([w.block_table, np.zeros((extra, w.block_table.shape[1]),
+                                                              np.int32)])
+    else:
+        kw["mgr_block_table"] = np.vstack([w.mgr_block_table,
+                                           np.zeros((extra, w.mgr_block_table.shape[1]), np.int32)])
+    return dataclasses.replace(w, **kw)
+
+
 def make_workload(index: int, seed: Optional[int] = None, **kw) -> Workload:
     """Build config ``index`` (0..4) with ``seed`` (default 1000 + index).
 
