@@ -323,7 +323,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       const int nt = (t_end - t_begin) / kTile;
 
       // K as the score MFMA's A operand, V in row layout. An inactive
-      // entry reads null block 0 and is masked by the caller.
+      // entry reads null block 0 and is masked by the caller. V rows are
+      // read with the nontemporal hint (streamed past the caches): on
+      // MI355X that lifts long streams of reads from ~6.4 to ~7 TB/s; K
+      // stays a plain load, its latency heads the per-tile dependency chain.
       auto load = [&](int tt, TileBuf& bf) {
         const int bid = uniform(s_blk[((tt - off) >> bs_shift) - pb]);
         const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
@@ -339,13 +342,13 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         for (int i = 0; i < 4; ++i) {
           const char* src = vb + in_blk + v_lane_off + i * row_bytes;
           if constexpr (NVW == 2) {
-            const u32x2 x = *(const u32x2*)src;
+            const u32x2 x = __builtin_nontemporal_load((const u32x2*)src);
             bf.v[i][0] = x[0];
             bf.v[i][1] = x[1];
           } else {
 #pragma unroll
             for (int w = 0; w < NVW; w += 4) {
-              const u32x4 x = *(const u32x4*)(src + w * 4);
+              const u32x4 x = __builtin_nontemporal_load((const u32x4*)(src + w * 4));
               bf.v[i][w] = x[0];
               bf.v[i][w + 1] = x[1];
               bf.v[i][w + 2] = x[2];
