@@ -593,41 +593,75 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   }
 }
 
-// Split-K merge: one workgroup per (request, KV head) whose context was
-// split over more than one slice. Wave w merges partials w, w + NWC, ... in
-// ascending order; the NWC partial states are then merged in wave order
-// through LDS. The assignment is fixed, so the result is the same on every
-// run and for every walk mode. Lane l of a wave owns output float4s
-// l + 64 k (k < KC) of the (row, dimension) block. Fewer float4s per lane
-// leave room for more waves, so long contexts (many partials) merge with
-// 16 waves.
+// Split-K merge. A request whose context was cut into C > 1 segments has C
+// partial states per (KV head, row): (m, l, acc), m the running max in log2
+// units, l and acc the sums of exp2(score - m) and of its products with the
+// values. The merged output is defined by one fixed association, so it does
+// not depend on the launch shape, the batch around the request (padding with
+// dummy requests included) or the walk mode:
+// * NG logical groups (NG fixed per row count and head_dim); group j merges
+//   partials j, j + NG, j + 2 NG, ... in that order, starting empty;
+// * the output merges group states 0 .. NG - 1 in that order, starting empty.
+// When C <= NG every group holds at most one partial, a state merged into an
+// empty state comes back unchanged, and the definition reduces to merging
+// partials 0 .. C - 1 in order. The kernel uses that for units with few
+// partials (C <= CS, all loads in flight at once): one wave merges the unit,
+// each lane its own float4s, sequentially, with no LDS and no barrier. Other
+// units take the grouped path (one wave per group, group states through
+// LDS). Either path gives the defined result; the threshold only picks the
+// faster one. Each workgroup owns a tile of T consecutive (request, KV head)
+// units; T only spreads work over workgroups and never changes a result.
+
+// Merge the state (m, l, o) into the running state (M, Lt, ot). The one merge
+// step of every path, with the rounding pinned by explicit fma.
+__device__ __forceinline__ void merge_state(float& M, float& Lt, f32x4& ot, float m, float l,
+                                            f32x4 o) {
+  if (m == -INFINITY) return;  // a state that saw no key
+  const float mn = fmaxf(M, m);
+  const float so = __builtin_amdgcn_exp2f(M - mn);
+  const float sn = __builtin_amdgcn_exp2f(m - mn);
+  Lt = __builtin_fmaf(Lt, so, l * sn);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ot[e] = __builtin_fmaf(ot[e], so, o[e] * sn);
+  M = mn;
+}
+
+// KC: output float4s per lane of one unit (rows * head_dim / 4 <= 64 KC).
 template <int KC>
 struct MergeShape {
-  static constexpr int NWC = KC <= 2 ? 16 : 32 / KC;  // waves per workgroup
-  static constexpr int CB = KC == 1 ? 8 : (KC == 2 ? 3 : (KC == 4 ? 2 : 1));  // chunks in flight per wave
+  static constexpr int NG = KC <= 2 ? 16 : 32 / KC;  // logical groups = waves per workgroup
+  static constexpr int CB = KC == 1 ? 8 : (KC == 2 ? 3 : (KC == 4 ? 2 : 1));  // grouped: partials in flight per wave
+  static constexpr int CS = 16 / KC;  // sequential: at most this many partials, all in flight
 };
 
 template <int D, int KC>
-__global__ void __launch_bounds__(MergeShape<KC>::NWC * 64)
-paged_decode_combine_kernel(const DecodeParams p) {
+__global__ void __launch_bounds__(MergeShape<KC>::NG * 64, 2)
+paged_decode_combine_kernel(const DecodeParams p, int T) {
   constexpr int F4ROW = D / 4;
   constexpr int PSTRIDE = D + 4;
+  constexpr int NG = MergeShape<KC>::NG;
   constexpr int CB = MergeShape<KC>::CB;
-  constexpr int NWC = MergeShape<KC>::NWC;
-  __shared__ float s_m[NWC][KC * 64];
-  __shared__ float s_l[NWC][KC * 64];
-  __shared__ f32x4 s_o[NWC][KC * 64];
+  constexpr int CS = MergeShape<KC>::CS;
+  static_assert(CS <= NG, "the sequential path needs C <= NG");
+  __shared__ float s_m[NG][KC * 64];
+  __shared__ float s_l[NG][KC * 64];
+  __shared__ f32x4 s_o[NG][KC * 64];
+  __shared__ int s_cnt[NG], s_slot[NG];  // partial count and first slot of the tile's units
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int B = p.num_seqs;
   const int Hkv = p.num_kv_heads;
-  const int Hq = p.num_q_heads;
-  const int G = Hq / Hkv;
+  const int G = p.num_q_heads / Hkv;
   const int Sq = p.q_len;
   const int nrows = G * Sq;
-  const int f4_total = nrows * F4ROW;
+  const int f4_total = nrows * F4ROW;  // <= 64 KC
+  const int64_t cstride = (int64_t)Hkv * nrows * PSTRIDE;  // floats between partial slots
+  const int64_t units = (int64_t)p.num_seqs * Hkv;
+  const int64_t u0 = (int64_t)blockIdx.x * T;
+  const int tn = (int)min((int64_t)T, units - u0);
 
+  // Lane l owns float4s l + 64 k (k < KC) of a unit's rows: offsets of the
+  // float4 and of its row's (m, l) within one partial slot.
   int roff[KC], moff[KC];
   bool ok[KC];
 #pragma unroll
@@ -638,16 +672,67 @@ paged_decode_combine_kernel(const DecodeParams p) {
     roff[k] = row * PSTRIDE + (f - row * F4ROW) * 4;
     moff[k] = row * PSTRIDE + D;
   }
+  auto partials_of = [&](int g, int slot) {
+    return p.partials + ((int64_t)slot * Hkv + g) * nrows * PSTRIDE;
+  };
+  // Output float4 f of unit (r, g): normalise and store, with the row's lse.
+  auto emit = [&](int r, int g, int f, float M, float Lt, f32x4 ot) {
+    const int row = f / F4ROW;
+    const int jr = row / G;
+    const int hr = row - jr * G;
+    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+    const int64_t orow = ((int64_t)r * Sq + jr) * (G * Hkv) + (int64_t)g * G + hr;
+    *(f32x4*)(p.out + orow * D + (f - row * F4ROW) * 4) = ot * inv;
+    if (p.lse_out && f == row * F4ROW) p.lse_out[orow] = row_lse(M, Lt);
+  };
 
-  for (int64_t u = blockIdx.x; u < (int64_t)B * Hkv; u += gridDim.x) {
+  // ---- wave w: unit w of the tile; merged here when 2 <= C <= CS ----------
+  if (wave < tn) {
+    const int64_t u = u0 + wave;
     const int r = (int)(u / Hkv);
     const int g = (int)(u - (int64_t)r * Hkv);
-    const int Cv = p.chunk_meta[2 * r + 1];  // pass 1 records it for every request
-    if (Cv <= 1) continue;                    // pass 1 wrote this output directly
-    const int64_t pidx0 = p.chunk_meta[2 * r];
-    const int64_t cstride = (int64_t)Hkv * nrows * PSTRIDE;
-    const float* pbase = p.partials + (pidx0 * Hkv + g) * nrows * PSTRIDE;
+    const int C = uniform(p.chunk_meta[2 * r + 1]);
+    const int slot = uniform(p.chunk_meta[2 * r]);
+    if (lane == 0) {
+      s_cnt[wave] = C;
+      s_slot[wave] = slot;
+    }
+    if (C >= 2 && C <= CS) {
+      const float* pbase = partials_of(g, slot);
+      f32x4 a[CS][KC];
+      f32x2 ml[CS][KC];
+#pragma unroll
+      for (int j = 0; j < CS; ++j) {
+        const float* pc = pbase + (int64_t)j * cstride;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          if (j < C && ok[k]) {
+            a[j][k] = *(const f32x4*)(pc + roff[k]);
+            ml[j][k] = *(const f32x2*)(pc + moff[k]);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float M = -INFINITY, Lt = 0.0f;
+        f32x4 ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < CS; ++j)
+          if (j < C) merge_state(M, Lt, ot, ml[j][k][0], ml[j][k][1], a[j][k]);
+        if (ok[k]) emit(r, g, lane + 64 * k, M, Lt, ot);
+      }
+    }
+  }
+  __syncthreads();
 
+  // ---- units with C > CS, one after another: wave w merges group w ---------
+  for (int ui = 0; ui < tn; ++ui) {
+    const int Cv = s_cnt[ui];
+    if (Cv <= CS) continue;  // written by pass 1, or merged above
+    const int64_t u = u0 + ui;
+    const int r = (int)(u / Hkv);
+    const int g = (int)(u - (int64_t)r * Hkv);
+    const float* pbase = partials_of(g, s_slot[ui]);
     float Mx[KC], Ls[KC];
     f32x4 o[KC];
 #pragma unroll
@@ -656,12 +741,12 @@ paged_decode_combine_kernel(const DecodeParams p) {
       Ls[k] = 0.0f;
       o[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    for (int c0 = wave; c0 < Cv; c0 += NWC * CB) {
+    for (int c0 = wave; c0 < Cv; c0 += NG * CB) {
       f32x4 a[CB][KC];
       f32x2 ml[CB][KC];
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
-        const int cc = c0 + j * NWC;
+        const int cc = c0 + j * NG;
         const float* pc = pbase + (int64_t)cc * cstride;
 #pragma unroll
         for (int k = 0; k < KC; ++k) {
@@ -674,16 +759,9 @@ paged_decode_combine_kernel(const DecodeParams p) {
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-          if (c0 + j * NWC < Cv && ok[k] && ml[j][k][0] != -INFINITY) {
-            const float mn = fmaxf(Mx[k], ml[j][k][0]);
-            const float so = __builtin_amdgcn_exp2f(Mx[k] - mn);
-            const float sn = __builtin_amdgcn_exp2f(ml[j][k][0] - mn);
-            Ls[k] = Ls[k] * so + ml[j][k][1] * sn;
-            o[k] = o[k] * so + a[j][k] * sn;
-            Mx[k] = mn;
-          }
-        }
+        for (int k = 0; k < KC; ++k)
+          if (c0 + j * NG < Cv && ok[k])
+            merge_state(Mx[k], Ls[k], o[k], ml[j][k][0], ml[j][k][1], a[j][k]);
       }
     }
 #pragma unroll
@@ -693,40 +771,24 @@ paged_decode_combine_kernel(const DecodeParams p) {
       s_o[wave][lane + 64 * k] = o[k];
     }
     __syncthreads();
-    for (int f = threadIdx.x; f < f4_total; f += NWC * 64) {
+    for (int f = threadIdx.x; f < f4_total; f += NG * 64) {
       float M = -INFINITY, Lt = 0.0f;
       f32x4 ot = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < NWC; ++w) {
-        const float mw = s_m[w][f];
-        if (mw == -INFINITY) continue;
-        const float mn = fmaxf(M, mw);
-        const float so = __builtin_amdgcn_exp2f(M - mn);
-        const float sn = __builtin_amdgcn_exp2f(mw - mn);
-        Lt = Lt * so + s_l[w][f] * sn;
-        ot = ot * so + s_o[w][f] * sn;
-        M = mn;
-      }
-      const int row = f / F4ROW;
-      const int jr = row / G;
-      const int hr = row - jr * G;
-      const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
-      float* orow = p.out + (((int64_t)r * Sq + jr) * Hq + (int64_t)g * G + hr) * D;
-      *(f32x4*)(orow + (f - row * F4ROW) * 4) = ot * inv;
-      if (p.lse_out && f == row * F4ROW)
-        p.lse_out[((int64_t)r * Sq + jr) * Hq + (int64_t)g * G + hr] = row_lse(M, Lt);
+#pragma unroll 4
+      for (int w = 0; w < NG; ++w) merge_state(M, Lt, ot, s_m[w][f], s_l[w][f], s_o[w][f]);
+      emit(r, g, f, M, Lt, ot);
     }
     __syncthreads();
   }
 }
 
-// Pass-1 workgroups of one instantiation that the device holds at once, at
-// the largest LDS the kernel asks for. Queried once per device. The context
-// walk's figure serves both walks, so both cut the batch the same way.
-template <bool BF16, int D, int NW>
-hipError_t resident_workgroups(int* out) {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices];
+// Workgroups of a kernel the device holds at once (compute units times
+// workgroups per unit at that size and LDS), queried once per device and
+// kernel; `cache` is the kernel's per-device slot.
+constexpr int kMaxDevices = 64;
+
+hipError_t resident_of(const void* kernel, int threads, size_t lds,
+                       std::atomic<int> (&cache)[kMaxDevices], int* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -735,14 +797,40 @@ hipError_t resident_workgroups(int* out) {
   int cus = 0, per_cu = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, kContextWalk>),
-      NW * 64,
-      decode_lds_bytes(kDecodeMaxSeqs));
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds);
   if (e != hipSuccess) return e;
   *out = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
   if (cached) cache[dev].store(*out, std::memory_order_relaxed);
   return hipSuccess;
+}
+
+// Pass-1 workgroups at the largest LDS the kernel asks for. The context
+// walk's figure serves every mode, so all modes cut the batch the same way.
+template <bool BF16, int D, int NW>
+hipError_t resident_workgroups(int* out) {
+  static std::atomic<int> cache[kMaxDevices];
+  return resident_of(
+      reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, kContextWalk>), NW * 64,
+      decode_lds_bytes(kDecodeMaxSeqs), cache, out);
+}
+
+// The merge: tiles of T units (request, KV head), T the smallest count that
+// fits every tile into one round of resident workgroups (at most NG).
+template <int D, int KC>
+hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
+  constexpr int NG = MergeShape<KC>::NG;
+  static std::atomic<int> cache[kMaxDevices];
+  int resident = 0;
+  hipError_t e = resident_of(reinterpret_cast<const void*>(&paged_decode_combine_kernel<D, KC>),
+                             NG * 64, 0, cache, &resident);
+  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads;
+  int64_t T = (units + resident - 1) / resident;
+  T = T < 1 ? 1 : (T > NG ? NG : T);
+  const int64_t tiles = (units + T - 1) / T;  // <= 8192 requests x Hkv
+  const dim3 grid((unsigned)tiles);
+  paged_decode_combine_kernel<D, KC><<<grid, dim3(NG * 64), 0, stream>>>(p, (int)T);
+  return hipGetLastError();
 }
 
 template <bool BF16, int D, int NW>
@@ -766,20 +854,12 @@ hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t strea
     paged_decode_kernel<BF16, D, NW, kContextWalk><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t cgrid = (int64_t)p.num_seqs * p.num_kv_heads;
-  if (cgrid > 65536) cgrid = 65536;
   const int nrows = p.num_q_heads / p.num_kv_heads * p.q_len;
   const int kc = (nrows * (D / 4) + 63) / 64;
-  const dim3 cg((unsigned)cgrid);
-#define KVS_MERGE(KC)                                                             \
-  paged_decode_combine_kernel<D, KC>                                              \
-      <<<cg, dim3(MergeShape<KC>::NWC * 64), 0, stream>>>(p)
-  if (kc <= 1) KVS_MERGE(1);
-  else if (kc <= 2) KVS_MERGE(2);
-  else if (kc <= 4) KVS_MERGE(4);
-  else KVS_MERGE(8);
-#undef KVS_MERGE
-  return hipGetLastError();
+  if (kc <= 1) return launch_merge<D, 1>(p, stream);
+  if (kc <= 2) return launch_merge<D, 2>(p, stream);
+  if (kc <= 4) return launch_merge<D, 4>(p, stream);
+  return launch_merge<D, 8>(p, stream);
 }
 
 template <bool BF16, int D>
