@@ -599,18 +599,21 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 // values. The merged output is defined by one fixed association, so it does
 // not depend on the launch shape, the batch around the request (padding with
 // dummy requests included) or the walk mode:
-// * NG logical groups (NG fixed per row count and head_dim); group j merges
-//   partials j, j + NG, j + 2 NG, ... in that order, starting empty;
+// * NG logical groups (NG fixed by the row count and head_dim); group j
+//   merges partials j, j + NG, j + 2 NG, ... in that order, starting empty;
 // * the output merges group states 0 .. NG - 1 in that order, starting empty.
 // When C <= NG every group holds at most one partial, a state merged into an
 // empty state comes back unchanged, and the definition reduces to merging
 // partials 0 .. C - 1 in order. The kernel uses that for units with few
-// partials (C <= CS, all loads in flight at once): one wave merges the unit,
-// each lane its own float4s, sequentially, with no LDS and no barrier. Other
-// units take the grouped path (one wave per group, group states through
-// LDS). Either path gives the defined result; the threshold only picks the
-// faster one. Each workgroup owns a tile of T consecutive (request, KV head)
-// units; T only spreads work over workgroups and never changes a result.
+// partials (C <= CS, all loads in flight at once): one wave merges them, each
+// lane its own float4, sequentially, with no LDS and no barrier. Other units
+// take the grouped path (one wave per group, group states through LDS).
+// Either path gives the defined result; the threshold only picks the faster.
+// Every output float4 is merged on its own, so a unit (request, KV head) is
+// cut into column pieces of 64 float4s (one per lane) that separate
+// workgroups merge: a long context's partials are read by as many compute
+// units as it has pieces. A workgroup owns a tile of T consecutive pieces;
+// neither the pieces nor T change a result.
 
 // Merge the state (m, l, o) into the running state (M, Lt, ot). The one merge
 // step of every path, with the rounding pinned by explicit fma.
@@ -626,27 +629,26 @@ __device__ __forceinline__ void merge_state(float& M, float& Lt, f32x4& ot, floa
   M = mn;
 }
 
-// KC: output float4s per lane of one unit (rows * head_dim / 4 <= 64 KC).
-template <int KC>
-struct MergeShape {
-  static constexpr int NG = KC <= 2 ? 16 : 32 / KC;  // logical groups = waves per workgroup
-  static constexpr int CB = KC == 1 ? 8 : (KC == 2 ? 3 : (KC == 4 ? 2 : 1));  // grouped: partials in flight per wave
-  static constexpr int CS = 16 / KC;  // sequential: at most this many partials, all in flight
-};
+// Logical groups NG of a unit made of `pieces` columns of 64 float4s (1 to 8):
+// 16 up to two pieces, 8 up to four, 4 beyond.
+__host__ __device__ constexpr int merge_groups(int pieces) {
+  return pieces <= 2 ? 16 : (pieces <= 4 ? 8 : 4);
+}
 
-template <int D, int KC>
-__global__ void __launch_bounds__(MergeShape<KC>::NG * 64, 2)
+// KCW: float4s per lane of a piece (a piece is KCW columns of 64 float4s).
+template <int D, int NG, int KCW>
+__global__ void __launch_bounds__(NG * 64)
 paged_decode_combine_kernel(const DecodeParams p, int T) {
   constexpr int F4ROW = D / 4;
   constexpr int PSTRIDE = D + 4;
-  constexpr int NG = MergeShape<KC>::NG;
-  constexpr int CB = MergeShape<KC>::CB;
-  constexpr int CS = MergeShape<KC>::CS;
-  static_assert(CS <= NG, "the sequential path needs C <= NG");
-  __shared__ float s_m[NG][KC * 64];
-  __shared__ float s_l[NG][KC * 64];
-  __shared__ f32x4 s_o[NG][KC * 64];
-  __shared__ int s_cnt[NG], s_slot[NG];  // partial count and first slot of the tile's units
+  // Sequential path: up to CS partials, all in flight; CS <= NG keeps it
+  // equal to the grouped definition.
+  constexpr int CS = (16 / KCW) < NG ? 16 / KCW : NG;
+  constexpr int CB = KCW >= 8 ? 1 : 8 / KCW;  // grouped path: partials in flight per wave
+  __shared__ float s_m[NG][KCW * 64];
+  __shared__ float s_l[NG][KCW * 64];
+  __shared__ f32x4 s_o[NG][KCW * 64];
+  __shared__ int s_cnt[NG], s_slot[NG];  // partial count and first slot of the tile's pieces
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -654,24 +656,25 @@ paged_decode_combine_kernel(const DecodeParams p, int T) {
   const int G = p.num_q_heads / Hkv;
   const int Sq = p.q_len;
   const int nrows = G * Sq;
-  const int f4_total = nrows * F4ROW;  // <= 64 KC
-  const int64_t cstride = (int64_t)Hkv * nrows * PSTRIDE;  // floats between partial slots
-  const int64_t units = (int64_t)p.num_seqs * Hkv;
-  const int64_t u0 = (int64_t)blockIdx.x * T;
-  const int tn = (int)min((int64_t)T, units - u0);
+  const int f4_total = nrows * F4ROW;
+  const int pieces = (f4_total + 64 * KCW - 1) / (64 * KCW);  // per unit
+  const int64_t cstride = (int64_t)Hkv * nrows * PSTRIDE;     // floats between partial slots
+  const int64_t npieces = (int64_t)p.num_seqs * Hkv * pieces;
+  const int64_t v0 = (int64_t)blockIdx.x * T;
+  const int tn = (int)min((int64_t)T, npieces - v0);
 
-  // Lane l owns float4s l + 64 k (k < KC) of a unit's rows: offsets of the
-  // float4 and of its row's (m, l) within one partial slot.
-  int roff[KC], moff[KC];
-  bool ok[KC];
-#pragma unroll
-  for (int k = 0; k < KC; ++k) {
-    const int f = lane + 64 * k;
+  // Piece v: unit u = v / pieces = (r, g); this lane's float4s f0 + 64 k.
+  auto piece = [&](int64_t v, int& r, int& g, int& f0) {
+    const int64_t u = v / pieces;
+    f0 = (int)(v - u * pieces) * 64 * KCW + lane;
+    r = (int)(u / Hkv);
+    g = (int)(u - (int64_t)r * Hkv);
+  };
+  auto float_offset = [&](int f) {  // of float4 f within one partial slot
     const int row = f / F4ROW;
-    ok[k] = f < f4_total;
-    roff[k] = row * PSTRIDE + (f - row * F4ROW) * 4;
-    moff[k] = row * PSTRIDE + D;
-  }
+    return row * PSTRIDE + (f - row * F4ROW) * 4;
+  };
+  auto ml_offset = [&](int f) { return (f / F4ROW) * PSTRIDE + D; };
   auto partials_of = [&](int g, int slot) {
     return p.partials + ((int64_t)slot * Hkv + g) * nrows * PSTRIDE;
   };
@@ -686,11 +689,10 @@ paged_decode_combine_kernel(const DecodeParams p, int T) {
     if (p.lse_out && f == row * F4ROW) p.lse_out[orow] = row_lse(M, Lt);
   };
 
-  // ---- wave w: unit w of the tile; merged here when 2 <= C <= CS ----------
+  // ---- wave w: piece w of the tile; merged here when 2 <= C <= CS ---------
   if (wave < tn) {
-    const int64_t u = u0 + wave;
-    const int r = (int)(u / Hkv);
-    const int g = (int)(u - (int64_t)r * Hkv);
+    int r, g, f0;
+    piece(v0 + wave, r, g, f0);
     const int C = uniform(p.chunk_meta[2 * r + 1]);
     const int slot = uniform(p.chunk_meta[2 * r]);
     if (lane == 0) {
@@ -698,85 +700,88 @@ paged_decode_combine_kernel(const DecodeParams p, int T) {
       s_slot[wave] = slot;
     }
     if (C >= 2 && C <= CS) {
-      const float* pbase = partials_of(g, slot);
-      f32x4 a[CS][KC];
-      f32x2 ml[CS][KC];
+      const float* base = partials_of(g, slot);
+      f32x4 a[CS][KCW];
+      f32x2 ml[CS][KCW];
 #pragma unroll
       for (int j = 0; j < CS; ++j) {
-        const float* pc = pbase + (int64_t)j * cstride;
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-          if (j < C && ok[k]) {
-            a[j][k] = *(const f32x4*)(pc + roff[k]);
-            ml[j][k] = *(const f32x2*)(pc + moff[k]);
+        for (int k = 0; k < KCW; ++k) {
+          const int f = f0 + 64 * k;
+          if (j < C && f < f4_total) {
+            a[j][k] = *(const f32x4*)(base + j * cstride + float_offset(f));
+            ml[j][k] = *(const f32x2*)(base + j * cstride + ml_offset(f));
           }
         }
       }
 #pragma unroll
-      for (int k = 0; k < KC; ++k) {
+      for (int k = 0; k < KCW; ++k) {
+        const int f = f0 + 64 * k;
         float M = -INFINITY, Lt = 0.0f;
         f32x4 ot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < CS; ++j)
           if (j < C) merge_state(M, Lt, ot, ml[j][k][0], ml[j][k][1], a[j][k]);
-        if (ok[k]) emit(r, g, lane + 64 * k, M, Lt, ot);
+        if (f < f4_total) emit(r, g, f, M, Lt, ot);
       }
     }
   }
   __syncthreads();
 
-  // ---- units with C > CS, one after another: wave w merges group w ---------
-  for (int ui = 0; ui < tn; ++ui) {
-    const int Cv = s_cnt[ui];
+  // ---- pieces with C > CS, one after another: wave w merges group w --------
+  for (int vi = 0; vi < tn; ++vi) {
+    const int Cv = s_cnt[vi];
     if (Cv <= CS) continue;  // written by pass 1, or merged above
-    const int64_t u = u0 + ui;
-    const int r = (int)(u / Hkv);
-    const int g = (int)(u - (int64_t)r * Hkv);
-    const float* pbase = partials_of(g, s_slot[ui]);
-    float Mx[KC], Ls[KC];
-    f32x4 o[KC];
+    int r, g, f0;
+    piece(v0 + vi, r, g, f0);
+    const float* base = partials_of(g, s_slot[vi]);
+    float Mx[KCW], Ls[KCW];
+    f32x4 o[KCW];
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
+    for (int k = 0; k < KCW; ++k) {
       Mx[k] = -INFINITY;
       Ls[k] = 0.0f;
       o[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     for (int c0 = wave; c0 < Cv; c0 += NG * CB) {
-      f32x4 a[CB][KC];
-      f32x2 ml[CB][KC];
+      f32x4 a[CB][KCW];
+      f32x2 ml[CB][KCW];
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const int cc = c0 + j * NG;
-        const float* pc = pbase + (int64_t)cc * cstride;
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-          if (cc < Cv && ok[k]) {
-            a[j][k] = *(const f32x4*)(pc + roff[k]);
-            ml[j][k] = *(const f32x2*)(pc + moff[k]);
+        for (int k = 0; k < KCW; ++k) {
+          const int f = f0 + 64 * k;
+          if (cc < Cv && f < f4_total) {
+            a[j][k] = *(const f32x4*)(base + (int64_t)cc * cstride + float_offset(f));
+            ml[j][k] = *(const f32x2*)(base + (int64_t)cc * cstride + ml_offset(f));
           }
         }
       }
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
 #pragma unroll
-        for (int k = 0; k < KC; ++k)
-          if (c0 + j * NG < Cv && ok[k])
+        for (int k = 0; k < KCW; ++k)
+          if (c0 + j * NG < Cv && f0 + 64 * k < f4_total)
             merge_state(Mx[k], Ls[k], o[k], ml[j][k][0], ml[j][k][1], a[j][k]);
       }
     }
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
+    for (int k = 0; k < KCW; ++k) {
       s_m[wave][lane + 64 * k] = Mx[k];
       s_l[wave][lane + 64 * k] = Ls[k];
       s_o[wave][lane + 64 * k] = o[k];
     }
     __syncthreads();
-    for (int f = threadIdx.x; f < f4_total; f += NG * 64) {
-      float M = -INFINITY, Lt = 0.0f;
-      f32x4 ot = {0.f, 0.f, 0.f, 0.f};
+    for (int i = threadIdx.x; i < 64 * KCW; i += NG * 64) {
+      const int f = f0 - lane + i;  // float4 of the unit this thread combines
+      if (f < f4_total) {
+        float M = -INFINITY, Lt = 0.0f;
+        f32x4 ot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-      for (int w = 0; w < NG; ++w) merge_state(M, Lt, ot, s_m[w][f], s_l[w][f], s_o[w][f]);
-      emit(r, g, f, M, Lt, ot);
+        for (int w = 0; w < NG; ++w) merge_state(M, Lt, ot, s_m[w][i], s_l[w][i], s_o[w][i]);
+        emit(r, g, f, M, Lt, ot);
+      }
     }
     __syncthreads();
   }
@@ -814,23 +819,36 @@ hipError_t resident_workgroups(int* out) {
       decode_lds_bytes(kDecodeMaxSeqs), cache, out);
 }
 
-// The merge: tiles of T units (request, KV head), T the smallest count that
-// fits every tile into one round of resident workgroups (at most NG).
-template <int D, int KC>
-hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
-  constexpr int NG = MergeShape<KC>::NG;
-  static std::atomic<int> cache[kMaxDevices];
-  int resident = 0;
-  hipError_t e = resident_of(reinterpret_cast<const void*>(&paged_decode_combine_kernel<D, KC>),
-                             NG * 64, 0, cache, &resident);
+// The merge of units made of `kc` columns of 64 float4s. One float4 per lane
+// (pieces of one column) when all those pieces fit into one round of
+// resident workgroups: the partials of a long context are then read by kc
+// times as many compute units. Otherwise every lane takes 32 / NG float4s
+// (one piece per unit), which keeps more loads in flight per wave. Tiles of
+// T pieces, T the smallest count that fits one round (at most NG).
+template <int D, int KCW, int NG>
+hipError_t launch_merge_shape(const DecodeParams& p, int64_t n, int resident, hipStream_t stream) {
+  int64_t T = (n + resident - 1) / resident;
+  T = T < 1 ? 1 : (T > NG ? NG : T);
+  const int64_t tiles = (n + T - 1) / T;  // <= 8192 requests x Hkv x 8 pieces
+  paged_decode_combine_kernel<D, NG, KCW>
+      <<<dim3((unsigned)tiles), dim3(NG * 64), 0, stream>>>(p, (int)T);
+  return hipGetLastError();
+}
+
+template <int D, int NG>
+hipError_t launch_merge(const DecodeParams& p, int kc, hipStream_t stream) {
+  constexpr int KMAX = 32 / NG;  // float4s per lane that cover a unit of this NG
+  static std::atomic<int> cache1[kMaxDevices], cachew[kMaxDevices];
+  int res1 = 0, resw = 0;
+  hipError_t e = resident_of(reinterpret_cast<const void*>(&paged_decode_combine_kernel<D, NG, 1>),
+                             NG * 64, 0, cache1, &res1);
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads;
-  int64_t T = (units + resident - 1) / resident;
-  T = T < 1 ? 1 : (T > NG ? NG : T);
-  const int64_t tiles = (units + T - 1) / T;  // <= 8192 requests x Hkv
-  const dim3 grid((unsigned)tiles);
-  paged_decode_combine_kernel<D, KC><<<grid, dim3(NG * 64), 0, stream>>>(p, (int)T);
-  return hipGetLastError();
+  if (units * kc <= res1) return launch_merge_shape<D, 1, NG>(p, units * kc, res1, stream);
+  e = resident_of(reinterpret_cast<const void*>(&paged_decode_combine_kernel<D, NG, KMAX>),
+                  NG * 64, 0, cachew, &resw);
+  if (e != hipSuccess) return e;
+  return launch_merge_shape<D, KMAX, NG>(p, units * ((kc + KMAX - 1) / KMAX), resw, stream);
 }
 
 template <bool BF16, int D, int NW>
@@ -856,10 +874,9 @@ hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t strea
   if (e != hipSuccess) return e;
   const int nrows = p.num_q_heads / p.num_kv_heads * p.q_len;
   const int kc = (nrows * (D / 4) + 63) / 64;
-  if (kc <= 1) return launch_merge<D, 1>(p, stream);
-  if (kc <= 2) return launch_merge<D, 2>(p, stream);
-  if (kc <= 4) return launch_merge<D, 4>(p, stream);
-  return launch_merge<D, 8>(p, stream);
+  if (kc <= 2) return launch_merge<D, merge_groups(2)>(p, kc, stream);
+  if (kc <= 4) return launch_merge<D, merge_groups(4)>(p, kc, stream);
+  return launch_merge<D, merge_groups(8)>(p, kc, stream);
 }
 
 template <bool BF16, int D>
