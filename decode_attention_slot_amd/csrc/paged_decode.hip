@@ -35,7 +35,8 @@
 //   tile t is computed and are never under a data-dependent branch (an
 //   inactive table entry reads null block 0 and is masked; the loop tail
 //   re-loads its last tile, which hits in cache), so one tile stays in
-//   flight behind the one being computed.
+//   flight behind the one being computed. A barrier every two tiles keeps
+//   the waves of a workgroup in step.
 // * Tile of 16 tokens. S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (fp32 KV:
 //   v_mfma_f32_16x16x4f32): K is the A operand (lane l holds token l % 16,
 //   16 bytes of its head row per piece), Q^T the B operand (lane l holds
@@ -362,6 +363,13 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 #pragma unroll
       for (int s = 0; s < kDepth - 1; ++s) load(tile_at(s), bufs[s]);
       for (int t = 0; t < nt; t += kDepth) {
+        // Keep the workgroup's waves in step (every wave walks the same
+        // tiles, for its own KV head). Two waves share each SIMD, and the
+        // older one wins issue arbitration; left alone it runs ahead and the
+        // other finishes its last tiles with half the loads in flight. A
+        // bare s_barrier waits for no memory access, so the tiles already
+        // requested stay in flight across it.
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int s = 0; s < kDepth; ++s) {
           load(tile_at(t + s + kDepth - 1), bufs[(s + kDepth - 1) % kDepth]);
