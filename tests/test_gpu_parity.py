@@ -599,12 +599,15 @@ def test_dcp_workload_scale(cuda):
 # decode batch padding: dummy requests
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("index,buckets", [(1, [1, 2, 4, 8, 16]), (4, [8, 32, 96, 128]),
-                                           (0, [8])])
+                                           (0, [8]), (1, [512])])
 def test_batch_padding_leaves_real_rows_bitwise(cuda, index, buckets):
     """Padding the batch to its bucket with dummy requests changes nothing for
     the real requests (bitwise: slots, cache image, attention), writes
     nothing for the dummies and gives them zero outputs; the padded step
-    matches the oracle."""
+    matches the oracle. Padding the 12-request workload to 512 rows also
+    moves the split-K merge from one float4 per lane to the wide launch
+    shape, and some of its requests from the sequential to the grouped
+    merge path, which must not change a bit either."""
     w = W.make_workload(index)
     rows = K.select_batch_bucket(w.num_rows, buckets)
     assert rows == O.select_batch_bucket(w.num_rows, buckets) and rows > w.num_rows
