@@ -60,8 +60,16 @@ KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_slot_amd", "csrc", "paged_d
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the decode kernels' code: the source with // comments,
+    trailing blanks and empty lines removed, so that editing a comment does not
+    retire a counter measurement of unchanged code."""
+    lines = []
+    with open(KERNEL_SOURCE, encoding="utf-8") as f:
+        for line in f:
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
 def attention_bytes(w, walk_blocks: int, table_walk: bool) -> int:
@@ -426,8 +434,9 @@ def main(argv=None) -> int:
 def measured_traffic(workload: str, walk: str):
     """HBM bytes per launch from the committed counter summary, or None.
 
-    The summary records the kernel source hash it was taken with; once the
-    kernel has changed the figure no longer applies and None is reported.
+    The summary records the hash of the kernel code it was taken with
+    (kernel_source_hash); once the code has changed the figure no longer
+    applies and None is reported.
     """
     path = os.path.join(ROOT, "profiles", f"paged_decode_attention_{workload}_{walk}_traffic.json")
     try:

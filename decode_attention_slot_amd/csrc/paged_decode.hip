@@ -51,8 +51,9 @@
 //   accumulator lands with query row = l % 16, matching the softmax state.
 // * A segment that holds a whole request writes its output. Otherwise its
 //   partial state (acc, m, l per row) goes to slot slice + request of the
-//   workspace; a second kernel merges a request's partials in slice order,
-//   so results do not depend on scheduling.
+//   workspace, and a second kernel merges a request's partials in one fixed
+//   association (below), so results do not depend on scheduling, on the
+//   launch shape or on the batch around the request.
 // * Masked keys are removed by select, never by multiplying by zero, and the
 //   values of keys past the context are replaced by -0.0, so unwritten (NaN
 //   canary) cache rows cannot leak into the output and a masked product is
