@@ -17,8 +17,8 @@ int elem_bytes(kvs_dtype d) {
   switch (d) {
     case KVS_F32: return 4;
     case KVS_BF16: return 2;
+    default: return 0;  // any other value, the range markers included: unsupported
   }
-  return 0;
 }
 
 constexpr int kMaxRows = 16;        // (Hq / Hkv) * q_len: one MFMA column tile
@@ -213,6 +213,8 @@ int select_ctx_bucket(int64_t max_num_computed_tokens, int32_t num_speculative_t
   // "Per-step bucket selection": needed_seq = max(num_computed_tokens) + 1 +
   // num_speculative_tokens; the smallest bucket >= needed_seq, falling back
   // to max_model_len.
+  // (max_num_computed_tokens < max_model_len <= INT32_MAX keeps the sum in range)
+  if (max_num_computed_tokens >= max_model_len) return KVS_ERANGE;
   const int64_t needed_seq = max_num_computed_tokens + 1 + (int64_t)num_speculative_tokens;
   if (needed_seq > max_model_len) return KVS_ERANGE;
   int32_t bucket = max_model_len;

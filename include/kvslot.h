@@ -49,8 +49,16 @@ extern "C" {
 #define KVS_ENOSPACE (-5)     /* workspace smaller than required               */
 #define KVS_EHIP (-6)         /* a kernel launch failed (hipGetLastError)      */
 
-/* Element type of caches, new K/V rows and q. */
-typedef enum { KVS_F32 = 0, KVS_BF16 = 1 } kvs_dtype;
+/* Element type of caches, new K/V rows and q. The two range markers are not
+ * dtypes: they make every int32 value a valid value of the type in C and C++
+ * alike, so a caller passing some other number gets KVS_EUNSUPPORTED rather
+ * than undefined behaviour. */
+typedef enum {
+  KVS_F32 = 0,
+  KVS_BF16 = 1,
+  KVS_DTYPE_RANGE_LO_ = -0x7fffffff - 1,
+  KVS_DTYPE_RANGE_HI_ = 0x7fffffff
+} kvs_dtype;
 
 /* paged_decode_attention flag: walk every one of the first walk_blocks table
  * columns of every row, as a fixed-shape kernel does; inactive entries read
