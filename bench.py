@@ -39,6 +39,7 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 EVENT_EVERY = 8  # timed steps whose attention call is bracketed by HIP events
+SLOT_SWEEP_TOKENS = 1 << 20  # slot mapping measured at this many tokens as well
 WORKLOADS = {
     "block_config_bf16": 1,
     "ctx_bucketing": 2,
@@ -357,6 +358,27 @@ def main(argv=None) -> int:
     t_write = back_to_back(f_write, write_args, args.steps)
     t_fused = back_to_back(f_fused, fused_args, args.steps)
 
+    # Slot mapping at 2^20 tokens (the step's few tokens only measure the
+    # launch): tokens of random real requests at random positions below
+    # their context lengths, mapped through this workload's table.
+    sweep = None
+    if w.num_reqs:
+        rng = np.random.default_rng(w.seed + 7)
+        nt = SLOT_SWEEP_TOKENS
+        req = rng.integers(0, w.num_reqs, nt).astype(np.int32)
+        lens = np.maximum(w.seq_lens[: w.num_reqs].astype(np.int64), 1)
+        pos = (rng.random(nt) * lens[req]).astype(np.int64)
+        d_req = torch.from_numpy(req).to(cuda)
+        d_pos = torch.from_numpy(pos).to(cuda)
+        d_slots = torch.empty(nt, dtype=torch.int64, device=cuda)
+        big = (d_req.data_ptr(), d_pos.data_ptr(), nt, nt, s.block_table.data_ptr(), int(rows),
+               int(stride), w.block_size, d_slots.data_ptr(), sp)
+        t_big = back_to_back(f_slot, [big], 50)
+        sweep = {"tokens": nt, "us": round(t_big * 1e6, 3),
+                 "tokens_per_s": round(nt / t_big, 1),
+                 "gbps": round(slot_map_bytes(nt) / t_big / 1e9, 2),
+                 "frac_of_peak": round(slot_map_bytes(nt) / t_big / 1e9 / HBM_PEAK_GBPS, 4)}
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=cuda).fill_(1)
@@ -404,6 +426,7 @@ def main(argv=None) -> int:
         "attention_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
         "decode_tokens_per_s": round(decode_tokens / (ms_per_step * 1e-3), 1),
         "slot_map_tokens_per_s": round(T / t_slot, 1),
+        "slot_map_sweep": sweep,
         "kernel_us": {"kv_slot_mapping": round(t_slot * 1e6, 3),
                       "kv_cache_write": round(t_write * 1e6, 3),
                       "kv_slot_mapping_cache_write": round(t_fused * 1e6, 3),
