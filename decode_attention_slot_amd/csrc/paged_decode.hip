@@ -639,9 +639,12 @@ __device__ __forceinline__ void merge_state(float& M, float& Lt, f32x4& ot, floa
 }
 
 // Logical groups NG of a unit made of `pieces` columns of 64 float4s (1 to 8):
-// 16 up to two pieces, 8 up to four, 4 beyond.
+// 8 up to four pieces, 4 beyond. (16 groups for one- and two-column units
+// merged 1 us slower on the 12-request and bucketing workloads: the launch
+// of 1024-thread workgroups costs more than the extra partials in flight
+// gain; 4 groups for four-column units doubled the 256-request merge.)
 __host__ __device__ constexpr int merge_groups(int pieces) {
-  return pieces <= 2 ? 16 : (pieces <= 4 ? 8 : 4);
+  return pieces <= 4 ? 8 : 4;
 }
 
 // KCW: float4s per lane of a piece (a piece is KCW columns of 64 float4s).
@@ -883,7 +886,6 @@ hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t strea
   if (e != hipSuccess) return e;
   const int nrows = p.num_q_heads / p.num_kv_heads * p.q_len;
   const int kc = (nrows * (D / 4) + 63) / 64;
-  if (kc <= 2) return launch_merge<D, merge_groups(2)>(p, kc, stream);
   if (kc <= 4) return launch_merge<D, merge_groups(4)>(p, kc, stream);
   return launch_merge<D, merge_groups(8)>(p, kc, stream);
 }
