@@ -178,8 +178,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every box here has one GPU); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the "
+              "sharding design is per-GPU and exchange-free); run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
