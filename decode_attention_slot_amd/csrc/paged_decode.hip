@@ -619,10 +619,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 // take the grouped path (one wave per group, group states through LDS).
 // Either path gives the defined result; the threshold only picks the faster.
 // Every output float4 is merged on its own, so a unit (request, KV head) is
-// cut into column pieces of 64 float4s (one per lane) that separate
-// workgroups merge: a long context's partials are read by as many compute
-// units as it has pieces. A workgroup owns a tile of T consecutive pieces;
-// neither the pieces nor T change a result.
+// cut into column pieces of 64 KCW float4s (KCW per lane) that separate
+// workgroups merge: with KCW = 1 a long context's partials are read by as
+// many compute units as the unit has 64-float4 columns. A workgroup owns a
+// tile of T consecutive pieces; neither KCW nor T changes a result.
 
 // Merge the state (m, l, o) into the running state (M, Lt, ot). The one merge
 // step of every path, with the rounding pinned by explicit fma.
