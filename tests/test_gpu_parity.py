@@ -20,7 +20,16 @@ from workloads import device as dev
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}
+# The stated bar is max-abs-error 1e-5 (fp32 KV) and 2e-2 (bf16 KV). Both
+# sides read the same bf16 values exactly (widened to fp32 / fp64), so only
+# fp32 rounding of the scores, the exp2 evaluations and the accumulations
+# separates them: about (D + log2 L) * 2^-24 relative, observed at most 3e-7
+# on outputs of magnitude <= 2.5. The tests therefore hold bf16 to 1e-5 as
+# well, tight enough that dropping or doubling one key of a 10K-token
+# context (an output change of about 1e-4) fails.
+TOL_BAR = {"f32": 1e-5, "bf16": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 1e-5}
+assert all(TOL[k] <= TOL_BAR[k] for k in TOL)
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:
