@@ -358,6 +358,25 @@ def main(argv=None) -> int:
     t_write = back_to_back(f_write, write_args, args.steps)
     t_fused = back_to_back(f_fused, fused_args, args.steps)
 
+    # Under context parallelism the ranks' (out, lse) would be all-gathered
+    # and merged by decode_lse_merge; one GPU holds only rank 0's share, so
+    # the merge is timed on world copies of it (its cost depends on the
+    # shapes, not the values).
+    lse_merge = None
+    if dcp:
+        world = dcp[0]
+        rows_m = w.num_rows * w.q_len * w.num_q_heads
+        outs = out.reshape(1, rows_m, w.head_dim).expand(world, -1, -1).contiguous()
+        lses = lse.reshape(1, rows_m).expand(world, -1).contiguous()
+        m_out = torch.empty((rows_m, w.head_dim), dtype=torch.float32, device=cuda)
+        m_lse = torch.empty(rows_m, dtype=torch.float32, device=cuda)
+        m_args = (outs.data_ptr(), lses.data_ptr(), world, rows_m, w.head_dim, m_out.data_ptr(),
+                  m_lse.data_ptr(), sp)
+        t_m = back_to_back(lib.decode_lse_merge, [m_args], 100)
+        m_bytes = (world + 1) * rows_m * (w.head_dim + 1) * 4
+        lse_merge = {"world": world, "rows": rows_m, "us": round(t_m * 1e6, 3),
+                     "algorithmic_bytes": m_bytes, "gbps": round(m_bytes / t_m / 1e9, 2)}
+
     # Slot mapping at 2^20 tokens (the step's few tokens only measure the
     # launch): tokens of random real requests at random positions below
     # their context lengths, mapped through this workload's table.
@@ -427,6 +446,7 @@ def main(argv=None) -> int:
         "decode_tokens_per_s": round(decode_tokens / (ms_per_step * 1e-3), 1),
         "slot_map_tokens_per_s": round(T / t_slot, 1),
         "slot_map_sweep": sweep,
+        "lse_merge": lse_merge,
         "kernel_us": {"kv_slot_mapping": round(t_slot * 1e6, 3),
                       "kv_cache_write": round(t_write * 1e6, 3),
                       "kv_slot_mapping_cache_write": round(t_fused * 1e6, 3),
