@@ -7,10 +7,12 @@ synthetic and already resident in HBM when the timed region starts (the
 prior context is prefilled through the library beforehand, untimed).
 HIP events on the launch stream bracket the attention call of every eighth
 timed step (an event is a marker the GPU processes in line, so marking every
-step would slow the steps being timed); the slot mapping and cache write
-kernels (and their one-launch fusion, which the step uses unless
---separate-write) are timed after the steps, each in a run of back-to-back
-launches.
+step would slow the steps being timed). The events are created with
+hipEventDisableSystemFence: a default event's record also writes back and
+invalidates the caches at system scope, which adds to the timed work. The
+slot mapping and cache write kernels (and their one-launch fusion, which the
+step uses unless --separate-write) are timed after the steps, each in a run
+of back-to-back launches.
 
 The step rotates over several identical copies of the KV cache so that the
 bytes a step reads come from HBM, not from the last step's L2 / MALL lines.
@@ -71,6 +73,58 @@ def kernel_source_hash() -> str:
             if code:
                 lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
+class HipEvent:
+    """A HIP timing event recorded on a given stream, created with
+    hipEventDisableSystemFence: recording it writes a timestamp without the
+    system-scope cache writeback and invalidation a default event performs,
+    which would otherwise add to (and perturb) the work being timed. Uses the
+    HIP runtime the process already runs (torch's, which the library shares).
+    """
+
+    _hip = None
+
+    @classmethod
+    def _rt(cls):
+        if cls._hip is None:
+            import ctypes
+
+            import torch
+
+            lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        self._ev = ctypes.c_void_p()
+        if self._rt().hipEventCreateWithFlags(ctypes.byref(self._ev), self.DISABLE_SYSTEM_FENCE):
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream_ptr: int) -> None:
+        if self._rt().hipEventRecord(self._ev, stream_ptr):
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        import ctypes
+
+        ms = ctypes.c_float()
+        if self._rt().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self._ev:
+            self._hip.hipEventDestroy(self._ev)
 
 
 def attention_bytes(w, walk_blocks: int, table_walk: bool) -> int:
@@ -312,10 +366,10 @@ def main(argv=None) -> int:
         else:
             st = f_fused(*fused_args[j])
         if ev is not None:
-            ev[0].record(stream)
+            ev[0].record(sp)
         st |= f_attn(*attn_args[j])
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].record(sp)
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
@@ -329,30 +383,29 @@ def main(argv=None) -> int:
     # the GPU a few microseconds, so marking every step would slow the very
     # steps being timed); their average is the attention call's time.
     marked = [i for i in range(args.steps) if i % EVENT_EVERY == 0]
-    events = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in marked}
+    events = {i: [HipEvent(), HipEvent()] for i in marked}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, events.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_attn = np.mean([e[0].elapsed_time(e[1]) for e in events.values()]) * 1e-3
+    t_attn = np.mean([e[0].elapsed_ms(e[1]) for e in events.values()]) * 1e-3
     ms_per_step = wall / args.steps * 1e3
 
     # Slot mapping and cache write on their own: back-to-back launches
     # between two events give each kernel's time in a busy stream.
     def back_to_back(fn, arg_list, n):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        e0, e1 = HipEvent(), HipEvent()
         for k in range(min(n, 10)):
             fn(*arg_list[k % len(arg_list)])
-        e0.record(stream)
+        e0.record(sp)
         for k in range(n):
             if fn(*arg_list[k % len(arg_list)]):
                 raise RuntimeError("library call failed")
-        e1.record(stream)
+        e1.record(sp)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / n
+        return e0.elapsed_ms(e1) * 1e-3 / n
 
     t_slot = back_to_back(f_slot, [slot_args], args.steps)
     t_write = back_to_back(f_write, write_args, args.steps)
