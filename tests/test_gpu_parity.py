@@ -272,6 +272,45 @@ def test_shapes_vs_oracle(cuda, shape):
     assert err <= TOL[dtype], err
 
 
+def random_case_params(seed):
+    """A seeded random batch shape: dtype, head_dim, block size, heads, query
+    tokens, lengths (mostly short, a few long), walk and flags."""
+    rng = np.random.default_rng(10_000 + seed)
+    dtype = ["f32", "bf16"][rng.integers(2)]
+    d = [64, 128][rng.integers(2)]
+    bs = [16, 32, 64, 128, 256][rng.integers(5)]
+    hkv = [1, 2, 4, 8][rng.integers(4)]
+    sq = int(rng.integers(1, 5))
+    g = int(rng.choice([x for x in (1, 2, 3, 4, 8) if x * sq <= 16]))
+    nb = int(rng.integers(1, 41))
+    kind = rng.random(nb)
+    lens = np.where(kind < 0.6, rng.integers(sq, 40, nb),
+                    np.where(kind < 0.9, rng.integers(40, 600, nb), rng.integers(600, 4000, nb)))
+    trim = bool(rng.random() < 0.3)
+    table_walk = bool(rng.random() < 0.3)
+    holes = int(rng.integers(0, 3))  # inactive entries inside a context
+    return dtype, d, bs, hkv, g, sq, [int(x) for x in lens], trim, table_walk, holes, rng
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_batches_vs_oracle(cuda, seed):
+    """Seeded random batches (shape, lengths, head trim, fixed-shape walk,
+    inactive entries inside a context) against the oracle."""
+    dtype, d, bs, hkv, g, sq, lens, trim, table_walk, holes, rng = random_case_params(seed)
+    c = small_case(cuda, seed, lens, bs, hkv, g, sq, d, dtype)
+    for _ in range(holes):
+        r = int(rng.integers(len(lens)))
+        n = -(-lens[r] // bs)
+        c["table"][r, int(rng.integers(n))] = -1
+    c["d_bt"] = torch.from_numpy(c["table"]).to(cuda)
+    width = c["table"].shape[1]
+    walk = max(1, -(-max(lens) // bs) - int(rng.integers(0, 2))) if trim else width
+    out = gpu_attn(c, walk_blocks=walk, flags=K.KVS_WALK_TABLE if table_walk else 0)
+    torch.cuda.synchronize()
+    err = max_err(out, ref_attn(c, walk=walk))
+    assert err <= TOL[dtype], (err, dtype, d, bs, hkv, g, sq, len(lens), walk, table_walk)
+
+
 def test_invariants_bitwise(cuda):
     c = small_case(cuda, 3, [1, 50, 64, 700, 3000], 64, 8, 4, 2, 128, "bf16", width=64)
     base = gpu_attn(c)
