@@ -524,20 +524,22 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         p.lse_out[((int64_t)r * Sq + jrow) * Hq + (int64_t)g * G + hh] = row_lse(m_run, l_tot);
       return;
     }
-    // split: publish this segment's partial state
-    float* prow = p.partials + ((((int64_t)slice + r) * Hkv + g) * nrows + rho) * PSTRIDE;
+    // split: publish this segment's partial state, in store order: float4
+    // k = i * NT / 4 + n0 / 4 of lane (jg, rho) sits at float4 index
+    // (k * 4 + jg) * nrows + rho of the slot, so each store writes one
+    // contiguous run (a row-major layout would put each lane's 16 bytes in
+    // a different cache line); (m, l) of row rho follow all the float4s.
+    float* pslot = p.partials + (((int64_t)slice + r) * Hkv + g) * nrows * PSTRIDE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int n0 = 0; n0 < NT; n0 += 4) {
+        const int k = i * (NT / 4) + n0 / 4;
         f32x4 v = {acc[n0][i], acc[n0 + 1][i], acc[n0 + 2][i], acc[n0 + 3][i]};
-        *(f32x4*)(prow + d_base + i * NT + n0) = v;
+        *(f32x4*)(pslot + ((k * 4 + jg) * nrows + rho) * 4) = v;
       }
     }
-    if (jg == 0) {
-      prow[D] = m_run;
-      prow[D + 1] = l_tot;
-    }
+    if (jg == 0) *(f32x2*)(pslot + nrows * D + 2 * rho) = (f32x2){m_run, l_tot};
   };
 
   // ---- this slice's context tiles, request by request ---------------------
@@ -676,29 +678,38 @@ paged_decode_combine_kernel(const DecodeParams p, int T) {
   const int tn = (int)min((int64_t)T, npieces - v0);
 
   // Piece v: unit u = v / pieces = (r, g); this lane's float4s f0 + 64 k.
+  // A unit's float4s are numbered in the order pass 1 stores them: float4 f
+  // of a partial slot holds dimensions (4 jg + i) NT + n0 .. + 3 of row rho,
+  // where f = (k * 4 + jg) * nrows + rho and k = i NT / 4 + n0 / 4
+  // (NT = D / 16); the (m, l) pairs of the rows follow the nrows * D floats.
   auto piece = [&](int64_t v, int& r, int& g, int& f0) {
     const int64_t u = v / pieces;
     f0 = (int)(v - u * pieces) * 64 * KCW + lane;
     r = (int)(u / Hkv);
     g = (int)(u - (int64_t)r * Hkv);
   };
-  auto float_offset = [&](int f) {  // of float4 f within one partial slot
-    const int row = f / F4ROW;
-    return row * PSTRIDE + (f - row * F4ROW) * 4;
+  auto row_of = [&](int f) { return f % nrows; };
+  auto ml_offset = [&](int f) { return nrows * D + 2 * row_of(f); };
+  auto dim_of = [&](int f) {  // first dimension of float4 f
+    constexpr int NT = D / 16;
+    const int kj = f / nrows;  // k * 4 + jg
+    const int k = kj >> 2, jg = kj & 3;
+    const int i = k / (NT / 4), n0 = (k - i * (NT / 4)) * 4;
+    return (4 * jg + i) * NT + n0;
   };
-  auto ml_offset = [&](int f) { return (f / F4ROW) * PSTRIDE + D; };
   auto partials_of = [&](int g, int slot) {
     return p.partials + ((int64_t)slot * Hkv + g) * nrows * PSTRIDE;
   };
   // Output float4 f of unit (r, g): normalise and store, with the row's lse.
   auto emit = [&](int r, int g, int f, float M, float Lt, f32x4 ot) {
-    const int row = f / F4ROW;
+    const int row = row_of(f);
+    const int d = dim_of(f);
     const int jr = row / G;
     const int hr = row - jr * G;
     const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
     const int64_t orow = ((int64_t)r * Sq + jr) * (G * Hkv) + (int64_t)g * G + hr;
-    *(f32x4*)(p.out + orow * D + (f - row * F4ROW) * 4) = ot * inv;
-    if (p.lse_out && f == row * F4ROW) p.lse_out[orow] = row_lse(M, Lt);
+    *(f32x4*)(p.out + orow * D + d) = ot * inv;
+    if (p.lse_out && d == 0) p.lse_out[orow] = row_lse(M, Lt);
   };
 
   // ---- wave w: piece w of the tile; merged here when 2 <= C <= CS ---------
@@ -721,7 +732,7 @@ paged_decode_combine_kernel(const DecodeParams p, int T) {
         for (int k = 0; k < KCW; ++k) {
           const int f = f0 + 64 * k;
           if (j < C && f < f4_total) {
-            a[j][k] = *(const f32x4*)(base + j * cstride + float_offset(f));
+            a[j][k] = *(const f32x4*)(base + j * cstride + 4 * f);
             ml[j][k] = *(const f32x2*)(base + j * cstride + ml_offset(f));
           }
         }
@@ -765,7 +776,7 @@ paged_decode_combine_kernel(const DecodeParams p, int T) {
         for (int k = 0; k < KCW; ++k) {
           const int f = f0 + 64 * k;
           if (cc < Cv && f < f4_total) {
-            a[j][k] = *(const f32x4*)(base + (int64_t)cc * cstride + float_offset(f));
+            a[j][k] = *(const f32x4*)(base + (int64_t)cc * cstride + 4 * f);
             ml[j][k] = *(const f32x2*)(base + (int64_t)cc * cstride + ml_offset(f));
           }
         }
