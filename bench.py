@@ -145,6 +145,20 @@ def attention_bytes(w, walk_blocks: int, table_walk: bool) -> int:
     return blocks * per_block + q_out + 4 * w.num_rows
 
 
+def attention_bytes_token_exact(w, walk_blocks: int) -> int:
+    """Lower bound beside the block count: only the K and V rows of the
+    visible positions (L instead of whole blocks), one table entry per block
+    holding one, q, fp32 out and seq_len."""
+    es = w.es
+    per_token = 2 * w.num_kv_heads * w.head_dim * es
+    total = 0
+    for r in range(w.num_rows):
+        vis = min(max(int(w.seq_lens[r]), 0), walk_blocks * w.block_size)
+        total += vis * per_token + 4 * (-(-vis // w.block_size))
+    q_out = w.num_rows * w.q_len * w.num_q_heads * w.head_dim * (es + 4)
+    return total + q_out + 4 * w.num_rows
+
+
 def dcp_attention_bytes(w, world: int, rank: int, interleave: int) -> int:
     """Algorithmic bytes of one rank's decode attention under context parallelism.
 
@@ -281,6 +295,9 @@ def main(argv=None) -> int:
     T = int(step_req.numel())
     T_live = int((step_req >= 0).sum().item())
     a_bytes = attention_bytes(w, walk_blocks, table_walk)
+    exact_bytes = attention_bytes_token_exact(w, walk_blocks)
+    if dcp or args.window:
+        exact_bytes = None  # reported for the plain walks only
     if dcp:
         a_bytes = dcp_attention_bytes(w, *dcp)
         walk_blocks = int(s.block_table.shape[1])
@@ -496,6 +513,8 @@ def main(argv=None) -> int:
         },
         "attention_gbps": round(attn_gbps, 2),
         "attention_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "attention_gbps_token_exact": (round(exact_bytes / t_attn / 1e9, 2)
+                                       if exact_bytes is not None else None),
         "decode_tokens_per_s": round(decode_tokens / (ms_per_step * 1e-3), 1),
         "slot_map_tokens_per_s": round(T / t_slot, 1),
         "slot_map_sweep": sweep,
@@ -506,7 +525,8 @@ def main(argv=None) -> int:
                       "paged_decode_attention": round(t_attn * 1e6, 3)},
         "algorithmic_bytes": {"kv_slot_mapping": slot_map_bytes(T),
                               "kv_cache_write": cache_write_bytes(w, T_live, T),
-                              "paged_decode_attention": a_bytes},
+                              "paged_decode_attention": a_bytes,
+                              "paged_decode_attention_token_exact": exact_bytes},
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_decode_attention",
