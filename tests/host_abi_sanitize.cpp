@@ -209,6 +209,10 @@ void check_gpu_entry_argument_checks() {
                                  128, 64, 1024, 0.088f, KVS_BF16, 0, nullptr, 0, nullptr,
                                  nullptr) == KVS_EINVAL,
           "null buffers");
+  require(paged_decode_attention(nullptr, nullptr, nullptr, nullptr, 80, 80, nullptr, 8193, 1, 32, 8,
+                                 128, 64, 1024, 0.088f, KVS_BF16, 0, nullptr, 0, nullptr,
+                                 nullptr) == KVS_EUNSUPPORTED,
+          "batch above the largest the decode kernels take");
   require(paged_decode_attention(nullptr, nullptr, nullptr, nullptr, 80, 81, nullptr, 12, 1, 32, 8,
                                  128, 64, 1024, 0.088f, KVS_BF16, 0, nullptr, 0, nullptr,
                                  nullptr) == KVS_EINVAL,

@@ -272,6 +272,30 @@ def test_shapes_vs_oracle(cuda, shape):
     assert err <= TOL[dtype], err
 
 
+@pytest.mark.parametrize("n, hkv", [(8192, 2), (1500, 8)])
+def test_many_requests_vs_oracle(cuda, n, hkv):
+    """Batches with several requests per thread in pass 1's prefix scan, up
+    to the largest batch the library takes (8192): mostly short contexts, a
+    few long ones split over several slices, some empty; checked against the
+    oracle on sampled rows, and empty rows give zeros."""
+    rng = np.random.default_rng(n)
+    lens = rng.integers(0, 64, n)
+    long_rows = rng.choice(n, 8, replace=False)
+    lens[long_rows] = rng.integers(500, 3000, 8)
+    c = small_case(cuda, n, [int(x) for x in lens], 16, hkv, 2, 1, 64, "bf16")
+    out = gpu_attn(c)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 200), long_rows,
+                                     np.flatnonzero(lens == 0)[:4]]))
+    want = O.paged_decode_attention(c["q"][rows], c["kc"], c["vc"], c["table"][rows],
+                                    lens[rows].astype(np.int32), c["table"].shape[1],
+                                    c["w"].scale, "bf16")
+    err = max_err(out[torch.from_numpy(rows).to(cuda)], want)
+    assert err <= TOL["bf16"], err
+    empty = torch.from_numpy(np.flatnonzero(lens == 0)).to(cuda)
+    assert empty.numel() > 0 and (out[empty] == 0).all()
+
+
 def random_case_params(seed):
     """A seeded random batch shape: dtype, head_dim, block size, heads, query
     tokens, lengths (mostly short, a few long), walk and flags."""
