@@ -775,6 +775,57 @@ def test_fused_step_vs_oracle(cuda, index):
     assert max_err(out, ref.attention(w.q())) <= TOL[w.dtype]
 
 
+def test_grid_stride_at_scale(cuda):
+    """Work past one launch's 65536 x 256 threads, so every thread of the
+    slot-map, cache-write and fused kernels takes a second grid stride:
+    2^24 + 1000 slots, and 1.1M tokens x 16 pieces of 16 bytes written,
+    against the oracle, bit-exact."""
+    rng = np.random.default_rng(11)
+    # slot map over 2^24 + 500 tokens (+500 tail): pads, rows and columns past the table
+    rows, width, bs = 4096, 64, 64
+    table = rng.permutation(np.arange(1, rows * width + 1)).reshape(rows, width).astype(np.int32)
+    T = (1 << 24) + 500
+    req = rng.integers(-1, rows + 1, T).astype(np.int32)
+    pos = rng.integers(0, width * bs + 64, T).astype(np.int64)
+    got = K.kv_slot_mapping(torch.from_numpy(req).to(cuda), torch.from_numpy(pos).to(cuda),
+                            torch.from_numpy(table).to(cuda), bs, max_num_tokens=T + 500)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), O.compute_slot_mapping(req, pos, table, bs, T + 500))
+    del got, req, pos
+
+    # 1100 requests x 1000 positions of fp32 rows (Hkv 1, D 64: 16 pieces a row)
+    nreq, per, width = 1100, 1000, 16
+    total = nreq * width + 1
+    table = rng.permutation(np.arange(1, total)).reshape(nreq, width).astype(np.int32)
+    table[rng.random(table.shape) < 0.02] = -1  # inactive entries: their tokens write nothing
+    req = np.repeat(np.arange(nreq, dtype=np.int32), per)
+    pos = np.tile(np.arange(per, dtype=np.int64), nreq)
+    req[rng.random(req.size) < 0.03] = -1  # padding tokens
+    T = req.size
+    k_new = rng.standard_normal((T, 1, 64)).astype(np.float32)
+    v_new = rng.standard_normal((T, 1, 64)).astype(np.float32)
+    want_slots = O.compute_slot_mapping(req, pos, table, bs)
+    kc = np.full((total, bs, 1, 64), np.nan, np.float32)
+    vc = kc.copy()
+    O.reshape_and_cache(k_new, v_new, want_slots, kc, vc)
+    d_req, d_pos = torch.from_numpy(req).to(cuda), torch.from_numpy(pos).to(cuda)
+    d_bt = torch.from_numpy(table).to(cuda)
+    d_k, d_v = torch.from_numpy(k_new).to(cuda), torch.from_numpy(v_new).to(cuda)
+    for fused in (True, False):
+        gk = torch.full((total, bs, 1, 64), float("nan"), dtype=torch.float32, device=cuda)
+        gv = gk.clone()
+        if fused:
+            slots = K.kv_slot_mapping_cache_write(d_req, d_pos, d_bt, d_k, d_v, gk, gv)
+        else:
+            slots = K.kv_slot_mapping(d_req, d_pos, d_bt, bs)
+            K.kv_cache_write(d_k, d_v, slots, gk, gv)
+        torch.cuda.synchronize()
+        assert np.array_equal(slots.cpu().numpy(), want_slots)
+        assert np.array_equal(host_bits(gk), kc.view(np.uint32)), f"fused={fused}"
+        assert np.array_equal(host_bits(gv), vc.view(np.uint32)), f"fused={fused}"
+        del gk, gv
+
+
 def test_fused_slot_write_empty(cuda):
     kc = torch.zeros((2, 16, 1, 64), dtype=torch.bfloat16, device=cuda)
     e32 = torch.zeros(0, dtype=torch.int32, device=cuda)
