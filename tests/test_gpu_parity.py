@@ -632,6 +632,34 @@ def test_dcp_ranks_and_merge_vs_oracle(cuda, world, interleave, bs, dtype, sq, g
     assert max_err(merged, want) <= TOL[dtype]
 
 
+def test_lse_merge_past_one_launch(cuda):
+    """decode_lse_merge over more float4s than one launch's threads (its grid
+    is capped at 65536 workgroups and loops): 2 ranks x 1.05M rows of 64,
+    some rows unseen by a rank or by both; sampled rows (those of the second
+    grid stride included) against the oracle merge."""
+    rng = np.random.default_rng(12)
+    world, rows, d = 2, 1_050_000, 64
+    outs = rng.standard_normal((world, rows, d)).astype(np.float32)
+    lses = (3 * rng.standard_normal((world, rows))).astype(np.float32)
+    lses[rng.random((world, rows)) < 0.05] = -np.inf
+    lses[:, rng.integers(0, rows, 100)] = -np.inf  # rows no rank saw
+    merged, mlse = K.decode_lse_merge(torch.from_numpy(outs).to(cuda), torch.from_numpy(lses).to(cuda))
+    torch.cuda.synchronize()
+    first_past = (65536 * 256) // (d // 4)  # first row of the second grid stride
+    sample = np.unique(np.concatenate([rng.integers(0, rows, 4000),
+                                       np.arange(first_past - 8, rows, 97), [0, rows - 1],
+                                       np.flatnonzero(np.isneginf(lses).all(axis=0))[:20]]))
+    want = O.merge_lse(outs[:, sample], lses[:, sample])
+    got = merged.cpu().numpy()[sample]
+    assert np.abs(got.astype(np.float64) - want).max() <= TOL["f32"]
+    gl = mlse.cpu().numpy()[sample].astype(np.float64)
+    with np.errstate(divide="ignore"):
+        wl = np.log(np.exp(lses[:, sample].astype(np.float64)).sum(axis=0))
+    assert np.array_equal(np.isneginf(gl), np.isneginf(wl))
+    fin = np.isfinite(wl)
+    assert (np.abs(gl[fin] - wl[fin]) <= LSE_TOL * np.maximum(1, np.abs(wl[fin]))).all()
+
+
 def test_dcp_workload_scale(cuda):
     """Ragged + speculative workload (64 requests, S_q 4) on rank 1 of 4: the
     rank's cache built and stepped through the library; sampled rows vs the
