@@ -296,6 +296,17 @@ def test_many_requests_vs_oracle(cuda, n, hkv):
     assert empty.numel() > 0 and (out[empty] == 0).all()
 
 
+def test_longest_context_vs_oracle(cuda):
+    """One request at 131071 tokens (the longest context below a 131072
+    max_model_len) beside a one-token request: 2048 blocks of 64, split over
+    every slice, merged from the most partials any request has."""
+    c = small_case(cuda, 77, [131071, 1], 64, 8, 4, 1, 128, "bf16")
+    out = gpu_attn(c)
+    torch.cuda.synchronize()
+    err = max_err(out, ref_attn(c))
+    assert err <= TOL["bf16"], err
+
+
 def random_case_params(seed):
     """A seeded random batch shape: dtype, head_dim, block size, heads, query
     tokens, lengths (mostly short, a few long), walk and flags."""
