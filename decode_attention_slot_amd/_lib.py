@@ -249,7 +249,8 @@ def paged_decode_attention_workspace_bytes(num_seqs: int, q_len: int, num_q_head
 
 def make_workspace(num_seqs: int, q_len: int, num_q_heads: int, num_kv_heads: int,
                    head_dim: int, device) -> torch.Tensor:
-    """A zero-filled workspace of the required size (zero before first use)."""
+    """A workspace of the required size (zero-filled, though the library needs
+    no initial contents)."""
     n = paged_decode_attention_workspace_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim)
     if n == 0:
         raise ValueError("invalid sizes for the decode workspace")

@@ -865,6 +865,46 @@ def test_grid_stride_at_scale(cuda):
         del gk, gv
 
 
+def test_step_replays_from_a_hip_graph(cuda):
+    """The bench step (fused slot map + write, then attention), its buffers
+    allocated beforehand, captured once in a HIP graph and replayed: every
+    replay, with eager library calls and host synchronisation in between,
+    gives the eager step's slots and output bitwise (the write is
+    idempotent: the same rows go to the same slots)."""
+    w = W.make_workload(1)
+    s = dev.build(w, cuda)
+    ws = K.make_workspace(w.num_rows, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim, cuda)
+    out = torch.empty((w.num_rows, w.q_len, w.num_q_heads, w.head_dim), dtype=torch.float32,
+                      device=cuda)
+    T = int(s.chunk_req.numel() + s.dec_req.numel())
+    slots = torch.empty(T, dtype=torch.int64, device=cuda)
+    dev.run_step(s, workspace=ws, out=out, slots_out=slots, fused=True)
+    torch.cuda.synchronize()
+    want_slots, want = slots.clone(), out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture's kind of stream
+        dev.run_step(s, workspace=ws, out=out, slots_out=slots, fused=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dev.run_step(s, workspace=ws, out=out, slots_out=slots, fused=True)
+    other_ws = K.make_workspace(w.num_rows, w.q_len, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                cuda)
+    for i in range(4):
+        out.fill_(float("nan"))
+        slots.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(slots, want_slots), i
+        assert torch.equal(out.view(torch.int32), want.view(torch.int32)), i
+        eager = K.paged_decode_attention(s.q, s.k_cache, s.v_cache, s.block_table, s.seq_lens,
+                                         w.scale, workspace=other_ws)
+        torch.cuda.synchronize()
+        assert torch.equal(eager.view(torch.int32), want.view(torch.int32)), i
+
+
 def test_fused_slot_write_empty(cuda):
     kc = torch.zeros((2, 16, 1, 64), dtype=torch.bfloat16, device=cuda)
     e32 = torch.zeros(0, dtype=torch.int32, device=cuda)
