@@ -2,6 +2,7 @@
 // points, and launches of the HIP kernels on the caller's stream.
 // The contract of every function is documented in include/kvslot.h.
 #include <limits.h>
+#include <stdint.h>
 #include <math.h>
 
 #include "kvslot.h"
@@ -12,6 +13,11 @@ namespace {
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? KVS_OK : KVS_EHIP; }
+
+// The kernels move element arrays with 16-byte vector operations and index
+// arrays element by element: the former need 16-byte alignment, the latter
+// their natural one. A null pointer counts as aligned (checked separately).
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
 int elem_bytes(kvs_dtype d) {
   switch (d) {
@@ -56,6 +62,10 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
     return KVS_EUNSUPPORTED;
   if (num_seqs == 0) return KVS_OK;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
+    return KVS_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(kv_pos_offset, 4) ||
+      !aligned(out, 16) || !aligned(lse, 4) || !aligned(workspace, 16))
     return KVS_EINVAL;
   const size_t need =
       paged_decode_attention_workspace_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim);
@@ -121,6 +131,9 @@ int kv_slot_mapping(const int32_t* req_indices, const int64_t* positions, int64_
   if (max_num_tokens > 0 && !slot_mapping) return KVS_EINVAL;
   if (num_tokens > 0 && (!req_indices || !positions)) return KVS_EINVAL;
   if (table_rows > 0 && !block_table) return KVS_EINVAL;
+  if (!aligned(req_indices, 4) || !aligned(positions, 8) || !aligned(block_table, 4) ||
+      !aligned(slot_mapping, 8))
+    return KVS_EINVAL;
   return launch_status(kvs::launch_slot_mapping(req_indices, positions, num_tokens,
                                                 max_num_tokens, block_table, table_rows,
                                                 table_stride, block_size, slot_mapping,
@@ -140,6 +153,9 @@ int kv_cache_write(const void* k_new, const void* v_new, const int64_t* slot_map
   if (total_blocks > INT64_MAX / block_size) return KVS_EINVAL;
   if (num_tokens == 0) return KVS_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return KVS_EINVAL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+    return KVS_EINVAL;
   return launch_status(kvs::launch_cache_write(k_new, v_new, slot_mapping, num_tokens, k_cache,
                                                v_cache, total_blocks * block_size,
                                                (int32_t)row_bytes, (hipStream_t)stream));
@@ -159,6 +175,9 @@ int kv_slot_mapping_dcp(const int32_t* req_indices, const int64_t* positions, in
   if (max_num_tokens > 0 && !slot_mapping) return KVS_EINVAL;
   if (num_tokens > 0 && (!req_indices || !positions)) return KVS_EINVAL;
   if (table_rows > 0 && !block_table) return KVS_EINVAL;
+  if (!aligned(req_indices, 4) || !aligned(positions, 8) || !aligned(block_table, 4) ||
+      !aligned(slot_mapping, 8))
+    return KVS_EINVAL;
   return launch_status(kvs::launch_slot_mapping_dcp(
       req_indices, positions, num_tokens, max_num_tokens, block_table, table_rows, table_stride,
       block_size, cp_world_size, cp_rank, cp_interleave, slot_mapping, (hipStream_t)stream));
@@ -184,6 +203,10 @@ int kv_slot_mapping_cache_write(const int32_t* req_indices, const int64_t* posit
       (!req_indices || !positions || !k_new || !v_new || !k_cache || !v_cache))
     return KVS_EINVAL;
   if (table_rows > 0 && !block_table) return KVS_EINVAL;
+  if (!aligned(req_indices, 4) || !aligned(positions, 8) || !aligned(block_table, 4) ||
+      !aligned(slot_mapping, 8) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return KVS_EINVAL;
   return launch_status(kvs::launch_slot_write(
       req_indices, positions, num_tokens, max_num_tokens, block_table, table_rows, table_stride,
       block_size, slot_mapping, k_new, v_new, k_cache, v_cache, total_blocks * block_size,
@@ -331,6 +354,8 @@ int decode_lse_merge(const float* outs, const float* lses, int32_t world, int64_
                      int32_t head_dim, float* out, float* lse, void* stream) {
   if (world < 1 || rows < 0 || head_dim < 4 || head_dim % 4 != 0) return KVS_EINVAL;
   if (rows > 0 && (!outs || !lses || !out)) return KVS_EINVAL;
+  if (!aligned(outs, 16) || !aligned(lses, 4) || !aligned(out, 16) || !aligned(lse, 4))
+    return KVS_EINVAL;
   if (rows > INT64_MAX / head_dim / world) return KVS_EINVAL;
   return launch_status(
       kvs::launch_lse_merge(outs, lses, world, rows, head_dim, out, lse, (hipStream_t)stream));

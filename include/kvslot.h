@@ -23,6 +23,11 @@
  *   the null stream) and returns. No entry point synchronises, reads device
  *   memory on the host, or allocates or frees memory. The caller owns every
  *   buffer.
+ * - Alignment: arrays of cache elements and of fp32 results (q, k_cache,
+ *   v_cache, k_new, v_new, out, outs and the decode workspace) must be
+ *   16-byte aligned, int32 and int64 arrays naturally aligned; otherwise
+ *   the entry point returns KVS_EINVAL. (Rows of the supported shapes are
+ *   multiples of 16 bytes, so whole-row offsets keep the alignment.)
  * - Only scalar arguments and pointers are checked. A bad value inside a
  *   device array (a block id, a slot, a length) is a caller error: the
  *   kernels clamp their reads to the given sizes and skip what is out of
@@ -42,7 +47,7 @@ extern "C" {
 #endif
 
 #define KVS_OK 0
-#define KVS_EINVAL (-1)       /* null pointer, negative size, bad scalar      */
+#define KVS_EINVAL (-1)       /* null or misaligned pointer, bad size/scalar  */
 #define KVS_EUNSUPPORTED (-2) /* dtype, head_dim, block_size or shape          */
 #define KVS_EBUCKET (-3)      /* bucket list fails the [CLB] validation rules  */
 #define KVS_ERANGE (-4)       /* needed_seq beyond max_model_len               */

@@ -217,6 +217,52 @@ void check_gpu_entry_argument_checks() {
                                  128, 64, 1024, 0.088f, KVS_BF16, 0, nullptr, 0, nullptr,
                                  nullptr) == KVS_EINVAL,
           "walk beyond the table");
+  // Misaligned pointers (fake addresses, never dereferenced): rejected
+  // before any device work, whatever else the call holds.
+  const auto at = [](uintptr_t a) { return reinterpret_cast<void*>(a); };
+  int32_t* const i16 = static_cast<int32_t*>(at(0x100000));
+  int64_t* const l16 = static_cast<int64_t*>(at(0x100000));
+  float* const f16 = static_cast<float*>(at(0x100000));
+  require(kv_slot_mapping(i16, static_cast<int64_t*>(at(0x100004)), 8, 8, i16, 4, 4, 16, l16,
+                          nullptr) == KVS_EINVAL,
+          "positions not 8-byte aligned");
+  require(kv_slot_mapping(static_cast<int32_t*>(at(0x100002)), l16, 8, 8, i16, 4, 4, 16, l16,
+                          nullptr) == KVS_EINVAL,
+          "request indices not 4-byte aligned");
+  require(kv_slot_mapping_dcp(i16, l16, 8, 8, i16, 4, 4, 16, 2, 0, 1,
+                              static_cast<int64_t*>(at(0x100004)), nullptr) == KVS_EINVAL,
+          "dcp slots not 8-byte aligned");
+  require(kv_cache_write(at(0x100008), at(0x100000), l16, 8, at(0x100000), at(0x100000), 4, 16,
+                         8, 128, KVS_BF16, nullptr) == KVS_EINVAL,
+          "new K rows not 16-byte aligned");
+  require(kv_cache_write(at(0x100000), at(0x100000), l16, 8, at(0x100000), at(0x100008), 4, 16,
+                         8, 128, KVS_BF16, nullptr) == KVS_EINVAL,
+          "V cache not 16-byte aligned");
+  require(kv_slot_mapping_cache_write(i16, l16, 8, 8, i16, 4, 4, 16, l16, at(0x100000),
+                                      at(0x100000), at(0x100004), at(0x100000), 4, 8, 128,
+                                      KVS_BF16, nullptr) == KVS_EINVAL,
+          "fused write: K cache not 16-byte aligned");
+  require(paged_decode_attention(at(0x100008), at(0x100000), at(0x100000), i16, 80, 80, i16, 12, 1,
+                                 32, 8, 128, 64, 1024, 0.088f, KVS_BF16, 0, at(0x100000),
+                                 SIZE_MAX, f16, nullptr) == KVS_EINVAL,
+          "q not 16-byte aligned");
+  require(paged_decode_attention(at(0x100000), at(0x100000), at(0x100000), i16, 80, 80, i16, 12, 1,
+                                 32, 8, 128, 64, 1024, 0.088f, KVS_BF16, 0, at(0x100008),
+                                 SIZE_MAX, f16, nullptr) == KVS_EINVAL,
+          "workspace not 16-byte aligned");
+  require(paged_decode_attention(at(0x100000), at(0x100000), at(0x100000), i16, 80, 80,
+                                 static_cast<int32_t*>(at(0x100002)), 12, 1, 32, 8, 128, 64, 1024,
+                                 0.088f, KVS_BF16, 0, at(0x100000), SIZE_MAX, f16,
+                                 nullptr) == KVS_EINVAL,
+          "seq_lens not 4-byte aligned");
+  require(paged_decode_attention_dcp(at(0x100000), at(0x100000), at(0x100000), i16, 80, 80, i16,
+                                     12, 1, 32, 8, 128, 64, 1024, 0.088f, KVS_BF16, 2, 0, 1,
+                                     at(0x100000), SIZE_MAX, f16,
+                                     static_cast<float*>(at(0x100002)), nullptr) == KVS_EINVAL,
+          "lse not 4-byte aligned");
+  require(decode_lse_merge(static_cast<float*>(at(0x100008)), f16, 2, 16, 128, f16, f16,
+                           nullptr) == KVS_EINVAL,
+          "merge inputs not 16-byte aligned");
   // workspace size query: extreme sizes neither overflow nor trap
   const int32_t big[] = {0, 1, 8192, INT32_MAX};
   for (int32_t B : big)
