@@ -238,6 +238,9 @@ def main(argv=None) -> int:
                     help="decode context parallelism over this many ranks: measure rank 0's share "
                          "(its cache holds only its tokens; paged_decode_attention_dcp)")
     ap.add_argument("--dcp-interleave", type=int, default=1)
+    ap.add_argument("--tp", type=int, default=1,
+                    help="tensor parallelism over KV heads: measure one rank's share "
+                         "(num_kv_heads / tp KV heads and the matching query heads)")
     ap.add_argument("--separate-write", action="store_true",
                     help="step uses kv_slot_mapping + kv_cache_write (two launches) instead of "
                          "kv_slot_mapping_cache_write")
@@ -266,6 +269,8 @@ def main(argv=None) -> int:
     idx = WORKLOADS[args.workload]
     extra = {"forced_max_ctx": args.max_ctx} if (idx == 2 and args.max_ctx is not None) else {}
     w = W.make_workload(idx, seed=args.seed, **extra)
+    if args.tp > 1:
+        w = W.tp_share(w, args.tp)
     batch_buckets = [int(x) for x in args.batch_buckets.split(",")] if args.batch_buckets else None
     num_active = w.num_rows
     if batch_buckets:
@@ -509,7 +514,10 @@ def main(argv=None) -> int:
             "cache_copies_rotated": R,
             "step_write": "separate" if (args.separate_write or dcp) else "fused",
             "dcp": {"world": dcp[0], "rank": dcp[1], "interleave": dcp[2]} if dcp else None,
-            "parallelism": "single GPU",
+            "tp": args.tp,
+            "heads": {"kv": w.num_kv_heads, "q": w.num_q_heads},
+            "parallelism": ("single GPU" if args.tp == 1 else
+                            f"single GPU: one rank's share under tensor parallelism {args.tp}"),
         },
         "attention_gbps": round(attn_gbps, 2),
         "attention_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
@@ -536,7 +544,8 @@ def main(argv=None) -> int:
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(args.workload,
                                         f"window{args.window}" if args.window else
-                                        (f"dcp{dcp[0]}" if dcp else args.walk)),
+                                        (f"dcp{dcp[0]}" if dcp else
+                                         (f"tp{args.tp}" if args.tp > 1 else args.walk))),
         },
         "setup_s": round(t_setup, 2),
     }

@@ -657,7 +657,7 @@ paged_decode_combine_kernel(const DecodeParams p, int T) {
   constexpr int PSTRIDE = D + 4;
   // Sequential path: up to CS partials, all in flight; CS <= NG keeps it
   // equal to the grouped definition.
-  constexpr int CS = (16 / KCW) < NG ? 16 / KCW : NG;
+  constexpr int CS = (32 / KCW) < NG ? 32 / KCW : NG;
   constexpr int CB = KCW >= 8 ? 1 : 8 / KCW;  // grouped path: partials in flight per wave
   __shared__ float s_m[NG][KCW * 64];
   __shared__ float s_l[NG][KCW * 64];
@@ -874,16 +874,36 @@ hipError_t launch_merge(const DecodeParams& p, int kc, hipStream_t stream) {
   return launch_merge_shape<D, KMAX, NG>(p, units * ((kc + KMAX - 1) / KMAX), resw, stream);
 }
 
+// Compute units of the current device, queried once per device.
+hipError_t device_cus(int* out) {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && (*out = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+  e = hipDeviceGetAttribute(out, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*out < 1) *out = 1;
+  if (cached) cache[dev].store(*out, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
 template <bool BF16, int D, int NW>
 hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t stream) {
   const int HG = pin.num_kv_heads / NW;
-  int resident = 0;
+  int resident = 0, cus = 0;
   hipError_t e = resident_workgroups<BF16, D, NW>(&resident);
   if (e != hipSuccess) return e;
-  // One slice per resident workgroup slot (per head group), never more than
-  // the workspace holds partials for.
+  e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  // One slice per resident workgroup slot (per head group), at most eight
+  // waves per compute unit (more waves add partials to merge but no bytes
+  // in flight that the stream needs), never more than the workspace holds
+  // partials for.
   DecodeParams p = pin;
-  p.slices = resident / HG > 1 ? resident / HG : 1;
+  const int wgs = resident < cus * (8 / NW) ? resident : cus * (8 / NW);
+  p.slices = wgs / HG > 1 ? wgs / HG : 1;
   if (p.slices > p.max_slices) p.slices = p.max_slices;
   const dim3 grid((unsigned)p.slices * (unsigned)HG);
   const size_t lds = decode_lds_bytes(p.num_seqs);

@@ -172,6 +172,25 @@ def test_large_batch_block_split(cuda, large_batch):
     assert (out[real:] == 0).all()  # padded rows produce zeros
 
 
+@pytest.mark.parametrize("tp", [2, 8])
+def test_tensor_parallel_share_at_scale(cuda, tp):
+    """One tensor-parallel rank's share of the 256-request batch (Hkv / tp KV
+    heads: 4, or 1 with 3072 one-wave slices): the step through the library,
+    sampled rows against the oracle, padded rows zero."""
+    w = W.tp_share(W.make_workload(3), tp)
+    s = dev.build(w, cuda, threads=16)
+    slots, out = dev.run_step(s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(tp)
+    real = w.num_reqs
+    rows = sorted({0, real - 1, *map(int, rng.choice(real, 4, replace=False)),
+                   int(np.argmax(w.seq_lens[:real]))})
+    ref = OracleStep(w, s.host_table, requests=rows, full_image=False)
+    assert np.array_equal(slots.cpu().numpy(), ref.write_step())
+    assert max_err(out, ref.attention(w.q()), rows) <= TOL[w.dtype]
+    assert (out[real:] == 0).all()
+
+
 def test_large_batch_manager_view_equals_kernel_view(cuda, large_batch):
     """The same pool read at manager block size 32 gives the same output."""
     w, s = large_batch

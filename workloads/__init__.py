@@ -315,6 +315,16 @@ def pad_batch(w: Workload, rows: int) -> Workload:
     return dataclasses.replace(w, **kw)
 
 
+def tp_share(w: Workload, tp: int) -> Workload:
+    """One tensor-parallel rank's share of a workload: num_kv_heads / tp KV
+    heads and the matching num_q_heads / tp query heads, as a rank holds them
+    ([KVC] KVCacheConfig at tensor parallelism 2: 8 KV heads become 4)."""
+    if tp < 1 or w.num_kv_heads % tp or w.num_q_heads % tp:
+        raise ValueError(f"tp {tp} does not divide {w.num_kv_heads} KV heads")
+    return dataclasses.replace(w, num_kv_heads=w.num_kv_heads // tp,
+                               num_q_heads=w.num_q_heads // tp)
+
+
 def make_workload(index: int, seed: Optional[int] = None, **kw) -> Workload:
     """Build config ``index`` (0..4) with ``seed`` (default 1000 + index).
 
