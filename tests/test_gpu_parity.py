@@ -278,6 +278,13 @@ SHAPES = [
     ("bf16", 128, 32, 4, 1, 16, [16, 40, 2100]),
     ("bf16", 128, 16, 2, 3, 5, [5, 6, 49, 5000]),  # G*Sq = 15, long split-K
     ("f32", 128, 16, 8, 1, 1, [9000, 9000]),        # many chunks per request
+    # KV-head counts that are not 1, 2, 4 or 8: one-wave groups of 3, two-wave
+    # groups of 6, and several 8-wave head groups per slice (12, 16, 32)
+    ("bf16", 128, 64, 3, 2, 1, [7, 700, 3000]),
+    ("bf16", 64, 16, 6, 2, 2, [2, 33, 1800]),
+    ("bf16", 128, 32, 12, 1, 4, [4, 500, 2500]),
+    ("bf16", 128, 64, 16, 2, 1, [1, 64, 4100]),
+    ("f32", 64, 16, 32, 1, 1, [1, 300, 1200]),
 ]
 
 
@@ -333,7 +340,7 @@ def random_case_params(seed):
     dtype = ["f32", "bf16"][rng.integers(2)]
     d = [64, 128][rng.integers(2)]
     bs = [16, 32, 64, 128, 256][rng.integers(5)]
-    hkv = [1, 2, 4, 8][rng.integers(4)]
+    hkv = [1, 2, 3, 4, 6, 8, 12, 16][rng.integers(8)]
     sq = int(rng.integers(1, 5))
     g = int(rng.choice([x for x in (1, 2, 3, 4, 8) if x * sq <= 16]))
     nb = int(rng.integers(1, 41))
