@@ -525,6 +525,24 @@ def test_swa_trimmed_vs_oracle(cuda, shape):
     np.testing.assert_array_equal(want, want_t)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_swa_random_vs_oracle(cuda, seed):
+    """Seeded random sliding-window batches (shape, window from 1 to past the
+    longest context, mostly short contexts) on the tail-trimmed table,
+    against the oracle over the whole table."""
+    dtype, d, bs, hkv, g, sq, lens, _, _, _, rng = random_case_params(20_000 + seed)
+    window = int(rng.choice([1, int(rng.integers(2, 64)), int(rng.integers(64, 2000)),
+                             max(lens) + 100]))
+    c = swa_case(cuda, (dtype, d, bs, hkv, g, sq, window, lens), seed=seed)
+    w = c["w"]
+    out = swa_gpu(c)
+    torch.cuda.synchronize()
+    want = O.paged_decode_attention(c["q"], c["kc"], c["vc"], c["table"], w.seq_lens,
+                                    c["table"].shape[1], w.scale, w.dtype, window=window)
+    err = max_err(out, want)
+    assert err <= TOL[dtype], (dtype, d, bs, hkv, g, sq, window, lens[:8], err)
+
+
 def test_swa_trimmed_equals_whole_table_bitwise(cuda):
     c = swa_case(cuda, SWA_SHAPES[4])
     trimmed = swa_gpu(c)
