@@ -17,8 +17,9 @@
 // How, on CDNA4:
 // * Work split: the 16-token tiles of every request's context, laid end to
 //   end over the batch, are cut into `slices` equal ranges, one per
-//   resident workgroup slot, so every workgroup streams the same number of
-//   bytes and all finish together (no rounds, no tail of short units). A
+//   resident workgroup slot (at most eight waves per compute unit), so every
+//   workgroup streams the same number of bytes and all finish together (no
+//   rounds, no tail of short units). A
 //   range may start or end inside a request and may span requests; each
 //   (slice, request) piece is a segment. One wavefront per KV head; a
 //   workgroup holds the waves of NW KV heads, so the [block][token][head]
