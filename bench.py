@@ -1,18 +1,22 @@
 """Benchmark of the Block KV decode step on one MI355X.
 
 One step = the whole hot path over one batch: the host bucket pick
-(select_ctx_bucket), then on the GPU kv_slot_mapping and kv_cache_write of
-the step's new tokens, then paged_decode_attention. Inputs are seeded and
-synthetic and already resident in HBM when the timed region starts (the
-prior context is prefilled through the library beforehand, untimed).
-HIP events on the launch stream bracket the attention call of every eighth
-timed step (an event is a marker the GPU processes in line, so marking every
-step would slow the steps being timed). The events are created with
+(select_ctx_bucket), then on the GPU the slot mapping and cache write of the
+step's new tokens and the decode attention. By default the GPU part is one
+paged_decode_attention_append call (the decode launch writes the step's rows
+itself when they qualify); --fused-write runs kv_slot_mapping_cache_write
+then paged_decode_attention, --separate-write kv_slot_mapping and
+kv_cache_write then paged_decode_attention. Inputs are seeded and synthetic
+and already resident in HBM when the timed region starts (the prior context
+is prefilled through the library beforehand, untimed).
+HIP events on the launch stream bracket the attention call (with the append,
+the call that also writes the step's rows) of every eighth timed step (an
+event is a marker the GPU processes in line, so marking every step would
+slow the steps being timed). The events are created with
 hipEventDisableSystemFence: a default event's record also writes back and
 invalidates the caches at system scope, which adds to the timed work. The
-slot mapping and cache write kernels (and their one-launch fusion, which the
-step uses unless --separate-write) are timed after the steps, each in a run
-of back-to-back launches.
+slot mapping and cache write kernels and their one-launch fusion are timed
+after the steps, each in a run of back-to-back launches.
 
 The step rotates over several identical copies of the KV cache so that the
 bytes a step reads come from HBM, not from the last step's L2 / MALL lines.
@@ -242,8 +246,11 @@ def main(argv=None) -> int:
                     help="tensor parallelism over KV heads: measure one rank's share "
                          "(num_kv_heads / tp KV heads and the matching query heads)")
     ap.add_argument("--separate-write", action="store_true",
-                    help="step uses kv_slot_mapping + kv_cache_write (two launches) instead of "
-                         "kv_slot_mapping_cache_write")
+                    help="step uses kv_slot_mapping + kv_cache_write (two launches), then "
+                         "paged_decode_attention")
+    ap.add_argument("--fused-write", action="store_true",
+                    help="step uses kv_slot_mapping_cache_write, then paged_decode_attention, "
+                         "instead of paged_decode_attention_append")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the steps, run one plain device copy of this size (counter scale)")
     args = ap.parse_args(argv)
@@ -363,6 +370,17 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
+    # The default step is one paged_decode_attention_append call (the step's
+    # write inside the decode launch when it qualifies); the sliding-window
+    # and context-parallel steps have no append call.
+    append = not (dcp or args.window or args.separate_write or args.fused_write)
+    f_append = lib.paged_decode_attention_append
+    append_args = [(step_req.data_ptr(), step_pos.data_ptr(), T, T, slots.data_ptr(),
+                    step_k.data_ptr(), step_v.data_ptr(), s.q.data_ptr(), kc.data_ptr(),
+                    vc.data_ptr(), s.block_table.data_ptr(), int(stride), int(walk_blocks),
+                    s.seq_lens.data_ptr(), w.num_rows, w.q_len, w.num_q_heads, w.num_kv_heads,
+                    w.head_dim, w.block_size, w.total_blocks, w.scale, dt, flags, ws.data_ptr(),
+                    int(ws.numel()), out.data_ptr(), sp) for kc, vc in caches]
     f_slot, f_write = lib.kv_slot_mapping, lib.kv_cache_write
     f_fused = lib.kv_slot_mapping_cache_write
     f_slot_dcp = lib.kv_slot_mapping_dcp
@@ -379,6 +397,15 @@ def main(argv=None) -> int:
         if batch_buckets:
             K.select_batch_bucket(num_active, batch_buckets)
         j = i % R
+        if append:
+            if ev is not None:
+                ev[0].record(sp)
+            st = f_append(*append_args[j])
+            if ev is not None:
+                ev[1].record(sp)
+            if st:
+                raise RuntimeError(f"library call failed with status {st}")
+            return
         if dcp:
             st = f_slot_dcp(*slot_dcp_args)
             st |= f_write(*write_args[j])
@@ -432,6 +459,9 @@ def main(argv=None) -> int:
     t_slot = back_to_back(f_slot, [slot_args], args.steps)
     t_write = back_to_back(f_write, write_args, args.steps)
     t_fused = back_to_back(f_fused, fused_args, args.steps)
+    # With the append step, the attention call on its own (back to back, the
+    # caches already holding the step's rows) for reference.
+    t_attn_only = back_to_back(f_attn, attn_args, args.steps) if append else t_attn
 
     # Under context parallelism the ranks' (out, lse) would be all-gathered
     # and merged by decode_lse_merge; one GPU holds only rank 0's share, so
@@ -486,7 +516,11 @@ def main(argv=None) -> int:
         write_bytes -= 8 * T  # the one-launch write keeps the slots in registers
     step_bytes = slot_map_bytes(T) + write_bytes + a_bytes
     decode_tokens = w.num_reqs * w.q_len
-    attn_gbps = a_bytes / t_attn / 1e9
+    attn_gbps = a_bytes / t_attn_only / 1e9
+    # the call the timed steps make: with the append it also moves the step's
+    # slots and rows, and is credited with those bytes
+    call_bytes = step_bytes if append else a_bytes
+    call_gbps = call_bytes / t_attn / 1e9
     result = {
         "metric": "paged decode attention HBM GB/s (% of peak) + decode tokens/s; slot_map tok/s",
         "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
@@ -512,7 +546,8 @@ def main(argv=None) -> int:
             "bucket_len": int(bucket_len),
             "step_tokens": T,
             "cache_copies_rotated": R,
-            "step_write": "separate" if (args.separate_write or dcp) else "fused",
+            "step_write": ("in the decode call (paged_decode_attention_append)" if append else
+                           "separate" if (args.separate_write or dcp) else "fused"),
             "dcp": {"world": dcp[0], "rank": dcp[1], "interleave": dcp[2]} if dcp else None,
             "tp": args.tp,
             "heads": {"kv": w.num_kv_heads, "q": w.num_q_heads},
@@ -521,7 +556,7 @@ def main(argv=None) -> int:
         },
         "attention_gbps": round(attn_gbps, 2),
         "attention_frac_of_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
-        "attention_gbps_token_exact": (round(exact_bytes / t_attn / 1e9, 2)
+        "attention_gbps_token_exact": (round(exact_bytes / t_attn_only / 1e9, 2)
                                        if exact_bytes is not None else None),
         "decode_tokens_per_s": round(decode_tokens / (ms_per_step * 1e-3), 1),
         "slot_map_tokens_per_s": round(T / t_slot, 1),
@@ -530,18 +565,21 @@ def main(argv=None) -> int:
         "kernel_us": {"kv_slot_mapping": round(t_slot * 1e6, 3),
                       "kv_cache_write": round(t_write * 1e6, 3),
                       "kv_slot_mapping_cache_write": round(t_fused * 1e6, 3),
-                      "paged_decode_attention": round(t_attn * 1e6, 3)},
+                      "paged_decode_attention": round(t_attn_only * 1e6, 3),
+                      "paged_decode_attention_append": round(t_attn * 1e6, 3) if append else None},
         "algorithmic_bytes": {"kv_slot_mapping": slot_map_bytes(T),
                               "kv_cache_write": cache_write_bytes(w, T_live, T),
                               "paged_decode_attention": a_bytes,
-                              "paged_decode_attention_token_exact": exact_bytes},
+                              "paged_decode_attention_token_exact": exact_bytes,
+                              "paged_decode_attention_append": call_bytes if append else None},
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_attention",
-            "achieved": round(attn_gbps, 2),
+            "kernel": ("paged_decode_attention_append (the step's slots and rows written "
+                       "inside; their bytes credited)" if append else "paged_decode_attention"),
+            "achieved": round(call_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+            "frac": round(call_gbps / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(args.workload,
                                         f"window{args.window}" if args.window else
                                         (f"dcp{dcp[0]}" if dcp else

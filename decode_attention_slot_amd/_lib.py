@@ -36,6 +36,7 @@ EXPORTS = (
     "kv_map_to_kernel_blocks",
     "paged_decode_attention_workspace_bytes",
     "paged_decode_attention",
+    "paged_decode_attention_append",
     "paged_decode_attention_swa",
     "kv_swa_tail_trim",
     "kv_slot_mapping_dcp",
@@ -82,6 +83,10 @@ def _lib():
             vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32, i64, f32,
             ctypes.c_int, u32, vp, sz, vp, vp,
         ]
+        lib.paged_decode_attention_append.argtypes = [
+            vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32,
+            i32, i64, f32, ctypes.c_int, u32, vp, sz, vp, vp,
+        ]
         lib.paged_decode_attention_swa.argtypes = [
             vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i64, f32,
             ctypes.c_int, vp, sz, vp, vp,
@@ -96,6 +101,7 @@ def _lib():
         lib.select_batch_bucket.argtypes = [i32, vp, i32, vp]
         for name in ("kv_slot_mapping", "kv_cache_write", "kv_slot_mapping_cache_write",
                      "select_ctx_bucket", "kv_map_to_kernel_blocks", "paged_decode_attention",
+                     "paged_decode_attention_append",
                      "paged_decode_attention_swa", "kv_swa_tail_trim", "kv_slot_mapping_dcp",
                      "paged_decode_attention_dcp", "decode_lse_merge", "select_batch_bucket"):
             getattr(lib, name).restype = ctypes.c_int
@@ -289,6 +295,52 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         _dev(out, "out", torch.float32), _stream(q, stream))
     _check(st, "paged_decode_attention")
     return out
+
+
+def paged_decode_attention_append(req_indices: torch.Tensor, positions: torch.Tensor,
+                                  k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                                  k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                                  walk_blocks: Optional[int] = None, flags: int = 0,
+                                  workspace: Optional[torch.Tensor] = None,
+                                  out: Optional[torch.Tensor] = None,
+                                  slot_mapping: Optional[torch.Tensor] = None,
+                                  max_num_tokens: Optional[int] = None, stream=None):
+    """The step's cache write and decode attention in one call; returns
+    (slot_mapping, out). See paged_decode_attention_append in kvslot.h."""
+    B, Sq, Hq, D = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != D or q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype \
+            or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("paged_decode_attention_append: shape or dtype mismatch")
+    T = int(req_indices.numel())
+    if positions.numel() != T or tuple(k_new.shape) != (T, hkv, D) \
+            or tuple(v_new.shape) != (T, hkv, D) or k_new.dtype != k_cache.dtype \
+            or v_new.dtype != k_cache.dtype:
+        raise ValueError("paged_decode_attention_append: step token shapes or dtypes mismatch")
+    if block_table.shape[0] < B or seq_lens.numel() < B:
+        raise ValueError("paged_decode_attention_append: block_table / seq_lens have too few rows")
+    stride = int(block_table.shape[1])
+    walk = stride if walk_blocks is None else int(walk_blocks)
+    if slot_mapping is None:
+        n = T if max_num_tokens is None else int(max_num_tokens)
+        slot_mapping = torch.empty(n, dtype=torch.int64, device=q.device)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = make_workspace(B, Sq, Hq, hkv, D, q.device)
+    st = _lib().paged_decode_attention_append(
+        _dev(req_indices, "req_indices", torch.int32), _dev(positions, "positions", torch.int64),
+        T, int(slot_mapping.numel()), _dev(slot_mapping, "slot_mapping", torch.int64),
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table", torch.int32, 2), stride, walk,
+        _dev(seq_lens, "seq_lens", torch.int32), int(B), int(Sq), int(Hq), int(hkv), int(D),
+        int(bs), int(nb), float(scale), _kvs_dtype(k_cache), int(flags),
+        _dev(workspace, "workspace", torch.uint8), int(workspace.numel()),
+        _dev(out, "out", torch.float32), _stream(q, stream))
+    _check(st, "paged_decode_attention_append")
+    return slot_mapping, out
 
 
 def paged_decode_attention_swa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -34,6 +34,16 @@ constexpr int kMaxSeqs = kvs::kDecodeMaxSeqs;
 
 namespace {
 
+// The step's tokens written by the decode launch itself (append entry point).
+struct AppendArgs {
+  const int32_t* req_indices;
+  const int64_t* positions;
+  int64_t num_tokens, max_num_tokens;
+  int64_t* slot_mapping;
+  const void* k_new;
+  const void* v_new;
+};
+
 int decode_common(const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_table, int32_t table_stride, int32_t walk_blocks,
                   const int32_t* seq_lens, const int32_t* kv_pos_offset, int32_t window,
@@ -41,7 +51,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
                   int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                   int32_t head_dim, int32_t block_size, int64_t total_blocks, float scale,
                   kvs_dtype dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
-                  float* out, float* lse, void* stream) {
+                  float* out, float* lse, void* stream, const AppendArgs* app = nullptr) {
   if (num_seqs < 0 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
       block_size < 1 || table_stride < 1 || walk_blocks < 0 || walk_blocks > table_stride ||
       total_blocks < 1 || !isfinite(scale) || window < 0 || cp_world < 1 || cp_rank < 0 ||
@@ -60,7 +70,27 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
   // the batch's 16-token tiles are counted in 32 bits, with headroom
   if ((int64_t)num_seqs * (walk_blocks * (int64_t)(block_size / 16) + 1) > INT_MAX / 2)
     return KVS_EUNSUPPORTED;
-  if (num_seqs == 0) return KVS_OK;
+  if (app) {
+    if (app->num_tokens < 0 || app->max_num_tokens < app->num_tokens) return KVS_EINVAL;
+    if (app->max_num_tokens > 0 && !app->slot_mapping) return KVS_EINVAL;
+    if (app->num_tokens > 0 && (!app->req_indices || !app->positions || !app->k_new ||
+                                !app->v_new || !k_cache || !v_cache || !block_table))
+      return KVS_EINVAL;
+    if (!aligned(app->req_indices, 4) || !aligned(app->positions, 8) ||
+        !aligned(app->slot_mapping, 8) || !aligned(app->k_new, 16) || !aligned(app->v_new, 16))
+      return KVS_EINVAL;
+    if (total_blocks > INT64_MAX / block_size) return KVS_EINVAL;
+  }
+  if (num_seqs == 0) {
+    // no attention; the step's tokens are still written (no table row to hit)
+    if (!app || app->max_num_tokens == 0) return KVS_OK;
+    return launch_status(kvs::launch_slot_write(
+        app->req_indices, app->positions, app->num_tokens, app->max_num_tokens, block_table, 0,
+        table_stride, block_size, app->slot_mapping, app->k_new, app->v_new,
+        const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+        total_blocks * block_size, num_kv_heads * head_dim * elem_bytes(dtype),
+        (hipStream_t)stream));
+  }
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
     return KVS_EINVAL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
@@ -101,6 +131,17 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   p.flags = flags;
   p.is_bf16 = dtype == KVS_BF16;
+  if (app && app->max_num_tokens > 0) {
+    p.app_req = app->req_indices;
+    p.app_pos = app->positions;
+    p.app_k = app->k_new;
+    p.app_v = app->v_new;
+    p.app_k_cache = const_cast<void*>(k_cache);
+    p.app_v_cache = const_cast<void*>(v_cache);
+    p.app_slots = app->slot_mapping;
+    p.app_tokens = app->num_tokens;
+    p.app_max_tokens = app->max_num_tokens;
+  }
   return launch_status(kvs::launch_paged_decode(p, (hipStream_t)stream));
 }
 
@@ -348,6 +389,24 @@ int paged_decode_attention_dcp(const void* q, const void* k_cache, const void* v
                        nullptr, 0, cp_world_size, cp_rank, cp_interleave, num_seqs, q_len,
                        num_q_heads, num_kv_heads, head_dim, block_size, total_blocks, scale,
                        dtype, 0, workspace, workspace_bytes, out, lse, stream);
+}
+
+int paged_decode_attention_append(const int32_t* req_indices, const int64_t* positions,
+                                  int64_t num_tokens, int64_t max_num_tokens,
+                                  int64_t* slot_mapping, const void* k_new, const void* v_new,
+                                  const void* q, void* k_cache, void* v_cache,
+                                  const int32_t* block_table, int32_t table_stride,
+                                  int32_t walk_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int64_t total_blocks,
+                                  float scale, kvs_dtype dtype, uint32_t flags, void* workspace,
+                                  size_t workspace_bytes, float* out, void* stream) {
+  const AppendArgs app{req_indices, positions, num_tokens, max_num_tokens,
+                       slot_mapping, k_new, v_new};
+  return decode_common(q, k_cache, v_cache, block_table, table_stride, walk_blocks, seq_lens,
+                       nullptr, 0, 1, 0, 1, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim,
+                       block_size, total_blocks, scale, dtype, flags, workspace,
+                       workspace_bytes, out, nullptr, stream, &app);
 }
 
 int decode_lse_merge(const float* outs, const float* lses, int32_t world, int64_t rows,

@@ -61,6 +61,17 @@ struct DecodeParams {
   int32_t slices;      // set by the launcher: slices the batch's tiles are cut into
   int32_t min_tiles;   // never cut a slice shorter than this many 16-token tiles
   int32_t start_tiles;  // units a request start counts for when cutting slices
+  // The step's new tokens, written by pass 1 itself (paged_decode_attention
+  // with an append): as kv_slot_mapping_cache_write with table_rows =
+  // num_seqs. app_max_tokens = 0: no append.
+  const int32_t* app_req;
+  const int64_t* app_pos;
+  const void* app_k;
+  const void* app_v;
+  void* app_k_cache;
+  void* app_v_cache;
+  int64_t* app_slots;
+  int64_t app_tokens, app_max_tokens;
   float scale_log2;          // softmax scale times log2(e)
   uint32_t flags;
   int is_bf16;

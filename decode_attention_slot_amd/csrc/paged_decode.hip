@@ -68,6 +68,7 @@
 #include <atomic>
 
 #include "kvslot_internal.h"
+#include "slot_formula.h"
 
 namespace kvs {
 namespace {
@@ -81,9 +82,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kFlagWalkTable = 0x1u;
 // Never set by the host. Testing it keeps the table-walk loads alive.
 constexpr uint32_t kFlagSink = 0x80000000u;
-// pass-1 modes: context walk, fixed-shape table walk, and the general walk
-// (sliding window, tail-trimmed table, context-parallel share)
-constexpr int kContextWalk = 0, kTableWalk = 1, kGeneral = 2;
+// pass-1 modes: context walk, fixed-shape table walk, the general walk
+// (sliding window, tail-trimmed table, context-parallel share), and the
+// context walk that first writes the step's new tokens (append)
+constexpr int kContextWalk = 0, kTableWalk = 1, kGeneral = 2, kAppend = 3;
 constexpr int kTile = 16;
 constexpr int kStage = 256;  // block ids staged in LDS at a time
 constexpr int kDepth = 2;    // tiles in flight per wave
@@ -194,6 +196,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int NTHR = NW * 64;
   constexpr bool TW = MODE == kTableWalk;
   constexpr bool GEN = MODE == kGeneral;
+  constexpr bool APP = MODE == kAppend;
   constexpr uint32_t kNegZero = BF16 ? 0x80008000u : 0x80000000u;
   static_assert(NP >= 1 && NVW >= 2, "unsupported head_dim");
   struct TileBuf {
@@ -204,6 +207,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   extern __shared__ int s_pref[];  // [num_seqs + 1]: first tile of each request
   __shared__ int s_blk[kStage];
   __shared__ int s_wave[NW], s_wave_n[NW];
+  // append: the step tokens whose rows this slice reads, and their slots
+  __shared__ int s_app_t[APP ? NW * 64 : 1];
+  __shared__ int64_t s_app_s[APP ? NW * 64 : 1];
+  __shared__ int s_app_n;
   // request holding this slice's first unit (context), first padding tile,
   // and the context tiles of the requests before the latter
   __shared__ int s_first[3];
@@ -238,6 +245,17 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // tiles (the cost of starting a segment), so a slice that starts a
   // request carries that many fewer tiles. s_pref holds these units.
   const int X = p.start_tiles;
+  // append: this thread's step token and its slot, looked up before the
+  // scan below so that the table read overlaps it
+  int app_r = -1;
+  int64_t app_p = -1, app_s = -1;
+  if constexpr (APP) {
+    if ((int64_t)threadIdx.x < p.app_tokens) {
+      app_r = p.app_req[threadIdx.x];
+      app_p = p.app_pos[threadIdx.x];
+      app_s = token_slot(app_r, app_p, p.block_table, B, p.table_stride, bs, bs_shift);
+    }
+  }
   for (int rr = threadIdx.x; rr < B; rr += NTHR)
     s_pref[rr] = request_span<GEN>(p, rr, p.seq_lens[rr], walk_tok, bs, Sq).n;
   if (threadIdx.x == 0) {
@@ -298,7 +316,62 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     run_n += n;
   }
   if (threadIdx.x == 0) s_pref[B] = total;
+  if constexpr (APP) {
+    if (threadIdx.x == 0) s_app_n = 0;
+  }
   __syncthreads();
+
+  // ---- append: write the step's new K/V rows before any tile is read ------
+  // A row lies in one tile of its request; the slice holding that tile (the
+  // cut above) writes it, each wave its own KV head's part, so the wave that
+  // later loads those bytes is the one that stored them, and it waits for
+  // its stores before going on. Rows of positions no slice reads (past the
+  // walked tiles) and the slot mapping itself are written by workgroup 0.
+  if constexpr (APP) {
+    constexpr int PR = D * ES / 16;  // 16-byte pieces of one head's row
+    const int64_t T = p.app_tokens;
+    const int64_t total_slots = p.total_blocks << bs_shift;
+    const bool first_wg = blockIdx.x == 0;
+    int owner = -1;  // slice that reads this token's tile
+    if (app_r >= 0 && app_r < B && app_p >= 0) {
+      const int wu = s_pref[app_r + 1] - s_pref[app_r];
+      const int64_t k = app_p >> 4;
+      if (wu > 0 && k < wu - X) owner = (s_pref[app_r] + X + (int)k) / Q;
+    }
+    const bool own = owner == slice;
+    const int64_t s = app_s;
+    const bool inb = s >= 0 && s < total_slots;
+    if (first_wg && (int64_t)threadIdx.x < p.app_max_tokens)
+      p.app_slots[threadIdx.x] = (int64_t)threadIdx.x < T ? s : -1;
+    const u32x4* kn = (const u32x4*)p.app_k;
+    const u32x4* vn = (const u32x4*)p.app_v;
+    u32x4* kc = (u32x4*)p.app_k_cache;
+    u32x4* vc = (u32x4*)p.app_v_cache;
+    if (first_wg && (int64_t)threadIdx.x < T && inb && owner < 0) {
+      for (int q4 = 0; q4 < Hkv * PR; ++q4) {
+        kc[s * Hkv * PR + q4] = kn[(int64_t)threadIdx.x * Hkv * PR + q4];
+        vc[s * Hkv * PR + q4] = vn[(int64_t)threadIdx.x * Hkv * PR + q4];
+      }
+    }
+    if (own && inb) {
+      const int i = atomicAdd(&s_app_n, 1);
+      s_app_t[i] = (int)threadIdx.x;
+      s_app_s[i] = s;
+    }
+    __syncthreads();
+    const int n_own = s_app_n;
+    for (int k0 = 0; k0 < n_own; k0 += 64 / PR) {
+      const int kk = k0 + lane / PR;
+      if (kk < n_own) {
+        const int pc = lane % PR;
+        const int64_t src = ((int64_t)s_app_t[kk] * Hkv + g) * PR + pc;
+        const int64_t dst = (s_app_s[kk] * Hkv + g) * PR + pc;
+        kc[dst] = kn[src];
+        vc[dst] = vn[src];
+      }
+    }
+    if (n_own > 0) __builtin_amdgcn_s_waitcnt(0);  // this wave's stores land before its loads
+  }
 
   uint32_t sink = 0;
   const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
@@ -875,6 +948,15 @@ hipError_t launch_merge(const DecodeParams& p, int kc, hipStream_t stream) {
   return launch_merge_shape<D, KMAX, NG>(p, units * ((kc + KMAX - 1) / KMAX), resw, stream);
 }
 
+// The split-K merge for the row count of these parameters.
+template <int D>
+hipError_t launch_merge_for(const DecodeParams& p, hipStream_t stream) {
+  const int nrows = p.num_q_heads / p.num_kv_heads * p.q_len;
+  const int kc = (nrows * (D / 4) + 63) / 64;
+  if (kc <= 4) return launch_merge<D, merge_groups(4)>(p, kc, stream);
+  return launch_merge<D, merge_groups(8)>(p, kc, stream);
+}
+
 // Compute units of the current device, queried once per device.
 hipError_t device_cus(int* out) {
   static std::atomic<int> cache[kMaxDevices];
@@ -908,6 +990,23 @@ hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t strea
   if (p.slices > p.max_slices) p.slices = p.max_slices;
   const dim3 grid((unsigned)p.slices * (unsigned)HG);
   const size_t lds = decode_lds_bytes(p.num_seqs);
+  if (p.app_max_tokens > 0) {
+    // The step's rows are written by pass 1 when all its tokens fit one
+    // workgroup's threads and the walk is the context walk; otherwise by
+    // the fused slot-map + write kernel first.
+    if (!(p.flags & kFlagWalkTable) && p.window == 0 && !p.kv_pos_offset && p.cp_world == 1 &&
+        p.app_max_tokens <= NW * 64) {
+      paged_decode_kernel<BF16, D, NW, kAppend><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_merge_for<D>(p, stream);
+    }
+    e = launch_slot_write(p.app_req, p.app_pos, p.app_tokens, p.app_max_tokens, p.block_table,
+                          p.num_seqs, p.table_stride, p.block_size, p.app_slots, p.app_k,
+                          p.app_v, p.app_k_cache, p.app_v_cache, p.total_blocks * p.block_size,
+                          p.num_kv_heads * p.head_dim * (p.is_bf16 ? 2 : 4), stream);
+    if (e != hipSuccess) return e;
+  }
   if (p.flags & kFlagWalkTable)
     paged_decode_kernel<BF16, D, NW, kTableWalk><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
   else if (p.window > 0 || p.kv_pos_offset || p.cp_world > 1)
@@ -916,10 +1015,7 @@ hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t strea
     paged_decode_kernel<BF16, D, NW, kContextWalk><<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nrows = p.num_q_heads / p.num_kv_heads * p.q_len;
-  const int kc = (nrows * (D / 4) + 63) / 64;
-  if (kc <= 4) return launch_merge<D, merge_groups(4)>(p, kc, stream);
-  return launch_merge<D, merge_groups(8)>(p, kc, stream);
+  return launch_merge_for<D>(p, stream);
 }
 
 template <bool BF16, int D>

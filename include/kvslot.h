@@ -275,6 +275,41 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
                            size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * paged_decode_attention_append - the step's cache write and the decode
+ * attention in one call: the result is that of kv_slot_mapping_cache_write
+ * (with table_rows = num_seqs: the step's tokens index the batch's rows)
+ * followed by paged_decode_attention with the same arguments, for the
+ * callers that hold both ([BKV] "Slot Mapping Computation" and "Slot ID -1"
+ * for the write, the passages cited above for the attention).
+ *
+ * Step tokens, as in kv_slot_mapping_cache_write: req_indices, positions
+ * [num_tokens]; slot_mapping [max_num_tokens] (written, -1 tail); k_new,
+ * v_new [num_tokens][num_kv_heads][head_dim] of dtype. Attention arguments
+ * as in paged_decode_attention; k_cache and v_cache are written and read.
+ *
+ * When max_num_tokens <= 64 * (the KV heads one workgroup holds: 8 when
+ * num_kv_heads is a multiple of 8) and flags is 0, the decode launch writes
+ * the rows itself: each row is written by the workgroup that reads it, so
+ * one launch fewer. This needs what a decode step guarantees: a written
+ * slot lies in a block that no other request of the batch reads in this
+ * call (the request's own tail block); otherwise the result is
+ * unspecified. Larger steps, and the fixed-shape walk, take the fused
+ * slot-map + write launch first; the result is the same.
+ * Errors: those of both calls.
+ */
+int paged_decode_attention_append(const int32_t* req_indices, const int64_t* positions,
+                                  int64_t num_tokens, int64_t max_num_tokens,
+                                  int64_t* slot_mapping, const void* k_new, const void* v_new,
+                                  const void* q, void* k_cache, void* v_cache,
+                                  const int32_t* block_table, int32_t table_stride,
+                                  int32_t walk_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int64_t total_blocks,
+                                  float scale, kvs_dtype dtype, uint32_t flags, void* workspace,
+                                  size_t workspace_bytes, float* out, void* stream);
+
+
+/*
  * paged_decode_attention_swa - decode attention for a sliding-window layer
  * over a tail-trimmed block table ([KVC] "Attention Type": a sliding-window
  * layer keeps only the recent tokens within its window; [CLB] "Block-table

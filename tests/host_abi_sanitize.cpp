@@ -260,6 +260,26 @@ void check_gpu_entry_argument_checks() {
                                      at(0x100000), SIZE_MAX, f16,
                                      static_cast<float*>(at(0x100002)), nullptr) == KVS_EINVAL,
           "lse not 4-byte aligned");
+  require(paged_decode_attention_append(i16, l16, 8, 8, l16, at(0x100008), at(0x100000),
+                                        at(0x100000), at(0x100000), at(0x100000), i16, 80, 80,
+                                        i16, 12, 1, 32, 8, 128, 64, 1024, 0.088f, KVS_BF16, 0,
+                                        at(0x100000), SIZE_MAX, f16, nullptr) == KVS_EINVAL,
+          "append: new K rows not 16-byte aligned");
+  require(paged_decode_attention_append(i16, l16, 8, 8, nullptr, at(0x100000), at(0x100000),
+                                        at(0x100000), at(0x100000), at(0x100000), i16, 80, 80,
+                                        i16, 12, 1, 32, 8, 128, 64, 1024, 0.088f, KVS_BF16, 0,
+                                        at(0x100000), SIZE_MAX, f16, nullptr) == KVS_EINVAL,
+          "append: no slot buffer");
+  require(paged_decode_attention_append(i16, l16, 9, 8, l16, at(0x100000), at(0x100000),
+                                        at(0x100000), at(0x100000), at(0x100000), i16, 80, 80,
+                                        i16, 12, 1, 32, 8, 128, 64, 1024, 0.088f, KVS_BF16, 0,
+                                        at(0x100000), SIZE_MAX, f16, nullptr) == KVS_EINVAL,
+          "append: more tokens than slots");
+  require(paged_decode_attention_append(nullptr, nullptr, 0, 0, nullptr, nullptr, nullptr,
+                                        nullptr, nullptr, nullptr, nullptr, 80, 80, nullptr, 12,
+                                        1, 32, 8, 96, 64, 1024, 0.088f, KVS_BF16, 0, nullptr, 0,
+                                        nullptr, nullptr) == KVS_EUNSUPPORTED,
+          "append: head_dim 96");
   require(decode_lse_merge(static_cast<float*>(at(0x100008)), f16, 2, 16, 128, f16, f16,
                            nullptr) == KVS_EINVAL,
           "merge inputs not 16-byte aligned");

@@ -949,6 +949,103 @@ def test_step_replays_from_a_hip_graph(cuda):
         assert torch.equal(eager.view(torch.int32), want.view(torch.int32)), i
 
 
+# ---------------------------------------------------------------------------
+# paged_decode_attention_append: the step's write inside the decode launch
+# ---------------------------------------------------------------------------
+def append_vs_two_launch(kc, vc, q, bt, sl, scale, req, pos, k_new, v_new, walk=None, flags=0,
+                         max_tokens=None):
+    """The append call against kv_slot_mapping_cache_write followed by
+    paged_decode_attention, on copies of the same caches: slots, both cache
+    images and the output must be bitwise equal."""
+    ka, va, kb, vb = kc.clone(), vc.clone(), kc.clone(), vc.clone()
+    sa = K.kv_slot_mapping_cache_write(req, pos, bt, k_new, v_new, ka, va,
+                                       max_num_tokens=max_tokens)
+    oa = K.paged_decode_attention(q, ka, va, bt, sl, scale, walk_blocks=walk, flags=flags)
+    sb, ob = K.paged_decode_attention_append(req, pos, k_new, v_new, q, kb, vb, bt, sl, scale,
+                                             walk_blocks=walk, flags=flags,
+                                             max_num_tokens=max_tokens)
+    torch.cuda.synchronize()
+    assert torch.equal(sa, sb)
+    assert torch.equal(host_bits_t(ka), host_bits_t(kb))
+    assert torch.equal(host_bits_t(va), host_bits_t(vb))
+    assert torch.equal(oa.view(torch.int32), ob.view(torch.int32))
+    return sb, ob
+
+
+def host_bits_t(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
+def test_append_step_equals_two_launches(cuda, index):
+    """Every workload's step through the append call: the large batch's 264
+    step tokens take the in-kernel write, the ragged step's 8448 the fused
+    write launch; the result is the two-launch step's, bitwise, and the
+    oracle's."""
+    w = W.make_workload(index)
+    s = dev.build(w, cuda, threads=16)
+    req, pos = s.step_req, s.step_pos
+    k_new = torch.cat([s.chunk_k, s.dec_k]).contiguous()
+    v_new = torch.cat([s.chunk_v, s.dec_v]).contiguous()
+    slots, out = append_vs_two_launch(s.k_cache, s.v_cache, s.q, s.block_table, s.seq_lens,
+                                      w.scale, req, pos, k_new, v_new)
+    if index in (0, 1):
+        ref = OracleStep(w, s.host_table)
+        assert np.array_equal(slots.cpu().numpy(), ref.write_step())
+        assert max_err(out, ref.attention(w.q())) <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_append_random_vs_two_launches(cuda, seed):
+    """Seeded random batches whose last q_len positions are the step's new
+    tokens (rows replaced by fresh draws, cache slots reset to the canary),
+    plus padding tokens, tokens past the walked tiles and a -1 tail."""
+    dtype, d, bs, hkv, g, sq, lens, trim, table_walk, _, rng = random_case_params(30_000 + seed)
+    c = small_case(cuda, seed, lens, bs, hkv, g, sq, d, dtype)
+    width = c["table"].shape[1]
+    walk = max(1, -(-max(lens) // bs) - int(rng.integers(0, 2))) if trim else width
+    req, pos = [], []
+    for r, L in enumerate(lens):
+        for j in range(min(sq, L)):
+            req.append(r)
+            pos.append(L - min(sq, L) + j)
+    for _ in range(int(rng.integers(0, 3))):  # padding tokens
+        req.append(-1)
+        pos.append(0)
+    T = len(req)
+    req_t = torch.tensor(req, dtype=torch.int32, device=cuda)
+    pos_t = torch.tensor(pos, dtype=torch.int64, device=cuda)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k_new = torch.randn((T, hkv, d), generator=torch.Generator().manual_seed(seed)).to(tdt).to(cuda)
+    v_new = torch.randn((T, hkv, d), generator=torch.Generator().manual_seed(seed + 1)).to(tdt).to(cuda)
+    append_vs_two_launch(c["d_kc"], c["d_vc"], c["d_q"], c["d_bt"], c["d_sl"], c["w"].scale,
+                         req_t, pos_t, k_new, v_new, walk=walk,
+                         flags=K.KVS_WALK_TABLE if table_walk else 0,
+                         max_tokens=T + int(rng.integers(0, 5)))
+
+
+@pytest.mark.parametrize("extra", [0, 1])
+def test_append_at_the_in_kernel_limit(cuda, extra):
+    """512 step tokens (the in-kernel write's limit at 8 KV heads) and 513
+    (the fused write launch), including tokens past the walked tiles."""
+    lens = [40 + 7 * i for i in range(64)]
+    c = small_case(cuda, 5, lens, 16, 8, 1, 1, 64, "bf16")
+    rng = np.random.default_rng(extra)
+    req = rng.integers(0, 64, 512 + extra).astype(np.int32)
+    pos = np.array([rng.integers(0, lens[r] + 20) for r in req], np.int64)
+    # one token per slot: keep the first of any repeated (request, position)
+    _, first = np.unique(req.astype(np.int64) * 4096 + pos, return_index=True)
+    keep = np.zeros(len(req), bool)
+    keep[first] = True
+    req = np.where(keep, req, -1).astype(np.int32)
+    T = len(req)
+    k_new = torch.randn((T, 8, 64)).to(torch.bfloat16).to(cuda)
+    v_new = torch.randn((T, 8, 64)).to(torch.bfloat16).to(cuda)
+    append_vs_two_launch(c["d_kc"], c["d_vc"], c["d_q"], c["d_bt"], c["d_sl"], c["w"].scale,
+                         torch.from_numpy(req).to(cuda), torch.from_numpy(pos).to(cuda),
+                         k_new, v_new, walk=3)
+
+
 def test_fused_slot_write_empty(cuda):
     kc = torch.zeros((2, 16, 1, 64), dtype=torch.bfloat16, device=cuda)
     e32 = torch.zeros(0, dtype=torch.int32, device=cuda)
