@@ -245,18 +245,29 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // tiles (the cost of starting a segment), so a slice that starts a
   // request carries that many fewer tiles. s_pref holds these units.
   const int X = p.start_tiles;
+  // The first request of this thread's share is loaded here, before the
+  // append's token loads, so that waiting for it does not wait for them.
+  const int len0 = (int)threadIdx.x < B ? p.seq_lens[threadIdx.x] : 0;
   // append: this thread's step token and its slot, looked up before the
   // scan below so that the table read overlaps it
-  int app_r = -1;
-  int64_t app_p = -1, app_s = -1;
+  // (the slot formula of slot_formula.h, with its table read issued here and
+  // its value first used after the scan)
+  int app_r = -1, app_blk = 0;
+  int64_t app_p = -1, app_lb = -1;
   if constexpr (APP) {
     if ((int64_t)threadIdx.x < p.app_tokens) {
       app_r = p.app_req[threadIdx.x];
       app_p = p.app_pos[threadIdx.x];
-      app_s = token_slot(app_r, app_p, p.block_table, B, p.table_stride, bs, bs_shift);
     }
   }
-  for (int rr = threadIdx.x; rr < B; rr += NTHR)
+  if ((int)threadIdx.x < B) s_pref[threadIdx.x] = request_span<GEN>(p, threadIdx.x, len0, walk_tok, bs, Sq).n;
+  if constexpr (APP) {
+    if (app_r >= 0 && app_r < B && app_p >= 0 && (app_p >> bs_shift) < p.table_stride) {
+      app_lb = app_p >> bs_shift;
+      app_blk = p.block_table[(int64_t)app_r * p.table_stride + app_lb];
+    }
+  }
+  for (int rr = threadIdx.x + NTHR; rr < B; rr += NTHR)
     s_pref[rr] = request_span<GEN>(p, rr, p.seq_lens[rr], walk_tok, bs, Sq).n;
   if (threadIdx.x == 0) {
     s_first[0] = 0;
@@ -339,7 +350,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       if (wu > 0 && k < wu - X) owner = (s_pref[app_r] + X + (int)k) / Q;
     }
     const bool own = owner == slice;
-    const int64_t s = app_s;
+    const int64_t s =
+        app_lb >= 0 && app_blk > 0 ? (int64_t)app_blk * bs + (app_p - (app_lb << bs_shift)) : -1;
     const bool inb = s >= 0 && s < total_slots;
     if (first_wg && (int64_t)threadIdx.x < p.app_max_tokens)
       p.app_slots[threadIdx.x] = (int64_t)threadIdx.x < T ? s : -1;
