@@ -287,10 +287,10 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
  * v_new [num_tokens][num_kv_heads][head_dim] of dtype. Attention arguments
  * as in paged_decode_attention; k_cache and v_cache are written and read.
  *
- * When max_num_tokens <= 64 * (the KV heads one workgroup holds: 8 when
- * num_kv_heads is a multiple of 8) and flags is 0, the decode launch writes
- * the rows itself: each row is written by the workgroup that reads it, so
- * one launch fewer. This needs what a decode step guarantees: a written
+ * When max_num_tokens <= 64 * NW, NW the largest of 8, 4, 2 and 1 that
+ * divides num_kv_heads (the KV heads one workgroup holds: 512 tokens at 8
+ * KV heads), and flags is 0, the decode launch writes the rows itself: each
+ * row is written by the workgroup that reads it, so one launch fewer. This needs what a decode step guarantees: a written
  * slot lies in a block that no other request of the batch reads in this
  * call (the request's own tail block); otherwise the result is
  * unspecified. Larger steps, and the fixed-shape walk, take the fused
