@@ -32,8 +32,12 @@ cache_write_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_
     const int64_t dst = s * pieces_per_row + piece;
     const u32x4 kv = __builtin_nontemporal_load(&k_new[i]);
     const u32x4 vv = __builtin_nontemporal_load(&v_new[i]);
-    k_cache[dst] = kv;
-    v_cache[dst] = vv;
+    // Streaming stores: the rows go on to memory now rather than staying
+    // dirty in cache, where their later eviction slowed the next launch's
+    // reads (a decode pass over 2.2 GB ran about 20 us longer after an
+    // 8448-row write with plain stores, within 1 us with these).
+    __builtin_nontemporal_store(kv, &k_cache[dst]);
+    __builtin_nontemporal_store(vv, &v_cache[dst]);
   }
 }
 
