@@ -931,9 +931,11 @@ hipError_t resident_workgroups(int* out) {
 
 // The merge of units made of `kc` columns of 64 float4s. One float4 per lane
 // (pieces of one column) when all those pieces fit into one round of
-// resident workgroups: the partials of a long context are then read by kc
-// times as many compute units. Otherwise every lane takes 32 / NG float4s
-// (one piece per unit), which keeps more loads in flight per wave. Tiles of
+// resident workgroups, or when requests average more than NG partials: the
+// partials of a long context are then read by kc times as many compute
+// units, with eight partials in flight per wave. Otherwise every lane takes
+// 32 / NG float4s (one piece per unit), which keeps more loads in flight
+// per wave. Tiles of
 // T pieces, T the smallest count that fits one round (at most NG).
 template <int D, int KCW, int NG>
 hipError_t launch_merge_shape(const DecodeParams& p, int64_t n, int resident, hipStream_t stream) {
@@ -954,7 +956,12 @@ hipError_t launch_merge(const DecodeParams& p, int kc, hipStream_t stream) {
                              NG * 64, 0, cache1, &res1);
   if (e != hipSuccess) return e;
   const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads;
-  if (units * kc <= res1) return launch_merge_shape<D, 1, NG>(p, units * kc, res1, stream);
+  // One float4 per lane also when requests average more than NG partials:
+  // at 32 / NG float4s per lane a wave of the grouped path keeps only
+  // 8 / (32 / NG) partials in flight, and a long unit then waits on
+  // several rounds of loads one after another.
+  if (units * kc <= res1 || (int64_t)p.slices > (int64_t)NG * p.num_seqs)
+    return launch_merge_shape<D, 1, NG>(p, units * kc, res1, stream);
   e = resident_of(reinterpret_cast<const void*>(&paged_decode_combine_kernel<D, NG, KMAX>),
                   NG * 64, 0, cachew, &resw);
   if (e != hipSuccess) return e;
