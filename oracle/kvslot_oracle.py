@@ -111,14 +111,16 @@ def reshape_and_cache(k_new, v_new, slot_mapping, k_cache, v_cache):
     v_rows = v_cache.reshape(n_slots, *v_cache.shape[2:])
     assert np.shares_memory(k_rows, k_cache) and np.shares_memory(v_rows, v_cache)
     T = k_new.shape[0]
-    live = [(t, int(slots[t])) for t in range(T) if 0 <= slots[t] < n_slots]
-    targets = [s for _, s in live]
-    if len(set(targets)) != len(targets):
+    slots = slots[:T]
+    # tokens whose slot lies inside the cache, and those slots
+    live = np.nonzero((slots >= 0) & (slots < n_slots))[0]
+    targets = slots[live]
+    if np.unique(targets).size != targets.size:
         raise OracleError("duplicate_slot", "two tokens map to one slot")
-    for t, s in live:
-        k_rows[s] = k_new[t]
-        v_rows[s] = v_new[t]
-    return len(live)
+    # one row copy per live token (targets are distinct, so order is immaterial)
+    k_rows[targets] = k_new[live]
+    v_rows[targets] = v_new[live]
+    return int(live.size)
 
 
 # ---------------------------------------------------------------------------
