@@ -203,11 +203,14 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, walk_bloc
             if not seen.any():
                 continue
             Kj, Vj = K[seen], V[seen]
-            for h in range(Hq):
-                g = h // G
-                s = scale * (Kj[:, g, :] @ q64[r, j, h])
-                p = np.exp(s - s.max())
-                out[r, j, h] = (p @ Vj[:, g, :]) / p.sum()
+            for g in range(Hkv):
+                # keys and values of KV head g, read by q heads g*G .. g*G + G - 1
+                Kg = np.ascontiguousarray(Kj[:, g, :])
+                Vg = np.ascontiguousarray(Vj[:, g, :])
+                for h in range(g * G, (g + 1) * G):
+                    s = scale * (Kg @ q64[r, j, h])
+                    p = np.exp(s - s.max())
+                    out[r, j, h] = (p @ Vg) / p.sum()
     return out
 
 
