@@ -8,23 +8,30 @@ itself when they qualify); --fused-write runs kv_slot_mapping_cache_write
 then paged_decode_attention, --separate-write kv_slot_mapping and
 kv_cache_write then paged_decode_attention. Inputs are seeded and synthetic
 and already resident in HBM when the timed region starts (the prior context
-is prefilled through the library beforehand, untimed).
-HIP events on the launch stream bracket the attention call (with the append,
-the call that also writes the step's rows) of every eighth timed step (an
-event is a marker the GPU processes in line, so marking every step would
-slow the steps being timed). The events are created with
-hipEventDisableSystemFence: a default event's record also writes back and
-invalidates the caches at system scope, which adds to the timed work. The
-slot mapping and cache write kernels and their one-launch fusion are timed
-after the steps, each in a run of back-to-back launches.
+is prefilled through the library beforehand, untimed). The default workload
+is the largest single-GPU one: 256 decode requests (+8 padded rows) over a
+kernel block size of 16, GQA 8, about 4.5 GB of KV per step.
 
-The step rotates over several identical copies of the KV cache so that the
-bytes a step reads come from HBM, not from the last step's L2 / MALL lines.
+Timing: the K timed steps run back to back, bracketed by synchronisations,
+and give the wall time per step. After them, the step's attention call (with
+the append, the call that also writes the step's rows) runs --calls more
+times (100 by default, never fewer than 50, whatever --steps says), each call
+bracketed by its own pair of HIP events; the median of those durations is the
+roofline figure. The events are created with hipEventDisableSystemFence: a
+default event's record also writes back and invalidates the caches at system
+scope, which adds to the timed work. The slot mapping and cache write kernels
+and their one-launch fusion are timed after that, each in a run of
+back-to-back launches.
+
+The step rotates over several identical copies of the KV cache when one
+step's bytes are below 1 GiB, so that the bytes a step reads come from HBM,
+not from the last step's L2 / MALL lines.
 
 Prints one JSON line: whole-step throughput (algorithmic bytes of every
 kernel / wall time per step), decode and slot-mapping tokens/s, a roofline
-entry for the attention kernel (algorithmic bytes / its event-timed average
-duration against 8 TB/s) and the CPU oracle timed on a bounded sample.
+entry for the attention call (algorithmic bytes / its event-timed median
+duration against 8 TB/s) and the CPU oracle timed on a bounded sample, on
+one host core and on all the host cores the process may use.
 """
 
 from __future__ import annotations
@@ -44,8 +51,9 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
-EVENT_EVERY = 8  # timed steps whose attention call is bracketed by HIP events
-SLOT_SWEEP_TOKENS = 1 << 20  # slot mapping measured at this many tokens as well
+MIN_CALLS = 50  # event-timed attention calls, at least
+SLOT_SWEEP_TOKENS = 1 << 22  # slot mapping measured at this many tokens per launch as well
+SLOT_SWEEP_SETS = 11  # distinct token sets rotated (11 x 100 MB: past the 256 MB MALL)
 WORKLOADS = {
     "block_config_bf16": 1,
     "ctx_bucketing": 2,
@@ -222,7 +230,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="block_config_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="large_batch_block_split", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--walk", default="context", choices=["context", "bucket", "full"],
                     help="context: read only covering blocks; bucket/full: fixed-shape walk of the "
@@ -230,7 +238,10 @@ def main(argv=None) -> int:
     ap.add_argument("--max-ctx", type=int, default=None,
                     help="bucketing workload: clip the drawn context lengths and pin the largest")
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = auto)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calls", type=int, default=100,
+                    help="event-timed attention calls after the steps (median; at least 50)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle time per leg (one core, then every core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window layer: attend over a tail-trimmed table with this window "
@@ -426,21 +437,26 @@ def main(argv=None) -> int:
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: whole steps. The host stays ahead of the GPU, so the wall
-    # time per step is GPU time. Events bracket the attention call of every
-    # EVENT_EVERY-th step (each event is a marker on the stream that costs
-    # the GPU a few microseconds, so marking every step would slow the very
-    # steps being timed); their average is the attention call's time.
-    marked = [i for i in range(args.steps) if i % EVENT_EVERY == 0]
-    events = {i: [HipEvent(), HipEvent()] for i in marked}
+    # Timed region: whole steps, back to back. The host stays ahead of the
+    # GPU, so the wall time per step is GPU time.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events.get(i))
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_attn = np.mean([e[0].elapsed_ms(e[1]) for e in events.values()]) * 1e-3
     ms_per_step = wall / args.steps * 1e3
+
+    # The step's attention call alone, each call bracketed by its own events
+    # (a marker the GPU processes in line): median and mean of the durations.
+    n_calls = max(args.calls, MIN_CALLS)
+    events = [(HipEvent(), HipEvent()) for _ in range(n_calls)]
+    for i, ev in enumerate(events):
+        step(args.steps + i, ev)
+    torch.cuda.synchronize()
+    durations = np.array([e0.elapsed_ms(e1) for e0, e1 in events]) * 1e-3
+    t_attn = float(np.median(durations))
+    t_attn_mean = float(np.mean(durations))
 
     # Slot mapping and cache write on their own: back-to-back launches
     # between two events give each kernel's time in a busy stream.
@@ -482,26 +498,39 @@ def main(argv=None) -> int:
         lse_merge = {"world": world, "rows": rows_m, "us": round(t_m * 1e6, 3),
                      "algorithmic_bytes": m_bytes, "gbps": round(m_bytes / t_m / 1e9, 2)}
 
-    # Slot mapping at 2^20 tokens (the step's few tokens only measure the
-    # launch): tokens of random real requests at random positions below
-    # their context lengths, mapped through this workload's table.
+    # Slot mapping at 2^22 tokens per launch (the step's few tokens only
+    # measure the launch): tokens of random real requests at random positions
+    # below their context lengths, mapped through this workload's table. The
+    # launches rotate over SLOT_SWEEP_SETS distinct token sets (about 1.1 GB of
+    # token and slot arrays), so their bytes come from HBM and not from the
+    # 256 MB last-level cache; only the table (a few hundred KB) stays cached.
     sweep = None
     if w.num_reqs:
-        rng = np.random.default_rng(w.seed + 7)
         nt = SLOT_SWEEP_TOKENS
-        req = rng.integers(0, w.num_reqs, nt).astype(np.int32)
-        lens = np.maximum(w.seq_lens[: w.num_reqs].astype(np.int64), 1)
-        pos = (rng.random(nt) * lens[req]).astype(np.int64)
-        d_req = torch.from_numpy(req).to(cuda)
-        d_pos = torch.from_numpy(pos).to(cuda)
-        d_slots = torch.empty(nt, dtype=torch.int64, device=cuda)
-        big = (d_req.data_ptr(), d_pos.data_ptr(), nt, nt, s.block_table.data_ptr(), int(rows),
-               int(stride), w.block_size, d_slots.data_ptr(), sp)
-        t_big = back_to_back(f_slot, [big], 50)
-        sweep = {"tokens": nt, "us": round(t_big * 1e6, 3),
+        gen = torch.Generator(device=cuda)
+        gen.manual_seed(w.seed + 7)
+        lens = torch.from_numpy(np.maximum(w.seq_lens[: w.num_reqs].astype(np.int64), 1)).to(cuda)
+        sets = []
+        for _ in range(SLOT_SWEEP_SETS):
+            d_req = torch.randint(0, w.num_reqs, (nt,), generator=gen, device=cuda,
+                                  dtype=torch.int64)
+            d_pos = (torch.rand(nt, generator=gen, device=cuda, dtype=torch.float64)
+                     * lens[d_req]).to(torch.int64)
+            d_req = d_req.to(torch.int32)
+            d_slots = torch.empty(nt, dtype=torch.int64, device=cuda)
+            sets.append((d_req, d_pos, d_slots))
+        big = [(a.data_ptr(), b.data_ptr(), nt, nt, s.block_table.data_ptr(), int(rows),
+                int(stride), w.block_size, c.data_ptr(), sp) for a, b, c in sets]
+        t_big = back_to_back(f_slot, big, 5 * SLOT_SWEEP_SETS)
+        sweep = {"tokens": nt, "token_sets_rotated": SLOT_SWEEP_SETS,
+                 "distinct_bytes": slot_map_bytes(nt) * SLOT_SWEEP_SETS,
+                 "us": round(t_big * 1e6, 3),
                  "tokens_per_s": round(nt / t_big, 1),
                  "gbps": round(slot_map_bytes(nt) / t_big / 1e9, 2),
-                 "frac_of_peak": round(slot_map_bytes(nt) / t_big / 1e9 / HBM_PEAK_GBPS, 4)}
+                 "frac_of_peak": round(slot_map_bytes(nt) / t_big / 1e9 / HBM_PEAK_GBPS, 4),
+                 "note": "24 B per token counted; the table entries (4 of them) are mostly "
+                         "cache hits, the token and slot arrays stream from HBM"}
+        del sets
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -580,6 +609,11 @@ def main(argv=None) -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(call_gbps / HBM_PEAK_GBPS, 4),
+            "calls": n_calls,
+            "call_us_median": round(t_attn * 1e6, 3),
+            "call_us_mean": round(t_attn_mean * 1e6, 3),
+            "call_us_p10_p90": [round(float(np.percentile(durations, 10)) * 1e6, 3),
+                                round(float(np.percentile(durations, 90)) * 1e6, 3)],
             "traffic": measured_traffic(args.workload,
                                         f"window{args.window}" if args.window else
                                         (f"dcp{dcp[0]}" if dcp else
@@ -612,47 +646,101 @@ def measured_traffic(workload: str, walk: str):
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, table, walk_blocks, seconds, window=0):
+def host_cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """CPU threads this process may use: its affinity set, capped by
+    OMP_NUM_THREADS when that is set (the share of a host the GPU job has)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(n, 1)
+
+
+def cpu_baseline(w, table, walk_blocks, seconds, window=0, sample_reqs=16):
     """The oracle as it stands, on the host cores, over a bounded sample.
 
-    Untimed: the oracle builds its own caches (prefill + step writes). Timed:
-    the oracle's paged_decode_attention, one request at a time in a cycle
-    over the batch, until ``seconds`` have passed. Throughput is the
-    algorithmic attention bytes of the requests processed per second. BLAS
-    is pinned to one thread, so the oracle runs on one core.
+    Untimed: the oracle builds its own caches (prefill + step writes) for a
+    sample of the batch's requests (the first ``sample_reqs`` real ones).
+    Timed, twice: the oracle's paged_decode_attention, one request per call,
+    cycling over the sample until ``seconds`` have passed; first on one
+    thread, then on a pool of host_threads() threads, each call one request
+    (numpy's BLAS calls and large copies release the GIL). BLAS is pinned to
+    one thread per caller in both legs. Throughput is the algorithmic
+    attention bytes of the requests processed per second.
     """
+    from concurrent.futures import ThreadPoolExecutor
+
     from threadpoolctl import threadpool_limits
 
     from oracle.runner import OracleStep
 
+    real = [i for i in range(w.num_reqs) if w.seq_lens[i] > 0][:sample_reqs]
+    es = w.es
+    per_block = 2 * w.block_size * w.num_kv_heads * w.head_dim * es + 4
+    per_req_fixed = w.q_len * w.num_q_heads * w.head_dim * (es + 4) + 4
+
+    def req_bytes(rr):
+        L = int(w.seq_lens[rr])
+        vis = min(L, walk_blocks * w.block_size)
+        first = max(0, L - w.q_len - window + 1) // w.block_size if window else 0
+        return (-(-vis // w.block_size) - first) * per_block + per_req_fixed
+
     with threadpool_limits(limits=1):
-        ref = OracleStep(w, table, full_image=False)
+        ref = OracleStep(w, table, requests=real, full_image=False)
         ref.write_step()
         q = w.q()
-        es = w.es
-        per_block = 2 * w.block_size * w.num_kv_heads * w.head_dim * es + 4
-        per_req_fixed = w.q_len * w.num_q_heads * w.head_dim * (es + 4) + 4
-        done_bytes, n, r = 0, 0, 0
-        real = [i for i in range(w.num_reqs) if w.seq_lens[i] > 0]
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            rr = real[r % len(real)]
+
+        def one(rr):
             ref.attention(q, walk_blocks=walk_blocks, requests=[rr], window=window)
-            L = int(w.seq_lens[rr])
-            vis = min(L, walk_blocks * w.block_size)
-            first = max(0, L - w.q_len - window + 1) // w.block_size if window else 0
-            done_bytes += (-(-vis // w.block_size) - first) * per_block + per_req_fixed
-            n += 1
-            r += 1
-        el = time.perf_counter() - t0
+            return req_bytes(rr)
+
+        legs = {}
+        for threads in (1, host_threads()):
+            done_bytes, n, r = 0, 0, 0
+            t0 = time.perf_counter()
+            if threads == 1:
+                while time.perf_counter() - t0 < seconds:
+                    done_bytes += one(real[r % len(real)])
+                    n += 1
+                    r += 1
+            else:
+                with ThreadPoolExecutor(max_workers=threads) as pool:
+                    while time.perf_counter() - t0 < seconds:
+                        batch = [real[(r + i) % len(real)] for i in range(threads)]
+                        done_bytes += sum(pool.map(one, batch))
+                        n += threads
+                        r += threads
+            el = time.perf_counter() - t0
+            legs[threads] = (done_bytes / el / 1e9, n, el)
+    model = host_cpu_model()
+    nthr = max(legs)
+    gbps, n, el = legs[nthr]
+    g1, n1, el1 = legs[1]
     return {
-        "value": round(done_bytes / el / 1e9, 6),
+        "value": round(gbps, 6),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": nthr,
         "kind": "oracle",
-        "sample": f"oracle fp64 paged_decode_attention, {n} request-steps of this workload "
-                  f"(cycling over its {len(real)} requests) in {el:.1f} s, BLAS on 1 thread; "
-                  f"host {os.cpu_count()} logical CPUs",
+        "sample": f"oracle fp64 paged_decode_attention over {len(real)} requests of this "
+                  f"workload, one request per call, cycled: {n} calls in {el:.1f} s on {nthr} "
+                  f"threads (BLAS 1 thread each); host {model}, {os.cpu_count()} logical CPUs, "
+                  f"{len(os.sched_getaffinity(0))} in this process's affinity set",
+        "cpu_model": model,
+        "single_core": {"value": round(g1, 6), "unit": "GB/s", "cores": 1,
+                        "sample": f"{n1} calls in {el1:.1f} s on one thread"},
     }
 
 

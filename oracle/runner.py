@@ -9,6 +9,8 @@ no code with the HIP library.
 
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from . import kvslot_oracle as O
@@ -23,7 +25,7 @@ class OracleStep:
     as (lazily allocated) zeros and only the chosen rows' blocks are written.
     """
 
-    def __init__(self, w, table, requests=None, full_image=True):
+    def __init__(self, w, table, requests=None, full_image=True, threads=1):
         self.w = w
         self.table = np.asarray(table, dtype=np.int32)
         self.rows = list(range(w.num_reqs)) if requests is None else \
@@ -35,15 +37,19 @@ class OracleStep:
         else:
             self.k_cache, self.v_cache = np.zeros(shape, sd), np.zeros(shape, sd)
         self.step_parts = {}
-        for r in self.rows:
-            k, v = w.request_kv(r)
-            c = int(w.computed[r])
-            self.step_parts[r] = (k[c:], v[c:])
-            if c:
-                req = np.full(c, r, np.int32)
-                pos = np.arange(c, dtype=np.int64)
-                slots = O.compute_slot_mapping(req, pos, self.table, w.block_size)
-                O.reshape_and_cache(k[:c], v[:c], slots, self.k_cache, self.v_cache)
+        # the generators' draws of each request, ``threads`` at a time (each
+        # request has its own random stream), then the oracle's own slot
+        # mapping and cache write of its prior context, request by request
+        with ThreadPoolExecutor(max_workers=max(1, threads)) as pool:
+            draws = pool.map(w.request_kv, self.rows)
+            for r, (k, v) in zip(self.rows, draws):
+                c = int(w.computed[r])
+                self.step_parts[r] = (k[c:], v[c:])
+                if c:
+                    req = np.full(c, r, np.int32)
+                    pos = np.arange(c, dtype=np.int64)
+                    slots = O.compute_slot_mapping(req, pos, self.table, w.block_size)
+                    O.reshape_and_cache(k[:c], v[:c], slots, self.k_cache, self.v_cache)
 
     def step_tokens(self):
         """(req, pos, k, v) of the step: the ragged chunk, then the decode tokens."""
@@ -71,9 +77,25 @@ class OracleStep:
         O.reshape_and_cache(k[mine], v[mine], slots[: len(req)][mine], self.k_cache, self.v_cache)
         return slots
 
-    def attention(self, q, walk_blocks=None, requests=None, window=0):
+    def attention(self, q, walk_blocks=None, requests=None, window=0, threads=1):
+        """The oracle's attention of the chosen rows (default: the materialised
+        ones); with ``threads`` > 1 the rows are spread over a thread pool, one
+        request per call, and their outputs gathered."""
         w = self.w
         walk = self.table.shape[1] if walk_blocks is None else walk_blocks
-        rows = self.rows if requests is None else requests
-        return O.paged_decode_attention(q, self.k_cache, self.v_cache, self.table, w.seq_lens,
-                                        walk, w.scale, w.dtype, requests=rows, window=window)
+        rows = self.rows if requests is None else list(requests)
+
+        def run(rs):
+            return O.paged_decode_attention(q, self.k_cache, self.v_cache, self.table,
+                                            w.seq_lens, walk, w.scale, w.dtype, requests=rs,
+                                            window=window)
+
+        if threads <= 1 or len(rows) <= 1:
+            return run(rows)
+        out = None
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            for r, o in zip(rows, pool.map(lambda r: run([r]), rows)):
+                if out is None:
+                    out = np.zeros_like(o)
+                out[r] = o[r]
+        return out
