@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     load,
     make_workspace,
     paged_decode_attention,
+    paged_decode_attention_noalloc,
     paged_decode_attention_append,
     paged_decode_attention_swa,
     kv_swa_tail_trim,

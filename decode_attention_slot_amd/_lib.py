@@ -36,6 +36,7 @@ EXPORTS = (
     "kv_map_to_kernel_blocks",
     "paged_decode_attention_workspace_bytes",
     "paged_decode_attention",
+    "paged_decode_attention_noalloc",
     "paged_decode_attention_append",
     "paged_decode_attention_swa",
     "kv_swa_tail_trim",
@@ -83,6 +84,10 @@ def _lib():
             vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32, i64, f32,
             ctypes.c_int, u32, vp, sz, vp, vp,
         ]
+        lib.paged_decode_attention_noalloc.argtypes = [
+            vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32, i64, f32,
+            ctypes.c_int, u32, vp, vp,
+        ]
         lib.paged_decode_attention_append.argtypes = [
             vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32,
             i32, i64, f32, ctypes.c_int, u32, vp, sz, vp, vp,
@@ -101,7 +106,7 @@ def _lib():
         lib.select_batch_bucket.argtypes = [i32, vp, i32, vp]
         for name in ("kv_slot_mapping", "kv_cache_write", "kv_slot_mapping_cache_write",
                      "select_ctx_bucket", "kv_map_to_kernel_blocks", "paged_decode_attention",
-                     "paged_decode_attention_append",
+                     "paged_decode_attention_noalloc", "paged_decode_attention_append",
                      "paged_decode_attention_swa", "kv_swa_tail_trim", "kv_slot_mapping_dcp",
                      "paged_decode_attention_dcp", "decode_lse_merge", "select_batch_bucket"):
             getattr(lib, name).restype = ctypes.c_int
@@ -129,6 +134,12 @@ def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None) -> int:
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _out_shape(t: torch.Tensor, shape, where: str) -> None:
+    """A caller-supplied output must have exactly the shape the call writes."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{where}: out has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _stream(t: torch.Tensor, stream) -> int:
@@ -284,6 +295,7 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     walk = stride if walk_blocks is None else int(walk_blocks)
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    _out_shape(out, (B, Sq, Hq, D), "paged_decode_attention")
     if workspace is None:
         workspace = make_workspace(B, Sq, Hq, hkv, D, q.device)
     st = _lib().paged_decode_attention(
@@ -294,6 +306,35 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         _dev(workspace, "workspace", torch.uint8), int(workspace.numel()),
         _dev(out, "out", torch.float32), _stream(q, stream))
     _check(st, "paged_decode_attention")
+    return out
+
+
+def paged_decode_attention_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                                   walk_blocks: Optional[int] = None, flags: int = 0,
+                                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """paged_decode_attention without a workspace: the library's own device
+    array holds the split-K partials (calls on one GPU must not overlap).
+    See paged_decode_attention_noalloc in kvslot.h."""
+    B, Sq, Hq, D = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != D or q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype \
+            or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("paged_decode_attention_noalloc: shape or dtype mismatch")
+    if block_table.shape[0] < B or seq_lens.numel() < B:
+        raise ValueError("paged_decode_attention_noalloc: block_table / seq_lens have too few rows")
+    stride = int(block_table.shape[1])
+    walk = stride if walk_blocks is None else int(walk_blocks)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    _out_shape(out, (B, Sq, Hq, D), "paged_decode_attention_noalloc")
+    st = _lib().paged_decode_attention_noalloc(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table", torch.int32, 2), stride, walk,
+        _dev(seq_lens, "seq_lens", torch.int32), int(B), int(Sq), int(Hq), int(hkv), int(D),
+        int(bs), int(nb), float(scale), _kvs_dtype(k_cache), int(flags),
+        _dev(out, "out", torch.float32), _stream(q, stream))
+    _check(st, "paged_decode_attention_noalloc")
     return out
 
 
@@ -327,6 +368,7 @@ def paged_decode_attention_append(req_indices: torch.Tensor, positions: torch.Te
         slot_mapping = torch.empty(n, dtype=torch.int64, device=q.device)
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    _out_shape(out, (B, Sq, Hq, D), "paged_decode_attention_append")
     if workspace is None:
         workspace = make_workspace(B, Sq, Hq, hkv, D, q.device)
     st = _lib().paged_decode_attention_append(
@@ -362,6 +404,7 @@ def paged_decode_attention_swa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
     walk = stride if walk_blocks is None else int(walk_blocks)
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
+    _out_shape(out, (B, Sq, Hq, D), "paged_decode_attention_swa")
     if workspace is None:
         workspace = make_workspace(B, Sq, Hq, hkv, D, q.device)
     off = None if kv_pos_offset is None else _dev(kv_pos_offset, "kv_pos_offset", torch.int32, 1)
@@ -416,6 +459,8 @@ def paged_decode_attention_dcp(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
         out = torch.empty((B, Sq, Hq, D), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, Sq, Hq), dtype=torch.float32, device=q.device)
+    _out_shape(out, (B, Sq, Hq, D), "paged_decode_attention_dcp")
+    _out_shape(lse, (B, Sq, Hq), "paged_decode_attention_dcp")
     if workspace is None:
         workspace = make_workspace(B, Sq, Hq, hkv, D, q.device)
     st = _lib().paged_decode_attention_dcp(
@@ -441,6 +486,8 @@ def decode_lse_merge(outs: torch.Tensor, lses: torch.Tensor, out: Optional[torch
         out = torch.empty(outs.shape[1:], dtype=torch.float32, device=outs.device)
     if lse is None:
         lse = torch.empty(lses.shape[1:], dtype=torch.float32, device=outs.device)
+    _out_shape(out, outs.shape[1:], "decode_lse_merge")
+    _out_shape(lse, lses.shape[1:], "decode_lse_merge")
     st = _lib().decode_lse_merge(_dev(outs, "outs", torch.float32), _dev(lses, "lses", torch.float32),
                                  world, rows, D, _dev(out, "out", torch.float32),
                                  _dev(lse, "lse", torch.float32), _stream(outs, stream))

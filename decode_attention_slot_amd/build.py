@@ -11,6 +11,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -18,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvslot.so")
 
-SOURCES = ["abi.cpp", "slot_mapping.hip", "cache_write.hip", "slot_write.hip", "paged_decode.hip", "lse_merge.hip"]
+SOURCES = ["abi.cpp", "slot_mapping.hip", "cache_write.hip", "slot_write.hip", "paged_decode.hip", "lse_merge.hip",
+           "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -43,13 +45,15 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="kvslot_build_") as tmp:
-        objs = []
+        cmds, objs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
-            _run(cmd, verbose)
+            cmds.append([cc, *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
+        # one compiler process per source, a few at a time
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1, 8)) as pool:
+            list(pool.map(lambda c: _run(c, verbose), cmds))
         tmp_lib = os.path.join(tmp, "libkvslot.so")
         _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib], verbose)
         os.replace(tmp_lib, LIB) if _same_fs(tmp_lib, LIB) else shutil.copyfile(tmp_lib, LIB)

@@ -51,7 +51,8 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
                   int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                   int32_t head_dim, int32_t block_size, int64_t total_blocks, float scale,
                   kvs_dtype dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
-                  float* out, float* lse, void* stream, const AppendArgs* app = nullptr) {
+                  float* out, float* lse, void* stream, const AppendArgs* app = nullptr,
+                  bool noalloc = false) {
   if (num_seqs < 0 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
       block_size < 1 || table_stride < 1 || walk_blocks < 0 || walk_blocks > table_stride ||
       total_blocks < 1 || !isfinite(scale) || window < 0 || cp_world < 1 || cp_rank < 0 ||
@@ -91,16 +92,23 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
         total_blocks * block_size, num_kv_heads * head_dim * elem_bytes(dtype),
         (hipStream_t)stream));
   }
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || (!workspace && !noalloc))
     return KVS_EINVAL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(kv_pos_offset, 4) ||
       !aligned(out, 16) || !aligned(lse, 4) || !aligned(workspace, 16))
     return KVS_EINVAL;
-  const size_t need =
-      paged_decode_attention_workspace_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim);
-  if (workspace_bytes < need) return KVS_ENOSPACE;
+  // The caller's workspace must hold the size query's bound, which fits any
+  // device; the library's own (noalloc) only what this launch uses.
+  if (!noalloc && workspace_bytes < paged_decode_attention_workspace_bytes(
+                                        num_seqs, q_len, num_q_heads, num_kv_heads, head_dim))
+    return KVS_ENOSPACE;
 
+  if (noalloc) {
+    // the library's array on the current device, looked up on first use
+    if (kvs::noalloc_scratch(&workspace) != hipSuccess) return KVS_EHIP;
+    workspace_bytes = kvs::kNoallocScratchBytes;
+  }
   kvs::DecodeParams p{};
   p.q = q;
   p.k_cache = k_cache;
@@ -141,6 +149,15 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
     p.app_slots = app->slot_mapping;
     p.app_tokens = app->num_tokens;
     p.app_max_tokens = app->max_num_tokens;
+  }
+  if (noalloc) {
+    // partial slots slice + request, below slices + num_seqs
+    int slices = 0;
+    if (kvs::decode_slices(p, &slices) != hipSuccess) return KVS_EHIP;
+    const size_t need = kvs::decode_meta_bytes(num_seqs) +
+                        kvs::decode_partial_slot_bytes(q_len, num_q_heads, head_dim) *
+                            ((size_t)slices + (size_t)num_seqs);
+    if (need > workspace_bytes) return KVS_ENOSPACE;
   }
   return launch_status(kvs::launch_paged_decode(p, (hipStream_t)stream));
 }
@@ -359,6 +376,21 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
                        nullptr, 0, 1, 0, 1, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim,
                        block_size, total_blocks, scale, dtype, flags, workspace,
                        workspace_bytes, out, nullptr, stream);
+}
+
+int paged_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, int32_t table_stride,
+                                   int32_t walk_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                                   int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t total_blocks,
+                                   float scale, kvs_dtype dtype, uint32_t flags, float* out,
+                                   void* stream) {
+  static_assert(KVS_NOALLOC_WORKSPACE_BYTES == kvs::kNoallocScratchBytes,
+                "public and internal sizes of the library's workspace differ");
+  return decode_common(q, k_cache, v_cache, block_table, table_stride, walk_blocks, seq_lens,
+                       nullptr, 0, 1, 0, 1, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim,
+                       block_size, total_blocks, scale, dtype, flags, nullptr, 0, out, nullptr,
+                       stream, nullptr, true);
 }
 
 int paged_decode_attention_swa(const void* q, const void* k_cache, const void* v_cache,

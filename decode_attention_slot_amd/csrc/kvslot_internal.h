@@ -86,9 +86,20 @@ size_t decode_meta_bytes(int32_t num_seqs);
 int32_t decode_max_slices(int32_t num_kv_heads);
 size_t decode_partial_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
                             int32_t num_kv_heads, int32_t head_dim);
+// Bytes of one partial slot (every KV head's rows of one (slice, request)).
+size_t decode_partial_slot_bytes(int32_t q_len, int32_t num_q_heads, int32_t head_dim);
 // Dynamic LDS of the pass-1 kernel: the batch's tile prefix.
 size_t decode_lds_bytes(int32_t num_seqs);
+// Slices a launch with these parameters cuts the batch into on the current
+// device (the launch uses partial slots below slices + num_seqs).
+hipError_t decode_slices(const DecodeParams& p, int* slices);
 
 hipError_t launch_paged_decode(const DecodeParams& p, hipStream_t stream);
+
+// The library's own device workspace for the entry point that allocates
+// nothing: kNoallocScratchBytes on each device, shared by every such call
+// on that device. Returns its address on the current device.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace kvs

@@ -994,25 +994,35 @@ hipError_t device_cus(int* out) {
   return hipSuccess;
 }
 
+// The slices the batch's tiles are cut into on the current device: one per
+// resident workgroup slot (per head group), at most eight waves per compute
+// unit (more waves add partials to merge but no bytes in flight that the
+// stream needs) and one workgroup per compute unit at four KV heads per
+// workgroup (4 waves: measured 4-6% faster than two such workgroups per
+// unit, while two-head workgroups are fastest at four per unit), never more
+// than the workspace holds partials for.
 template <bool BF16, int D, int NW>
-hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t stream) {
-  const int HG = pin.num_kv_heads / NW;
+hipError_t slices_typed(const DecodeParams& p, int* slices) {
+  const int HG = p.num_kv_heads / NW;
   int resident = 0, cus = 0;
   hipError_t e = resident_workgroups<BF16, D, NW>(&resident);
   if (e != hipSuccess) return e;
   e = device_cus(&cus);
   if (e != hipSuccess) return e;
-  // One slice per resident workgroup slot (per head group), at most eight
-  // waves per compute unit (more waves add partials to merge but no bytes
-  // in flight that the stream needs) and one workgroup per compute unit at
-  // four KV heads per workgroup (4 waves: measured 4-6% faster than two
-  // such workgroups per unit, while two-head workgroups are fastest at four
-  // per unit), never more than the workspace holds partials for.
-  DecodeParams p = pin;
   const int cap = cus * (NW == 4 ? 1 : 8 / NW);
   const int wgs = resident < cap ? resident : cap;
-  p.slices = wgs / HG > 1 ? wgs / HG : 1;
-  if (p.slices > p.max_slices) p.slices = p.max_slices;
+  int s = wgs / HG > 1 ? wgs / HG : 1;
+  if (s > p.max_slices) s = p.max_slices;
+  *slices = s;
+  return hipSuccess;
+}
+
+template <bool BF16, int D, int NW>
+hipError_t launch_typed(const DecodeParams& pin, int bs_shift, hipStream_t stream) {
+  const int HG = pin.num_kv_heads / NW;
+  DecodeParams p = pin;
+  hipError_t e = slices_typed<BF16, D, NW>(p, &p.slices);
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)p.slices * (unsigned)HG);
   const size_t lds = decode_lds_bytes(p.num_seqs);
   if (p.app_max_tokens > 0) {
@@ -1052,6 +1062,15 @@ hipError_t launch_heads(const DecodeParams& p, int bs_shift, hipStream_t stream)
   return launch_typed<BF16, D, 1>(p, bs_shift, stream);
 }
 
+template <bool BF16, int D>
+hipError_t slices_heads(const DecodeParams& p, int* slices) {
+  const int h = p.num_kv_heads;
+  if (h % 8 == 0) return slices_typed<BF16, D, 8>(p, slices);
+  if (h % 4 == 0) return slices_typed<BF16, D, 4>(p, slices);
+  if (h % 2 == 0) return slices_typed<BF16, D, 2>(p, slices);
+  return slices_typed<BF16, D, 1>(p, slices);
+}
+
 }  // namespace
 
 int32_t decode_max_slices(int32_t num_kv_heads) {
@@ -1073,8 +1092,21 @@ size_t decode_partial_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads
                             int32_t num_kv_heads, int32_t head_dim) {
   // Partial slot of (slice, request) is slice + request: every segment of
   // a slice's range has its own slot, below max_slices + num_seqs.
-  const size_t slots = (size_t)decode_max_slices(num_kv_heads) + (size_t)num_seqs;
-  return slots * (size_t)num_q_heads * (size_t)q_len * (size_t)(head_dim + 4) * sizeof(float);
+  return decode_partial_slot_bytes(q_len, num_q_heads, head_dim) *
+         ((size_t)decode_max_slices(num_kv_heads) + (size_t)num_seqs);
+}
+
+size_t decode_partial_slot_bytes(int32_t q_len, int32_t num_q_heads, int32_t head_dim) {
+  return (size_t)num_q_heads * (size_t)q_len * (size_t)(head_dim + 4) * sizeof(float);
+}
+
+hipError_t decode_slices(const DecodeParams& p, int* slices) {
+  if (p.is_bf16) {
+    if (p.head_dim == 128) return slices_heads<true, 128>(p, slices);
+    return slices_heads<true, 64>(p, slices);
+  }
+  if (p.head_dim == 128) return slices_heads<false, 128>(p, slices);
+  return slices_heads<false, 64>(p, slices);
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, hipStream_t stream) {

@@ -275,6 +275,43 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
                            size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * paged_decode_attention_noalloc - paged_decode_attention for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments and results
+ * without the workspace: the split-K partials go to a device array the
+ * library owns, KVS_NOALLOC_WORKSPACE_BYTES on each GPU it runs on, held
+ * from the loading of the library's code object until the process ends.
+ * The call allocates and frees nothing; its first call on a device looks
+ * the array's address up (hipGetSymbolAddress) with that device current.
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's contents (no call needs it cleared). Calls that overlap on
+ * one GPU (two streams, two threads) race on it and their results are
+ * unspecified: the caller orders them, e.g. on one stream.
+ *
+ * On one device the output is bitwise that of paged_decode_attention with
+ * the same arguments (the same kernels and launch). The call needs
+ * 256-rounded 8 * num_seqs bytes plus (S + num_seqs) partial slots of
+ * num_q_heads * q_len * (head_dim + 4) * 4 bytes, S being the number of
+ * slices the launch cuts the batch into (at most the device's resident
+ * pass-1 workgroups per head group: 256 on MI355X at 8 KV heads); a call
+ * that needs more than KVS_NOALLOC_WORKSPACE_BYTES returns KVS_ENOSPACE
+ * before anything is enqueued (the 256-request, 64-query-head batch needs
+ * about 18 MB).
+ * Errors: those of paged_decode_attention, KVS_ENOSPACE as above, KVS_EHIP
+ * when the array's address cannot be obtained.
+ */
+#define KVS_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+int paged_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, int32_t table_stride,
+                                   int32_t walk_blocks, const int32_t* seq_lens, int32_t num_seqs,
+                                   int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int64_t total_blocks,
+                                   float scale, kvs_dtype dtype, uint32_t flags, float* out,
+                                   void* stream);
+
+/*
  * paged_decode_attention_append - the step's cache write and the decode
  * attention in one call: the result is that of kv_slot_mapping_cache_write
  * (with table_rows = num_seqs: the step's tokens index the batch's rows)

@@ -280,6 +280,24 @@ void check_gpu_entry_argument_checks() {
                                         1, 32, 8, 96, 64, 1024, 0.088f, KVS_BF16, 0, nullptr, 0,
                                         nullptr, nullptr) == KVS_EUNSUPPORTED,
           "append: head_dim 96");
+  // the entry point without a workspace: argument errors come back before
+  // the library looks up its own array (no device needed here)
+  require(paged_decode_attention_noalloc(at(0x100008), at(0x100000), at(0x100000), i16, 80, 80,
+                                         i16, 12, 1, 32, 8, 128, 64, 1024, 0.088f, KVS_BF16, 0,
+                                         f16, nullptr) == KVS_EINVAL,
+          "noalloc: q not 16-byte aligned");
+  require(paged_decode_attention_noalloc(nullptr, nullptr, nullptr, nullptr, 80, 80, nullptr, 12,
+                                         1, 32, 8, 96, 64, 1024, 0.088f, KVS_BF16, 0, nullptr,
+                                         nullptr) == KVS_EUNSUPPORTED,
+          "noalloc: head_dim 96");
+  require(paged_decode_attention_noalloc(at(0x100000), at(0x100000), at(0x100000), i16, 80, 80,
+                                         i16, 12, 1, 32, 8, 128, 64, 1024, 0.088f, KVS_BF16, 0,
+                                         nullptr, nullptr) == KVS_EINVAL,
+          "noalloc: no output");
+  require(paged_decode_attention_noalloc(nullptr, nullptr, nullptr, nullptr, 80, 80, nullptr, 0,
+                                         1, 32, 8, 128, 64, 1024, 0.088f, KVS_BF16, 0, nullptr,
+                                         nullptr) == KVS_OK,
+          "noalloc: empty batch");
   require(decode_lse_merge(static_cast<float*>(at(0x100008)), f16, 2, 16, 128, f16, f16,
                            nullptr) == KVS_EINVAL,
           "merge inputs not 16-byte aligned");

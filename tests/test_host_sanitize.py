@@ -15,11 +15,13 @@ import subprocess
 
 import pytest
 
+from decode_attention_slot_amd import build
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "decode_attention_slot_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc"
-HIP_SOURCES = ["slot_mapping.hip", "cache_write.hip", "slot_write.hip", "paged_decode.hip",
-               "lse_merge.hip"]
+# the library's device sources, as its build lists them
+HIP_SOURCES = [s for s in build.SOURCES if s.endswith(".hip")]
 # each sanitizer flag applies to host code only
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-sanitize-recover=all"]
