@@ -68,22 +68,28 @@ DESCRIPTIONS = {
        "buckets [4096, 8192, 16384], bs 64, Hkv 8, Hq 32, D 128",
     3: "large batch bf16: 256 requests (+8 padded rows), ctx U[512,8192], manager bs 32 split to "
        "kernel bs 16, Hkv 8, Hq 64, D 128",
+    "3spec": "large batch bf16 with speculative decode: 256 requests (+8 padded rows), ctx "
+             "U[512,8192], 1+{n} causal decode tokens each, manager bs 32 split to kernel bs 16, "
+             "Hkv 8, Hq 64, D 128",
     4: "ragged + speculative bf16: 64 requests, 8192-token ragged chunk, then 1+3 causal decode "
        "tokens each, bs 64, Hkv 8, Hq 32, D 128",
 }
-KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_slot_amd", "csrc", "paged_decode.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_slot_amd", "csrc", f)
+                  for f in ("paged_decode.h", "paged_decode.hip", "paged_decode_nc2.hip",
+                            "paged_decode_nc4.hip")]
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of the decode kernels' code: the source with // comments,
+    """sha256[:16] of the decode kernels' code: the sources with // comments,
     trailing blanks and empty lines removed, so that editing a comment does not
     retire a counter measurement of unchanged code."""
     lines = []
-    with open(KERNEL_SOURCE, encoding="utf-8") as f:
-        for line in f:
-            code = line.split("//", 1)[0].rstrip()
-            if code:
-                lines.append(code)
+    for path in KERNEL_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
@@ -237,6 +243,9 @@ def main(argv=None) -> int:
                          "bucket's or the whole table's columns")
     ap.add_argument("--max-ctx", type=int, default=None,
                     help="bucketing workload: clip the drawn context lengths and pin the largest")
+    ap.add_argument("--num-spec", type=int, default=0,
+                    help="large-batch workload: decode 1 + this many causal tokens per request "
+                         "(3: 32 query rows per KV head)")
     ap.add_argument("--rotate", type=int, default=0, help="cache copies to rotate over (0 = auto)")
     ap.add_argument("--calls", type=int, default=100,
                     help="event-timed attention calls after the steps (median; at least 50)")
@@ -286,6 +295,10 @@ def main(argv=None) -> int:
     cuda = torch.device("cuda:0")
     idx = WORKLOADS[args.workload]
     extra = {"forced_max_ctx": args.max_ctx} if (idx == 2 and args.max_ctx is not None) else {}
+    if args.num_spec:
+        if idx != 3:
+            raise SystemExit("--num-spec applies to the large-batch workload")
+        extra["num_spec"] = args.num_spec
     w = W.make_workload(idx, seed=args.seed, **extra)
     if args.tp > 1:
         w = W.tp_share(w, args.tp)
@@ -564,7 +577,8 @@ def main(argv=None) -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, seeded block permutation; no dataset)",
         "config": {
-            "workload": DESCRIPTIONS[idx],
+            "workload": (DESCRIPTIONS["3spec"].format(n=args.num_spec) if args.num_spec
+                         else DESCRIPTIONS[idx]),
             "seed": w.seed,
             "max_ctx": int((w.computed + w.chunk_lens)[: w.num_reqs].max()),
             "num_seqs": w.num_rows,
@@ -617,7 +631,9 @@ def main(argv=None) -> int:
             "traffic": measured_traffic(args.workload,
                                         f"window{args.window}" if args.window else
                                         (f"dcp{dcp[0]}" if dcp else
-                                         (f"tp{args.tp}" if args.tp > 1 else args.walk))),
+                                         (f"tp{args.tp}" if args.tp > 1 else
+                                          (f"spec{args.num_spec}" if args.num_spec
+                                           else args.walk)))),
         },
         "setup_s": round(t_setup, 2),
     }

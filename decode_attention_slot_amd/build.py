@@ -19,8 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvslot.so")
 
-SOURCES = ["abi.cpp", "slot_mapping.hip", "cache_write.hip", "slot_write.hip", "paged_decode.hip", "lse_merge.hip",
-           "noalloc.hip"]
+SOURCES = ["abi.cpp", "slot_mapping.hip", "cache_write.hip", "slot_write.hip", "paged_decode.hip",
+           "paged_decode_nc2.hip", "paged_decode_nc4.hip", "lse_merge.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -27,7 +27,7 @@ int elem_bytes(kvs_dtype d) {
   }
 }
 
-constexpr int kMaxRows = 16;        // (Hq / Hkv) * q_len: one MFMA column tile
+constexpr int kMaxRows = 64;        // (Hq / Hkv) * q_len: four MFMA column tiles of 16
 constexpr int kMaxSeqs = kvs::kDecodeMaxSeqs;
 
 }  // namespace

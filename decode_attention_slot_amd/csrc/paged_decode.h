@@ -1,0 +1,936 @@
+// GQA paged decode attention for gfx950.
+//
+// What is computed ("Padding and Batching with Block KV", sections "Block
+// Table", "Cache Masking" and "Multi-Token Decode"; "Decode Context-Length
+// Bucketing", sections "Problem" and "Block-table head-trim vs. SWA
+// tail-trim"): query token j of request r sits at position L - q_len + j,
+// where L counts this step's tokens, and attends to every earlier-or-equal
+// position p below walk_blocks * block_size whose block-table entry is
+// active; q head h reads KV head h / (Hq / Hkv). The result is the softmax of
+// scale * <q, k> over those keys applied to the values, in fp32.
+// A sliding-window layer ("KV Caching with vLLM", section "Attention Type";
+// "Decode Context-Length Bucketing", the SWA tail trim) adds two things: a
+// window, so the query at qpos sees keys from qpos - window + 1 only, and a
+// per-request kv_pos_offset, the absolute position of the (tail-trimmed)
+// table's column 0; positions stay absolute.
+//
+// How, on CDNA4:
+// * Work split: the 16-token tiles of every request's context, laid end to
+//   end over the batch, are cut into `slices` equal ranges, one per
+//   resident workgroup slot (at most eight waves per compute unit, four
+//   with four KV heads per workgroup), so every
+//   workgroup streams the same number of bytes and all finish together (no
+//   rounds, no tail of short units). A
+//   range may start or end inside a request and may span requests; each
+//   (slice, request) piece is a segment. One wavefront per KV head; a
+//   workgroup holds the waves of NW KV heads, so the [block][token][head]
+//   rows it reads are contiguous in HBM.
+// * The cut is made on the device from seq_lens (no host synchronisation):
+//   every workgroup scans the batch's tile counts into an LDS prefix. It
+//   depends only on the visible context lengths and the device, so a
+//   head-trimmed walk, a full-table walk and the context walk produce the
+//   same partials.
+// * The block ids of a segment are staged in LDS by the workgroup (pieces of
+//   up to 256 blocks), so each tile's block id is an LDS read that does not
+//   hold up the vector-memory pipeline.
+// * The tile loop is straight-line: the loads of tile t+1 are issued before
+//   tile t is computed and are never under a data-dependent branch (an
+//   inactive table entry reads null block 0 and is masked; the loop tail
+//   re-loads its last tile, which hits in cache), so one tile stays in
+//   flight behind the one being computed. A barrier every two tiles keeps
+//   the waves of a workgroup in step.
+// * Tile of 16 tokens. S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (fp32 KV:
+//   v_mfma_f32_16x16x4f32): K is the A operand (lane l holds token l % 16,
+//   16 bytes of its head row per piece), Q^T the B operand (lane l holds
+//   query row l % 16; rows are (query token, head in group), at most 16).
+//   The result gives each lane four tokens of one query row.
+// * Online softmax per query row, in exp2 units, entirely inside the lane
+//   except one max over the four lane groups (two permlane swaps).
+// * O^T = V^T P^T on v_mfma_f32_16x16x4f32: lane l holds the fp32 value of
+//   dimension column l % 16 for token 4 * (l / 16) + i, which is exactly a
+//   16-byte slice of that token's head row, so V is read in its natural
+//   layout (each 16-lane group reads one whole 256-byte head row). The
+//   accumulator lands with query row = l % 16, matching the softmax state.
+// * A segment that holds a whole request writes its output. Otherwise its
+//   partial state (acc, m, l per row) goes to slot slice + request of the
+//   workspace, and a second kernel merges a request's partials in one fixed
+//   association (below), so results do not depend on scheduling, on the
+//   launch shape or on the batch around the request.
+// * Masked keys are removed by select, never by multiplying by zero, and the
+//   values of keys past the context are replaced by -0.0, so unwritten (NaN
+//   canary) cache rows cannot leak into the output and a masked product is
+//   -0.0, which leaves every accumulator bit-unchanged.
+// * The fixed-shape table walk is a separate instantiation: it computes
+//   the same segments, then reads every walked column past each context
+//   (cut the same way over the slices) and folds those bytes into a sink
+//   that is stored only under a flag the host never sets.
+#pragma once
+
+#include <math.h>
+
+#include <atomic>
+
+#include "kvslot_internal.h"
+#include "slot_formula.h"
+
+namespace kvs {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kFlagWalkTable = 0x1u;
+// Never set by the host. Testing it keeps the table-walk loads alive.
+constexpr uint32_t kFlagSink = 0x80000000u;
+// pass-1 modes: context walk, fixed-shape table walk, the general walk
+// (sliding window, tail-trimmed table, context-parallel share), and the
+// context walk that first writes the step's new tokens (append)
+constexpr int kContextWalk = 0, kTableWalk = 1, kGeneral = 2, kAppend = 3;
+constexpr int kTile = 16;
+constexpr int kStage = 256;  // block ids staged in LDS at a time
+constexpr int kDepth = 2;    // tiles in flight per wave
+
+// Wavefront scans on DPP: four row shifts build the prefix inside each row
+// of 16 lanes, two row broadcasts carry it across rows. Values move lane to
+// lane in the VALU, with no LDS round trip. Every lane must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, false);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+
+// Reductions over the four 16-lane groups of a wavefront (lanes l, l ^ 16,
+// l ^ 32, l ^ 48): permlane16_swap pairs rows 0-1 and 2-3, permlane32_swap
+// pairs the two halves. Each lane receives its partner's value; both
+// operands of the combine are then the same in every lane of the group.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// The tiles request r walks: absolute positions [16 * t_lo, E) in 16-token
+// tiles, n of them. off is the absolute position of table column 0 (a
+// tail-trimmed table; 0 for a whole table), rounded down to a block. E ends
+// the visible context: the request's length, cut at the walked columns. With
+// a sliding window the walk starts at the earliest key a query of this step
+// sees (L - q_len - window + 1). Positions stay below 2^31 - 64.
+struct ReqSpan {
+  int off, E, t_lo, n;
+};
+
+// Under context parallelism the walk runs over this rank's own positions
+// (its cache's local positions, 0 .. E - 1): the global positions below
+// min(L, walk_blocks * world * bs) that this rank stores.
+template <bool GEN>
+__device__ __forceinline__ ReqSpan request_span(const DecodeParams& p, int r, int L, int walk_tok,
+                                                int bs, int Sq) {
+  ReqSpan sp;
+  if (GEN && p.cp_world > 1) {
+    const int64_t eg = min((int64_t)L, (int64_t)walk_tok * p.cp_world);
+    const int64_t run = (int64_t)1 << p.cp_ishift;
+    const int64_t span = run * p.cp_world;
+    const int64_t rem = eg > 0 ? eg % span - (int64_t)p.cp_rank * run : 0;
+    const int64_t e_loc = eg > 0 ? (eg / span) * run + min(max(rem, (int64_t)0), run) : 0;
+    sp.off = 0;
+    sp.E = (int)min(e_loc, (int64_t)INT32_MAX - 64);
+    sp.t_lo = 0;
+    sp.n = (sp.E + 15) / 16;
+    return sp;
+  }
+  const int32_t* kv_pos_offset = p.kv_pos_offset;
+  const int32_t window = p.window;
+  const int off = GEN && kv_pos_offset ? kv_pos_offset[r] : 0;
+  sp.off = max(off, 0) & ~(bs - 1);
+  int64_t E = min((int64_t)L, (int64_t)sp.off + walk_tok);
+  E = min(E, (int64_t)INT32_MAX - 64);
+  sp.E = L <= 0 ? 0 : (int)E;
+  int64_t start = sp.off;
+  if (GEN && window > 0) start = max(start, (int64_t)L - Sq - window + 1);
+  sp.t_lo = (int)(start / 16);
+  sp.n = sp.E > start ? (sp.E + 15) / 16 - sp.t_lo : 0;
+  return sp;
+}
+
+// Natural-log sum of exp(scores) of a row from its running state: max m
+// (log2 units) and sum l of exp2(score - m); -inf when the row saw no key.
+__device__ __forceinline__ float row_lse(float m, float l) {
+  return l > 0.0f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
+// v_perm_b32 selectors over {x (bytes 4-7), y (bytes 0-3)}: the low halves
+// of y and x, or their high halves, as one pair (y's half first).
+constexpr uint32_t kPermLo = 0x05040100u, kPermHi = 0x07060302u;
+
+// The high 16 bits of two floats (their bf16 truncations), a first: one
+// bf16 pair.
+__device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), kPermHi);
+}
+
+// MODE: kContextWalk, kTableWalk (the fixed-shape walk) or kGeneral (a
+// sliding window over a possibly tail-trimmed table, or one rank's share
+// under context parallelism).
+// NC: column tiles of 16 query rows per wave (rows = (Hq / Hkv) * q_len,
+// at most 16 NC); at NC 4 a wave holds 64 rows of accumulators and runs one
+// per SIMD.
+template <bool BF16, int D, int NW, int MODE, int NC>
+__global__ void __launch_bounds__(NW * 64, NC >= 4 ? 1 : 2)
+paged_decode_kernel(const DecodeParams p, int bs_shift) {
+  constexpr int ES = BF16 ? 2 : 4;       // bytes per element
+  constexpr int EP = 16 / ES;            // elements per 16-byte piece
+  constexpr int NP = D / (4 * EP);       // 16-byte K pieces per lane per token
+  constexpr int NT = D / 16;             // P.V n-tiles (dimension columns of 16)
+  constexpr int NVW = NT * ES / 4;       // V dwords per lane per token
+  constexpr int PSTRIDE = D + 4;         // floats per partial row (acc, m, l, pad)
+  constexpr int NTHR = NW * 64;
+  constexpr bool TW = MODE == kTableWalk;
+  constexpr bool GEN = MODE == kGeneral;
+  constexpr bool APP = MODE == kAppend;
+  constexpr uint32_t kNegZero = BF16 ? 0x80008000u : 0x80000000u;
+  static_assert(NP >= 1 && NVW >= 2, "unsupported head_dim");
+  struct TileBuf {
+    u32x4 k[NP];         // K pieces of token rho of the tile
+    uint32_t v[4][NVW];  // V slices of tokens 4*jg .. 4*jg+3
+    int bid;             // block id the tile was read from (0: inactive entry)
+  };
+  extern __shared__ int s_pref[];  // [num_seqs + 1]: first tile of each request
+  __shared__ int s_blk[kStage];
+  __shared__ int s_wave[NW], s_wave_n[NW];
+  // append: the step tokens whose rows this slice reads, and their slots
+  __shared__ int s_app_t[APP ? NW * 64 : 1];
+  __shared__ int64_t s_app_s[APP ? NW * 64 : 1];
+  __shared__ int s_app_n;
+  // request holding this slice's first unit (context), first padding tile,
+  // and the context tiles of the requests before the latter
+  __shared__ int s_first[3];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rho = lane & 15;  // query row owned by this lane (MFMA column)
+  const int jg = lane >> 4;   // lane group: tokens 4*jg .. 4*jg+3 of a tile
+
+  const int B = p.num_seqs;
+  const int bs = 1 << bs_shift;
+  const int walk_tok = p.walk_blocks << bs_shift;
+  const int walk_tiles = walk_tok / kTile;
+  const int Hkv = p.num_kv_heads;
+  const int Hq = p.num_q_heads;
+  const int G = Hq / Hkv;
+  const int Sq = p.q_len;
+  const int nrows = G * Sq;
+  const int HG = Hkv / NW;  // the launcher picks NW dividing Hkv
+  const int S = p.slices;
+  const int slice = blockIdx.x / HG;
+  const int hg = blockIdx.x - slice * HG;
+  const int g = hg * NW + wave;
+  const int64_t block_bytes = ((int64_t)Hkv * D * ES) << bs_shift;
+  const uint32_t row_bytes = (uint32_t)(Hkv * D * ES);
+
+  // ---- work prefix of the batch, in LDS ------------------------------------
+  // The context tiles of all requests, laid end to end, are cut into S equal
+  // ranges, one per slice; a slice's range may start or end inside a
+  // request and may cover several requests. Its pieces are the segments.
+  // Each request with context also counts start_tiles units ahead of its
+  // tiles (the cost of starting a segment), so a slice that starts a
+  // request carries that many fewer tiles. s_pref holds these units.
+  const int X = p.start_tiles;
+  // The first request of this thread's share is loaded here, before the
+  // append's token loads, so that waiting for it does not wait for them.
+  const int len0 = (int)threadIdx.x < B ? p.seq_lens[threadIdx.x] : 0;
+  // append: this thread's step token and its slot, looked up before the
+  // scan below so that the table read overlaps it
+  // (the slot formula of slot_formula.h, with its table read issued here and
+  // its value first used after the scan)
+  int app_r = -1, app_blk = 0;
+  int64_t app_p = -1, app_lb = -1;
+  if constexpr (APP) {
+    if ((int64_t)threadIdx.x < p.app_tokens) {
+      app_r = p.app_req[threadIdx.x];
+      app_p = p.app_pos[threadIdx.x];
+    }
+  }
+  if ((int)threadIdx.x < B) s_pref[threadIdx.x] = request_span<GEN>(p, threadIdx.x, len0, walk_tok, bs, Sq).n;
+  if constexpr (APP) {
+    if (app_r >= 0 && app_r < B && app_p >= 0 && (app_p >> bs_shift) < p.table_stride) {
+      app_lb = app_p >> bs_shift;
+      app_blk = p.block_table[(int64_t)app_r * p.table_stride + app_lb];
+    }
+  }
+  for (int rr = threadIdx.x + NTHR; rr < B; rr += NTHR)
+    s_pref[rr] = request_span<GEN>(p, rr, p.seq_lens[rr], walk_tok, bs, Sq).n;
+  if (threadIdx.x == 0) {
+    s_first[0] = 0;
+    s_first[1] = 0;
+    s_first[2] = 0;
+  }
+  __syncthreads();
+  const int per = (B + NTHR - 1) / NTHR;  // contiguous requests per thread
+  const int rb = min((int)threadIdx.x * per, B);
+  const int re = min(rb + per, B);
+  int local = 0, local_n = 0;  // units and tiles of this thread's requests
+  for (int rr = rb; rr < re; ++rr) {
+    const int n = s_pref[rr];
+    local += n > 0 ? n + X : 0;
+    local_n += n;
+  }
+  const int incl = wave_inclusive_scan(local);
+  const int incl_n = TW ? wave_inclusive_scan(local_n) : 0;
+  if (lane == 63) {
+    s_wave[wave] = incl;
+    s_wave_n[wave] = incl_n;
+  }
+  __syncthreads();
+  int total = 0, run = incl - local, total_n = 0, run_n = incl_n - local_n;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = s_wave[w];
+    const int tn = s_wave_n[w];
+    total += t;
+    run += w < wave ? t : 0;
+    total_n += tn;
+    run_n += w < wave ? tn : 0;
+  }
+  // total <= num_seqs * (walk_tiles + X) < 2^31 (checked by the host)
+  const int Q = max((total + S - 1) / S, p.min_tiles);  // units per slice
+  const int a = (int)min((int64_t)slice * Q, (int64_t)total);
+  const int b = (int)min((int64_t)a + Q, (int64_t)total);
+  // Fixed-shape walk: the columns past each request's context (its padding
+  // tiles) are cut evenly into a second range per slice.
+  const int pad_total = TW ? B * walk_tiles - total_n : 0;
+  const int Qp = max((pad_total + S - 1) / S, p.min_tiles);
+  const int pa = (int)min((int64_t)slice * Qp, (int64_t)pad_total);
+  const int pbnd = (int)min((int64_t)pa + Qp, (int64_t)pad_total);
+  for (int rr = rb; rr < re; ++rr) {
+    const int n = s_pref[rr];
+    const int wu = n > 0 ? n + X : 0;
+    if (run <= a && a < run + wu) s_first[0] = rr;
+    if (TW) {
+      const int pr = rr * walk_tiles - run_n;  // padding tiles before request rr
+      if (pr <= pa && pa < pr + (walk_tiles - n)) {
+        s_first[1] = rr;
+        s_first[2] = run_n;
+      }
+    }
+    s_pref[rr] = run;
+    run += wu;
+    run_n += n;
+  }
+  if (threadIdx.x == 0) s_pref[B] = total;
+  if constexpr (APP) {
+    if (threadIdx.x == 0) s_app_n = 0;
+  }
+  __syncthreads();
+
+  // ---- append: write the step's new K/V rows before any tile is read ------
+  // A row lies in one tile of its request; the slice holding that tile (the
+  // cut above) writes it, each wave its own KV head's part, so the wave that
+  // later loads those bytes is the one that stored them, and it waits for
+  // its stores before going on. Rows of positions no slice reads (past the
+  // walked tiles) and the slot mapping itself are written by workgroup 0.
+  if constexpr (APP) {
+    constexpr int PR = D * ES / 16;  // 16-byte pieces of one head's row
+    const int64_t T = p.app_tokens;
+    const int64_t total_slots = p.total_blocks << bs_shift;
+    const bool first_wg = blockIdx.x == 0;
+    int owner = -1;  // slice that reads this token's tile
+    if (app_r >= 0 && app_r < B && app_p >= 0) {
+      const int wu = s_pref[app_r + 1] - s_pref[app_r];
+      const int64_t k = app_p >> 4;
+      if (wu > 0 && k < wu - X) owner = (s_pref[app_r] + X + (int)k) / Q;
+    }
+    const bool own = owner == slice;
+    const int64_t s =
+        app_lb >= 0 && app_blk > 0 ? (int64_t)app_blk * bs + (app_p - (app_lb << bs_shift)) : -1;
+    const bool inb = s >= 0 && s < total_slots;
+    if (first_wg && (int64_t)threadIdx.x < p.app_max_tokens)
+      p.app_slots[threadIdx.x] = (int64_t)threadIdx.x < T ? s : -1;
+    const u32x4* kn = (const u32x4*)p.app_k;
+    const u32x4* vn = (const u32x4*)p.app_v;
+    u32x4* kc = (u32x4*)p.app_k_cache;
+    u32x4* vc = (u32x4*)p.app_v_cache;
+    if (first_wg && (int64_t)threadIdx.x < T && inb && owner < 0) {
+      for (int q4 = 0; q4 < Hkv * PR; ++q4) {
+        kc[s * Hkv * PR + q4] = kn[(int64_t)threadIdx.x * Hkv * PR + q4];
+        vc[s * Hkv * PR + q4] = vn[(int64_t)threadIdx.x * Hkv * PR + q4];
+      }
+    }
+    if (own && inb) {
+      const int i = atomicAdd(&s_app_n, 1);
+      s_app_t[i] = (int)threadIdx.x;
+      s_app_s[i] = s;
+    }
+    __syncthreads();
+    const int n_own = s_app_n;
+    for (int k0 = 0; k0 < n_own; k0 += 64 / PR) {
+      const int kk = k0 + lane / PR;
+      if (kk < n_own) {
+        const int pc = lane % PR;
+        const int64_t src = ((int64_t)s_app_t[kk] * Hkv + g) * PR + pc;
+        const int64_t dst = (s_app_s[kk] * Hkv + g) * PR + pc;
+        kc[dst] = kn[src];
+        vc[dst] = vn[src];
+      }
+    }
+    if (n_own > 0) __builtin_amdgcn_s_waitcnt(0);  // this wave's stores land before its loads
+  }
+
+  uint32_t sink = 0;
+  const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
+  const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
+
+  // Tiles [tok_a, tok_b) (absolute positions, multiples of kTile) of table
+  // row trow, whose column 0 holds position off, through fn(position of the
+  // tile, its loads). Block ids are staged in LDS in pieces
+  // of kStage; a ring of kDepth tile buffers keeps tiles t+1 .. t+kDepth-1
+  // in flight while tile t is used. Loads past the last tile re-load the
+  // last tile (a cache hit), so no load depends on a branch.
+  auto walk_tiles_of = [&](const int32_t* trow, int off, int tok_a, int tok_b, auto&& fn) {
+    const int blk_first = (tok_a - off) >> bs_shift;
+    const int blk_end = ((tok_b - 1 - off) >> bs_shift) + 1;
+    for (int pb = blk_first; pb < blk_end; pb += kStage) {
+      const int pn = min(kStage, blk_end - pb);
+      __syncthreads();  // the previous piece is consumed by every wave
+      for (int i = threadIdx.x; i < pn; i += NTHR) {
+        const int col = pb + i;
+        s_blk[i] = col < p.table_stride ? trow[col] : 0;
+      }
+      __syncthreads();
+      const int t_begin = max(tok_a, off + (pb << bs_shift));
+      const int t_end = min(tok_b, off + ((pb + pn) << bs_shift));
+      const int nt = (t_end - t_begin) / kTile;
+
+      // K as the score MFMA's A operand, V in row layout. An inactive
+      // entry reads null block 0 and is masked by the caller. V rows are
+      // read with the nontemporal hint (streamed past the caches): on
+      // MI355X that lifts long streams of reads from ~6.4 to ~7 TB/s; K
+      // stays a plain load, its latency heads the per-tile dependency chain.
+      auto load = [&](int tt, TileBuf& bf) {
+        const int bid = uniform(s_blk[((tt - off) >> bs_shift) - pb]);
+        const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
+        const int64_t base = (int64_t)(active ? bid : 0) * block_bytes;
+        const char* kb = (const char*)p.k_cache + base;
+        const char* vb = (const char*)p.v_cache + base;
+        const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
+        bf.bid = active ? bid : 0;
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp)
+          bf.k[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const char* src = vb + in_blk + v_lane_off + i * row_bytes;
+          if constexpr (NVW == 2) {
+            const u32x2 x = __builtin_nontemporal_load((const u32x2*)src);
+            bf.v[i][0] = x[0];
+            bf.v[i][1] = x[1];
+          } else {
+#pragma unroll
+            for (int w = 0; w < NVW; w += 4) {
+              const u32x4 x = __builtin_nontemporal_load((const u32x4*)(src + w * 4));
+              bf.v[i][w] = x[0];
+              bf.v[i][w + 1] = x[1];
+              bf.v[i][w + 2] = x[2];
+              bf.v[i][w + 3] = x[3];
+            }
+          }
+        }
+      };
+      TileBuf bufs[kDepth];
+      auto tile_at = [&](int t) { return t_begin + min(t, nt - 1) * kTile; };
+#pragma unroll
+      for (int s = 0; s < kDepth - 1; ++s) load(tile_at(s), bufs[s]);
+      for (int t = 0; t < nt; t += kDepth) {
+        // Keep the workgroup's waves in step (every wave walks the same
+        // tiles, for its own KV head). Two waves share each SIMD, and the
+        // older one wins issue arbitration; left alone it runs ahead and the
+        // other finishes its last tiles with half the loads in flight. A
+        // bare s_barrier waits for no memory access, so the tiles already
+        // requested stay in flight across it.
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int s = 0; s < kDepth; ++s) {
+          load(tile_at(t + s + kDepth - 1), bufs[(s + kDepth - 1) % kDepth]);
+          if (t + s < nt) fn(t_begin + (t + s) * kTile, bufs[s]);
+        }
+      }
+    }
+  };
+
+  // ---- one segment: tiles [t0, t1) of request r (nr tiles, tile 0 at unit pr) --
+  auto segment = [&](int r, int t0, int t1, int nr, int pr) {
+    const int L = uniform(p.seq_lens[r]);
+    const ReqSpan sp = request_span<GEN>(p, r, L, walk_tok, bs, Sq);
+    const int E = uniform(sp.E);
+    const int off = uniform(sp.off);
+    const int t_lo = uniform(sp.t_lo);
+
+    // Query rows 16 c + rho, c < NC (rows are (query token, head in group));
+    // the B operand of the score MFMA of column tile c.
+    const int qpos_min = L - Sq;
+    const int all_lo =
+        GEN && p.window > 0 ? (int)max((int64_t)L - p.window, (int64_t)INT32_MIN) : INT32_MIN;
+    int jrow[NC], hh[NC], qpos[NC], qlo[NC];
+    u32x4 qp[NC][NP];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int row = 16 * c + rho;
+      jrow[c] = row / G;
+      hh[c] = row - jrow[c] * G;
+      qpos[c] = row < nrows ? L - Sq + jrow[c] : -1;
+      // sliding window: the row sees keys from qpos - window + 1; every row
+      // does from L - window on
+      qlo[c] = GEN && p.window > 0
+                   ? (int)max((int64_t)qpos[c] - p.window + 1, (int64_t)INT32_MIN)
+                   : INT32_MIN;
+      const char* qrow = (const char*)p.q +
+                         ((((int64_t)r * Sq + jrow[c]) * Hq + (int64_t)g * G + hh[c]) * D) * ES;
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        qp[c][pp] = (u32x4){0u, 0u, 0u, 0u};
+        if (row < nrows) qp[c][pp] = *(const u32x4*)(qrow + pp * 64 + jg * 16);
+      }
+    }
+    // Global position of a walked position: itself, except under context
+    // parallelism, where the walk runs over this rank's local positions.
+    auto gpos = [&](int lp) -> int64_t {
+      if constexpr (GEN) {
+        const int64_t run = lp >> p.cp_ishift;
+        return (((run * p.cp_world) + p.cp_rank) << p.cp_ishift) + (lp & ((1 << p.cp_ishift) - 1));
+      } else {
+        return lp;
+      }
+    };
+
+    // running softmax state of each query row
+    float m_run[NC], l_run[NC];  // l_run: this lane's tokens only
+    f32x4 acc[NC][NT];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      m_run[c] = -INFINITY;
+      l_run[c] = 0.0f;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[c][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Scores, online softmax and P.V for one tile whose loads have landed.
+    auto consume = [&](int tt, TileBuf& bf) {
+      const bool active = bf.bid > 0;
+      float sx[NC][4];  // scale_log2 * S^T[token 4*jg+i][row 16c+rho]
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          if constexpr (BF16) {
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf.k[pp]),
+                                                        __builtin_bit_cast(bf16x8, qp[c][pp]), s,
+                                                        0, 0, 0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(bf.k[pp][e]),
+                                                       __uint_as_float(qp[c][pp][e]), s, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sx[c][i] = s[i] * p.scale_log2;
+      }
+      const bool full = active && (tt + kTile <= E) && (gpos(tt + kTile - 1) <= qpos_min) &&
+                        (!GEN || tt >= all_lo);
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = tt + 4 * jg + i;
+          const bool kv_ok = active && pos < E;
+          const int64_t gp = gpos(pos);
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            if (!(kv_ok && gp <= qpos[c] && (!GEN || pos >= qlo[c]))) sx[c][i] = -INFINITY;
+          if (!kv_ok) {
+#pragma unroll
+            for (int w = 0; w < NVW; ++w) bf.v[i][w] = kNegZero;
+          }
+        }
+      }
+
+      // online softmax, per row
+      float pr4[NC][4];
+      bool moved = false;
+      float alpha[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float mx = fmaxf(fmaxf(sx[c][0], sx[c][1]), fmaxf(sx[c][2], sx[c][3]));
+        mx = max_over_groups(mx);
+        const float m_new = fmaxf(m_run[c], mx);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        alpha[c] = __builtin_amdgcn_exp2f(m_run[c] - m_use);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr4[c][i] = __builtin_amdgcn_exp2f(sx[c][i] - m_use);
+        l_run[c] = l_run[c] * alpha[c] + ((pr4[c][0] + pr4[c][1]) + (pr4[c][2] + pr4[c][3]));
+        m_run[c] = m_new;
+        moved |= alpha[c] != 1.0f;
+      }
+      if (__any(moved)) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[c][n] *= alpha[c];
+      }
+
+      // O^T += V^T P^T
+      if constexpr (BF16) {
+        // On v_mfma_f32_16x16x16_bf16, the whole tile at once: lane (jg, rho)
+        // gives A = V^T[dim column][tokens 4 jg .. 4 jg + 3] and B =
+        // P^T[those tokens][row 16 c + rho]. P is split into three bf16
+        // terms, each the top 8 significant bits of what the previous ones
+        // left (a truncation, so the remainder is exact): hi + mid + lo == p
+        // bit for bit, and the three products accumulate in fp32.
+        u32x2 pt[NC][3];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          float rem[4] = {pr4[c][0], pr4[c][1], pr4[c][2], pr4[c][3]};
+#pragma unroll
+          for (int term = 0; term < 3; ++term) {
+            pt[c][term] = (u32x2){bf16_pair_hi(rem[0], rem[1]), bf16_pair_hi(rem[2], rem[3])};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              rem[t] -= __uint_as_float(__float_as_uint(rem[t]) & 0xffff0000u);
+          }
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          // dimension column rho of n-tile n is dimension rho * NT + n: the
+          // low or high half of dword n / 2 of each token's 16-byte slice
+          const uint32_t sel = (n & 1) ? kPermHi : kPermLo;
+          const u32x2 a = {__builtin_amdgcn_perm(bf.v[1][n >> 1], bf.v[0][n >> 1], sel),
+                           __builtin_amdgcn_perm(bf.v[3][n >> 1], bf.v[2][n >> 1], sel)};
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int term = 0; term < 3; ++term)
+              acc[c][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                  __builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, pt[c][term]),
+                  acc[c][n], 0, 0, 0);
+        }
+      } else {
+        // fp32 values on v_mfma_f32_16x16x4f32, four tokens per step: lane
+        // (jg, rho) gives dimension column rho of token 4 jg + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+              acc[c][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(bf.v[i][n]),
+                                                               pr4[c][i], acc[c][n], 0, 0, 0);
+        }
+      }
+    };
+    walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, off, (t_lo + t0) * kTile,
+                  (t_lo + t1) * kTile, consume);
+
+    // acc[c][n][i] holds dimension (4*jg + i) * NT + n of query row 16c + rho.
+    const int d_base = 4 * jg * NT;
+    const bool whole = t0 == 0 && t1 == nr;
+    if (t0 == 0 && hg == 0 && threadIdx.x == 0) {
+      // Request r's partials sit at slots slice + r .. last slice + r.
+      p.chunk_meta[2 * r] = slice + r;
+      p.chunk_meta[2 * r + 1] = whole ? 1 : (pr + nr - 1) / Q - slice + 1;
+    }
+    float* pslot = p.partials + (((int64_t)slice + r) * Hkv + g) * nrows * PSTRIDE;
+    float l_sum[NC];  // whole-wave sums first: the stores below are per lane
+#pragma unroll
+    for (int c = 0; c < NC; ++c) l_sum[c] = sum_over_groups(l_run[c]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float l_tot = l_sum[c];
+      const int row = 16 * c + rho;
+      if (row >= nrows) continue;
+      if (whole) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        float* o =
+            p.out + (((int64_t)r * Sq + jrow[c]) * Hq + (int64_t)g * G + hh[c]) * D + d_base;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int n0 = 0; n0 < NT; n0 += 4) {
+            f32x4 v = {acc[c][n0][i] * inv, acc[c][n0 + 1][i] * inv, acc[c][n0 + 2][i] * inv,
+                       acc[c][n0 + 3][i] * inv};
+            *(f32x4*)(o + i * NT + n0) = v;
+          }
+        }
+        if (p.lse_out && jg == 0)
+          p.lse_out[((int64_t)r * Sq + jrow[c]) * Hq + (int64_t)g * G + hh[c]] =
+              row_lse(m_run[c], l_tot);
+        continue;
+      }
+      // split: publish this segment's partial state, in store order: float4
+      // k = i * NT / 4 + n0 / 4 of lane (jg, row) sits at float4 index
+      // (k * 4 + jg) * nrows + row of the slot, so each store writes
+      // contiguous runs of 16 rows (a row-major layout would put each lane's
+      // 16 bytes in a different cache line); (m, l) of the rows follow all
+      // the float4s.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int n0 = 0; n0 < NT; n0 += 4) {
+          const int k = i * (NT / 4) + n0 / 4;
+          f32x4 v = {acc[c][n0][i], acc[c][n0 + 1][i], acc[c][n0 + 2][i], acc[c][n0 + 3][i]};
+          *(f32x4*)(pslot + ((k * 4 + jg) * nrows + row) * 4) = v;
+        }
+      }
+      if (jg == 0) *(f32x2*)(pslot + nrows * D + 2 * row) = (f32x2){m_run[c], l_tot};
+    }
+  };
+
+  // ---- this slice's context tiles, request by request ---------------------
+  {
+    int r = uniform(s_first[0]);
+    int pos = a;
+    while (pos < b) {
+      const int pr = uniform(s_pref[r]);
+      const int pn = uniform(s_pref[r + 1]);
+      if (pn > pos) {
+        const int e = min(b, pn);
+        const int t_base = pr + X;  // unit of r's tile 0
+        const int t0 = max(pos, t_base) - t_base;
+        const int t1 = e - t_base;
+        if (t1 > t0) segment(r, t0, t1, pn - t_base, t_base);
+        pos = e;
+      }
+      ++r;
+    }
+  }
+
+  // ---- requests with no visible context produce zeros --------------------
+  for (int r = blockIdx.x; r < B; r += gridDim.x) {
+    if (s_pref[r + 1] == s_pref[r]) {
+      const int row_floats = Sq * Hq * D;
+      float* o = p.out + (int64_t)r * row_floats;
+      for (int i = threadIdx.x; i < row_floats; i += NTHR) o[i] = 0.0f;
+      if (p.lse_out)
+        for (int i = threadIdx.x; i < Sq * Hq; i += NTHR) p.lse_out[(int64_t)r * Sq * Hq + i] = -INFINITY;
+      if (threadIdx.x == 0) p.chunk_meta[2 * r + 1] = 0;
+    }
+  }
+
+  // ---- fixed-shape walk: read this slice's padding tiles, use none -------
+  if constexpr (TW) {
+    auto drain = [&](int, TileBuf& bf) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) sink ^= bf.k[pp][0] ^ bf.k[pp][1] ^ bf.k[pp][2] ^ bf.k[pp][3];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < NVW; ++w) sink ^= bf.v[i][w];
+    };
+    int r = uniform(s_first[1]);
+    int tp = uniform(s_first[2]);  // context tiles of the requests before r
+    int pos = pa;
+    while (pos < pbnd) {
+      const int wu = uniform(s_pref[r + 1]) - uniform(s_pref[r]);
+      const int n = wu > 0 ? wu - X : 0;
+      const int pr = r * walk_tiles - tp;
+      const int pn = pr + (walk_tiles - n);
+      if (pn > pos) {
+        const int e = min(pbnd, pn);
+        walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, 0, (n + pos - pr) * kTile,
+                      (n + e - pr) * kTile, drain);
+        pos = e;
+      }
+      tp += n;
+      ++r;
+    }
+    if (p.flags & kFlagSink) p.out[0] = __uint_as_float(sink);
+  }
+}
+
+// Workgroups of a kernel the device holds at once (compute units times
+// workgroups per unit at that size and LDS), queried once per device and
+// kernel; `cache` is the kernel's per-device slot.
+constexpr int kMaxDevices = 64;
+
+inline hipError_t resident_of(const void* kernel, int threads, size_t lds,
+                       std::atomic<int> (&cache)[kMaxDevices], int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && (*out = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds);
+  if (e != hipSuccess) return e;
+  *out = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  if (cached) cache[dev].store(*out, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
+// Pass-1 workgroups at the largest LDS the kernel asks for. The context
+// walk's figure serves every mode, so all modes cut the batch the same way.
+template <bool BF16, int D, int NW, int NC>
+hipError_t resident_workgroups(int* out) {
+  static std::atomic<int> cache[kMaxDevices];
+  return resident_of(
+      reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, kContextWalk, NC>), NW * 64,
+      decode_lds_bytes(kDecodeMaxSeqs), cache, out);
+}
+
+// Compute units of the current device, queried once per device.
+inline hipError_t device_cus(int* out) {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && (*out = cache[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+  e = hipDeviceGetAttribute(out, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (*out < 1) *out = 1;
+  if (cached) cache[dev].store(*out, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
+// The slices the batch's tiles are cut into on the current device: one per
+// resident workgroup slot (per head group), at most eight waves per compute
+// unit (more waves add partials to merge but no bytes in flight that the
+// stream needs) and one workgroup per compute unit at four KV heads per
+// workgroup (4 waves: measured 4-6% faster than two such workgroups per
+// unit, while two-head workgroups are fastest at four per unit), never more
+// than the workspace holds partials for.
+template <bool BF16, int D, int NW, int NC>
+hipError_t slices_typed(const DecodeParams& p, int* slices) {
+  const int HG = p.num_kv_heads / NW;
+  int resident = 0, cus = 0;
+  hipError_t e = resident_workgroups<BF16, D, NW, NC>(&resident);
+  if (e != hipSuccess) return e;
+  e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const int cap = cus * (NW == 4 ? 1 : 8 / NW);
+  const int wgs = resident < cap ? resident : cap;
+  int s = wgs / HG > 1 ? wgs / HG : 1;
+  if (s > p.max_slices) s = p.max_slices;
+  *slices = s;
+  return hipSuccess;
+}
+
+// Pass 1 over p.slices slices (the caller's cut): the step's writes first
+// when they do not qualify for the append mode, then the kernel of the
+// walk mode.
+template <bool BF16, int D, int NW, int NC>
+hipError_t pass1_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) {
+  const int HG = p.num_kv_heads / NW;
+  const dim3 grid((unsigned)p.slices * (unsigned)HG);
+  const size_t lds = decode_lds_bytes(p.num_seqs);
+  hipError_t e;
+  if (p.app_max_tokens > 0) {
+    // The step's rows are written by pass 1 when all its tokens fit one
+    // workgroup's threads and the walk is the context walk; otherwise by
+    // the fused slot-map + write kernel first.
+    if (!(p.flags & kFlagWalkTable) && p.window == 0 && !p.kv_pos_offset && p.cp_world == 1 &&
+        p.app_max_tokens <= NW * 64) {
+      paged_decode_kernel<BF16, D, NW, kAppend, NC>
+          <<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+      return hipGetLastError();
+    }
+    e = launch_slot_write(p.app_req, p.app_pos, p.app_tokens, p.app_max_tokens, p.block_table,
+                          p.num_seqs, p.table_stride, p.block_size, p.app_slots, p.app_k,
+                          p.app_v, p.app_k_cache, p.app_v_cache, p.total_blocks * p.block_size,
+                          p.num_kv_heads * p.head_dim * (p.is_bf16 ? 2 : 4), stream);
+    if (e != hipSuccess) return e;
+  }
+  if (p.flags & kFlagWalkTable)
+    paged_decode_kernel<BF16, D, NW, kTableWalk, NC>
+        <<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+  else if (p.window > 0 || p.kv_pos_offset || p.cp_world > 1)
+    paged_decode_kernel<BF16, D, NW, kGeneral, NC>
+        <<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+  else
+    paged_decode_kernel<BF16, D, NW, kContextWalk, NC>
+        <<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+  return hipGetLastError();
+}
+
+// KV heads per workgroup: the largest of 8, 4, 2, 1 dividing Hkv (at most 4
+// at NC 4, whose waves run one per SIMD).
+template <bool BF16, int D, int NC>
+hipError_t pass1_heads(const DecodeParams& p, int bs_shift, hipStream_t stream) {
+  const int h = p.num_kv_heads;
+  if constexpr (NC < 4) {
+    if (h % 8 == 0) return pass1_typed<BF16, D, 8, NC>(p, bs_shift, stream);
+  }
+  if (h % 4 == 0) return pass1_typed<BF16, D, 4, NC>(p, bs_shift, stream);
+  if (h % 2 == 0) return pass1_typed<BF16, D, 2, NC>(p, bs_shift, stream);
+  return pass1_typed<BF16, D, 1, NC>(p, bs_shift, stream);
+}
+
+template <bool BF16, int D, int NC>
+hipError_t slices_heads(const DecodeParams& p, int* slices) {
+  const int h = p.num_kv_heads;
+  if constexpr (NC < 4) {
+    if (h % 8 == 0) return slices_typed<BF16, D, 8, NC>(p, slices);
+  }
+  if (h % 4 == 0) return slices_typed<BF16, D, 4, NC>(p, slices);
+  if (h % 2 == 0) return slices_typed<BF16, D, 2, NC>(p, slices);
+  return slices_typed<BF16, D, 1, NC>(p, slices);
+}
+
+template <int NC>
+hipError_t pass1_for(const DecodeParams& p, hipStream_t stream) {
+  const int bs_shift = __builtin_ctz((unsigned)p.block_size);
+  if (p.is_bf16) {
+    if (p.head_dim == 128) return pass1_heads<true, 128, NC>(p, bs_shift, stream);
+    return pass1_heads<true, 64, NC>(p, bs_shift, stream);
+  }
+  if (p.head_dim == 128) return pass1_heads<false, 128, NC>(p, bs_shift, stream);
+  return pass1_heads<false, 64, NC>(p, bs_shift, stream);
+}
+
+template <int NC>
+hipError_t slices_for(const DecodeParams& p, int* slices) {
+  if (p.is_bf16) {
+    if (p.head_dim == 128) return slices_heads<true, 128, NC>(p, slices);
+    return slices_heads<true, 64, NC>(p, slices);
+  }
+  if (p.head_dim == 128) return slices_heads<false, 128, NC>(p, slices);
+  return slices_heads<false, 64, NC>(p, slices);
+}
+
+}  // namespace
+
+// Pass 1 (and the slices it cuts the batch into) at 16, 32 and 64 query
+// rows per KV head, one translation unit each (paged_decode.hip,
+// paged_decode_nc2.hip, paged_decode_nc4.hip).
+hipError_t decode_pass1_nc1(const DecodeParams& p, hipStream_t stream);
+hipError_t decode_pass1_nc2(const DecodeParams& p, hipStream_t stream);
+hipError_t decode_pass1_nc4(const DecodeParams& p, hipStream_t stream);
+hipError_t decode_slices_nc1(const DecodeParams& p, int* slices);
+hipError_t decode_slices_nc2(const DecodeParams& p, int* slices);
+hipError_t decode_slices_nc4(const DecodeParams& p, int* slices);
+
+}  // namespace kvs

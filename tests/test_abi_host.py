@@ -164,7 +164,8 @@ def test_gpu_entry_points_reject_bad_scalars(K):
     assert pda(d=96) == -2                  # head_dim
     assert pda(bs=48) == -2                 # block size
     assert pda(bs=8) == -2
-    assert pda(sq=5) == -2                  # 4 * 5 = 20 rows > 16
+    assert pda(sq=17) == -2                 # 4 * 17 = 68 rows > 64
+    assert pda(sq=16) == -1                 # 64 rows: supported (null pointers remain)
     assert pda(dtype=5) == -2
     assert pda(B=9000) == -2
     assert pda(scale=float("nan")) == -1

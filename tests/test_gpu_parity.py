@@ -179,6 +179,14 @@ def test_tensor_parallel_share_at_scale(cuda, tp):
     full_parity(W.tp_share(W.make_workload(3), tp), cuda)
 
 
+@pytest.mark.parametrize("num_spec,num_reqs", [(3, 256), (7, 64)])
+def test_large_batch_speculative(cuda, num_spec, num_reqs):
+    """The 256-request batch's heads (GQA 8) decoding 1 + num_spec causal
+    tokens per request: 32 query rows per KV head (all 256 requests) and 64
+    (64 requests); whole images and every row against the oracle."""
+    full_parity(W.make_workload(3, num_spec=num_spec, num_reqs=num_reqs), cuda)
+
+
 def test_large_batch_manager_view_equals_kernel_view(cuda, large_batch):
     """The same pool read at manager block size 32 gives the same output."""
     w, s = large_batch
@@ -266,6 +274,18 @@ SHAPES = [
     ("bf16", 128, 32, 12, 1, 4, [4, 500, 2500]),
     ("bf16", 128, 64, 16, 2, 1, [1, 64, 4100]),
     ("f32", 64, 16, 32, 1, 1, [1, 300, 1200]),
+    # more than 16 query rows per KV head: two column tiles of 16 rows per
+    # wave (17-32 rows) and four (33-64), the last tile partly filled
+    ("bf16", 128, 16, 8, 8, 4, [4, 5, 17, 600, 3000]),   # the 256-request heads, 1 + 3 tokens
+    ("bf16", 128, 16, 4, 6, 3, [3, 30, 1000]),           # 18 rows
+    ("bf16", 64, 64, 2, 12, 2, [2, 64, 65, 2200]),       # 24 rows, head_dim 64
+    ("bf16", 128, 64, 2, 16, 4, [4, 64, 65, 2000]),      # 64 rows
+    ("bf16", 64, 32, 4, 8, 8, [8, 9, 100, 1500]),        # 64 rows, head_dim 64
+    ("bf16", 128, 32, 3, 20, 3, [3, 90, 2500]),          # 60 rows, one-wave groups of 3
+    ("bf16", 128, 16, 8, 5, 7, [7, 8, 300, 6000]),       # 35 rows, eight heads in two groups
+    ("f32", 128, 16, 2, 12, 2, [2, 33, 700]),            # fp32, 24 rows
+    ("f32", 64, 64, 1, 8, 5, [5, 6, 400]),               # fp32, 40 rows
+    ("f32", 128, 32, 8, 4, 16, [16, 17, 300]),           # fp32, 64 rows
 ]
 
 
@@ -323,7 +343,7 @@ def random_case_params(seed):
     bs = [16, 32, 64, 128, 256][rng.integers(5)]
     hkv = [1, 2, 3, 4, 6, 8, 12, 16][rng.integers(8)]
     sq = int(rng.integers(1, 5))
-    g = int(rng.choice([x for x in (1, 2, 3, 4, 8) if x * sq <= 16]))
+    g = int(rng.choice([x for x in (1, 2, 3, 4, 8, 16) if x * sq <= 64]))
     nb = int(rng.integers(1, 41))
     kind = rng.random(nb)
     lens = np.where(kind < 0.6, rng.integers(sq, 40, nb),
@@ -1057,6 +1077,11 @@ def test_unsupported_shapes_raise(cuda):
     with pytest.raises(K.KvslotError) as e:
         gpu_attn(c, walk_blocks=c["table"].shape[1] + 1)
     assert e.value.name == "KVS_EINVAL"
+    # more than 64 query rows per KV head (GQA 16 with 5 tokens: 80)
+    c80 = small_case(cuda, 2, [10], 16, 1, 16, 5, 64, "bf16")
+    with pytest.raises(K.KvslotError) as e:
+        gpu_attn(c80)
+    assert e.value.name == "KVS_EUNSUPPORTED"
     small_ws = torch.zeros(16, dtype=torch.uint8, device=cuda)
     with pytest.raises(K.KvslotError) as e:
         gpu_attn(c, workspace=small_ws)

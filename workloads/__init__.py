@@ -330,7 +330,8 @@ def make_workload(index: int, seed: Optional[int] = None, **kw) -> Workload:
 
     Keyword overrides: ``num_reqs`` (configs 1, 3, 4), ``forced_max_ctx``
     (config 2: clip the lognormal draw and pin its maximum), ``ctx_hi``
-    (configs 1 and 3: upper end of the uniform context draw).
+    (configs 1 and 3: upper end of the uniform context draw), ``num_spec``
+    (config 3: speculative tokens decoded per request, default 0).
     """
     seed = 1000 + index if seed is None else seed
     builder = (_tiny, _block_config, _bucketing, _large_batch, _ragged_spec)[index]
@@ -396,12 +397,15 @@ def _bucketing(seed, forced_max_ctx=None, num_reqs=8, **kw):
     )
 
 
-def _large_batch(seed, num_reqs=256, num_pad_rows=8, ctx_lo=512, ctx_hi=8192, **kw):
+def _large_batch(seed, num_reqs=256, num_pad_rows=8, ctx_lo=512, ctx_hi=8192, num_spec=0, **kw):
+    # num_spec > 0: the same batch decoding 1 + num_spec causal tokens per
+    # request (speculative decoding), e.g. 32 query rows per KV head at 3
     mgr_bs, kern_bs = 32, 16
-    Wm = 257
+    q_len = 1 + num_spec
     g = _rng(seed, _TAG_LEN)
     computed = g.integers(ctx_lo, ctx_hi + 1, size=num_reqs).astype(np.int64)
-    seq = computed + 1
+    seq = computed + q_len
+    Wm = max(257, -(-(ctx_hi + q_len) // mgr_bs))
     nb = _blocks_for(seq, mgr_bs)
     mgr_total = int(nb.sum()) + 1
     perm = _rng(seed, _TAG_PERM).permutation(np.arange(1, mgr_total, dtype=np.int32))
@@ -417,11 +421,11 @@ def _large_batch(seed, num_reqs=256, num_pad_rows=8, ctx_lo=512, ctx_hi=8192, **
     return Workload(
         name="", index=3, seed=seed, dtype="bf16", block_size=kern_bs,
         total_blocks=mgr_total * (mgr_bs // kern_bs),
-        num_kv_heads=8, num_q_heads=64, head_dim=128, q_len=1, num_reqs=num_reqs,
+        num_kv_heads=8, num_q_heads=64, head_dim=128, q_len=q_len, num_reqs=num_reqs,
         computed=computed_full, chunk_lens=np.zeros(B, np.int64), seq_lens=seq_full,
         block_table=None,
         mgr_block_table=mgr_full, mgr_block_size=mgr_bs, max_model_len=Wm * mgr_bs,
-        num_decode_pad_tokens=num_pad_rows,
+        num_decode_pad_tokens=num_pad_rows * q_len,
     )
 
 
