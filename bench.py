@@ -628,20 +628,39 @@ def main(argv=None) -> int:
             "call_us_mean": round(t_attn_mean * 1e6, 3),
             "call_us_p10_p90": [round(float(np.percentile(durations, 10)) * 1e6, 3),
                                 round(float(np.percentile(durations, 90)) * 1e6, 3)],
-            "traffic": measured_traffic(args.workload,
-                                        f"window{args.window}" if args.window else
-                                        (f"dcp{dcp[0]}" if dcp else
-                                         (f"tp{args.tp}" if args.tp > 1 else
-                                          (f"spec{args.num_spec}" if args.num_spec
-                                           else args.walk)))),
+            "traffic": measured_traffic(args.workload, variant_key(args)),
         },
         "setup_s": round(t_setup, 2),
     }
+    # bytes of the attention launches of this walk: what the method needs
+    # (algorithmic, whole blocks) and what the counters measured (DRAM)
+    result["walk_bytes"] = {"walk": result["config"]["walk"], "algorithmic": a_bytes,
+                            "measured_dram": result["roofline"]["traffic"]}
     if not args.no_cpu_baseline and not dcp:
         result["cpu_baseline"] = cpu_baseline(w, s.host_table, walk_blocks, args.cpu_seconds,
                                               window=args.window)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def variant_key(args) -> str:
+    """Name of the measured variant of a workload, as the counter summaries
+    under profiles/ are keyed: the walk, or the sliding window, the
+    context-parallel or tensor-parallel share, the speculative tokens, and a
+    forced largest context."""
+    if args.window:
+        key = f"window{args.window}"
+    elif args.dcp > 1:
+        key = f"dcp{args.dcp}"
+    elif args.tp > 1:
+        key = f"tp{args.tp}"
+    elif args.num_spec:
+        key = f"spec{args.num_spec}"
+    else:
+        key = args.walk
+    if args.max_ctx is not None:
+        key += f"_maxctx{args.max_ctx}"
+    return key
 
 
 def measured_traffic(workload: str, walk: str):

@@ -39,18 +39,24 @@
 //   re-loads its last tile, which hits in cache), so one tile stays in
 //   flight behind the one being computed. A barrier every two tiles keeps
 //   the waves of a workgroup in step.
-// * Tile of 16 tokens. S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (fp32 KV:
-//   v_mfma_f32_16x16x4f32): K is the A operand (lane l holds token l % 16,
-//   16 bytes of its head row per piece), Q^T the B operand (lane l holds
-//   query row l % 16; rows are (query token, head in group), at most 16).
-//   The result gives each lane four tokens of one query row.
+// * Tile of 16 tokens. The query rows of a KV head ((query token, head in
+//   group) pairs, up to 64) form NC column tiles of 16. S^T = K Q^T on
+//   v_mfma_f32_16x16x32_bf16 (fp32 KV: v_mfma_f32_16x16x4f32), once per
+//   column tile: K is the A operand (lane l holds token l % 16, 16 bytes of
+//   its head row per piece), Q^T the B operand (lane l holds query row
+//   16 c + l % 16). The result gives each lane four tokens of one row.
 // * Online softmax per query row, in exp2 units, entirely inside the lane
 //   except one max over the four lane groups (two permlane swaps).
-// * O^T = V^T P^T on v_mfma_f32_16x16x4f32: lane l holds the fp32 value of
-//   dimension column l % 16 for token 4 * (l / 16) + i, which is exactly a
-//   16-byte slice of that token's head row, so V is read in its natural
-//   layout (each 16-lane group reads one whole 256-byte head row). The
-//   accumulator lands with query row = l % 16, matching the softmax state.
+// * O^T = V^T P^T, per column tile. Lane l reads a 16-byte slice of the
+//   head rows of tokens 4 * (l / 16) .. + 3 (each 16-lane group reads whole
+//   256-byte head rows: V stays in its natural layout), and dimension column
+//   l % 16 of n-tile n is dimension (l % 16) * NT + n. bf16 KV: one
+//   v_mfma_f32_16x16x16_bf16 per n-tile takes the 16 tokens at once, its A
+//   operand packed from those slices with v_perm, its B operand P^T in bf16;
+//   P is split exactly into three bf16 terms (each the truncation of what
+//   the previous left), so the products equal those of fp32 P. fp32 KV:
+//   v_mfma_f32_16x16x4f32, four tokens per step. The accumulator lands with
+//   query row 16 c + l % 16, matching the softmax state.
 // * A segment that holds a whole request writes its output. Otherwise its
 //   partial state (acc, m, l per row) goes to slot slice + request of the
 //   workspace, and a second kernel merges a request's partials in one fixed
@@ -429,12 +435,16 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       // read with the nontemporal hint (streamed past the caches): on
       // MI355X that lifts long streams of reads from ~6.4 to ~7 TB/s; K
       // stays a plain load, its latency heads the per-tile dependency chain.
-      auto load = [&](int tt, TileBuf& bf) {
+      // A load past the last tile (`tail`) re-loads the last tile and is never
+      // used; its V part then reads the same rows of the K cache, lines the
+      // tile's K loads just brought in, instead of missing again on V (whose
+      // nontemporal loads are not kept in cache).
+      auto load = [&](int tt, TileBuf& bf, bool tail) {
         const int bid = uniform(s_blk[((tt - off) >> bs_shift) - pb]);
         const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
         const int64_t base = (int64_t)(active ? bid : 0) * block_bytes;
         const char* kb = (const char*)p.k_cache + base;
-        const char* vb = (const char*)p.v_cache + base;
+        const char* vb = (const char*)(tail ? p.k_cache : p.v_cache) + base;
         const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
         bf.bid = active ? bid : 0;
 #pragma unroll
@@ -462,7 +472,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       TileBuf bufs[kDepth];
       auto tile_at = [&](int t) { return t_begin + min(t, nt - 1) * kTile; };
 #pragma unroll
-      for (int s = 0; s < kDepth - 1; ++s) load(tile_at(s), bufs[s]);
+      for (int s = 0; s < kDepth - 1; ++s) load(tile_at(s), bufs[s], s >= nt);
       for (int t = 0; t < nt; t += kDepth) {
         // Keep the workgroup's waves in step (every wave walks the same
         // tiles, for its own KV head). Two waves share each SIMD, and the
@@ -473,7 +483,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int s = 0; s < kDepth; ++s) {
-          load(tile_at(t + s + kDepth - 1), bufs[(s + kDepth - 1) % kDepth]);
+          load(tile_at(t + s + kDepth - 1), bufs[(s + kDepth - 1) % kDepth],
+               t + s + kDepth - 1 >= nt);
           if (t + s < nt) fn(t_begin + (t + s) * kTile, bufs[s]);
         }
       }
