@@ -259,7 +259,7 @@ size_t paged_decode_attention_workspace_bytes(int32_t num_seqs, int32_t q_len,
  * from the context lengths and the device's unit count, and the split
  * decides the fp32 summation order.)
  * Supported: head_dim 64 or 128; block_size 16, 32, 64, 128 or 256;
- * (num_q_heads / num_kv_heads) * q_len <= 16; num_seqs <= 8192;
+ * (num_q_heads / num_kv_heads) * q_len <= 64; num_seqs <= 8192;
  * num_seqs * (walk_blocks * block_size / 16 + 1) <= 2^30 - 1.
  * Errors: KVS_EINVAL (null pointers, non-positive sizes, num_q_heads not a
  * multiple of num_kv_heads, walk_blocks outside [0, table_stride]),
