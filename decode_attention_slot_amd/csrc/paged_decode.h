@@ -40,7 +40,9 @@
 //   flight behind the one being computed. A barrier every two tiles keeps
 //   the waves of a workgroup in step.
 // * Tile of 16 tokens. The query rows of a KV head ((query token, head in
-//   group) pairs, up to 64) form NC column tiles of 16. S^T = K Q^T on
+//   group) pairs, up to 64) form column tiles of 16: NC of them per wave, and
+//   above 32 rows two waves per KV head share the rows (both read the same
+//   tiles; the second read hits in cache). S^T = K Q^T on
 //   v_mfma_f32_16x16x32_bf16 (fp32 KV: v_mfma_f32_16x16x4f32), once per
 //   column tile: K is the A operand (lane l holds token l % 16, 16 bytes of
 //   its head row per piece), Q^T the B operand (lane l holds query row
@@ -201,11 +203,13 @@ __device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
 // MODE: kContextWalk, kTableWalk (the fixed-shape walk) or kGeneral (a
 // sliding window over a possibly tail-trimmed table, or one rank's share
 // under context parallelism).
-// NC: column tiles of 16 query rows per wave (rows = (Hq / Hkv) * q_len,
-// at most 16 NC); at NC 4 a wave holds 64 rows of accumulators and runs one
-// per SIMD.
-template <bool BF16, int D, int NW, int MODE, int NC>
-__global__ void __launch_bounds__(NW * 64, NC >= 4 ? 1 : 2)
+// NC: column tiles of 16 query rows per wave; RH: waves per KV head, each
+// holding 16 NC consecutive rows of the head's (Hq / Hkv) * q_len rows (at
+// most 16 NC RH). The waves of one head read the same K and V tiles (the
+// second read hits in cache); the head's accumulators are split between
+// them. Waves of a workgroup: NW KV heads times RH, head-major in each half.
+template <bool BF16, int D, int NW, int MODE, int NC, int RH>
+__global__ void __launch_bounds__(NW * RH * 64, 2)
 paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int ES = BF16 ? 2 : 4;       // bytes per element
   constexpr int EP = 16 / ES;            // elements per 16-byte piece
@@ -213,7 +217,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int NT = D / 16;             // P.V n-tiles (dimension columns of 16)
   constexpr int NVW = NT * ES / 4;       // V dwords per lane per token
   constexpr int PSTRIDE = D + 4;         // floats per partial row (acc, m, l, pad)
-  constexpr int NTHR = NW * 64;
+  constexpr int NTHR = NW * RH * 64;
+  constexpr int NWAVES = NW * RH;
   constexpr bool TW = MODE == kTableWalk;
   constexpr bool GEN = MODE == kGeneral;
   constexpr bool APP = MODE == kAppend;
@@ -226,10 +231,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   };
   extern __shared__ int s_pref[];  // [num_seqs + 1]: first tile of each request
   __shared__ int s_blk[kStage];
-  __shared__ int s_wave[NW], s_wave_n[NW];
+  __shared__ int s_wave[NWAVES], s_wave_n[NWAVES];
   // append: the step tokens whose rows this slice reads, and their slots
-  __shared__ int s_app_t[APP ? NW * 64 : 1];
-  __shared__ int64_t s_app_s[APP ? NW * 64 : 1];
+  __shared__ int s_app_t[APP ? NTHR : 1];
+  __shared__ int64_t s_app_s[APP ? NTHR : 1];
   __shared__ int s_app_n;
   // request holding this slice's first unit (context), first padding tile,
   // and the context tiles of the requests before the latter
@@ -253,7 +258,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   const int S = p.slices;
   const int slice = blockIdx.x / HG;
   const int hg = blockIdx.x - slice * HG;
-  const int g = hg * NW + wave;
+  const int g = hg * NW + wave % NW;  // this wave's KV head
+  const int row0 = 16 * NC * (wave / NW);  // its first query row of that head
   const int64_t block_bytes = ((int64_t)Hkv * D * ES) << bs_shift;
   const uint32_t row_bytes = (uint32_t)(Hkv * D * ES);
 
@@ -313,7 +319,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   __syncthreads();
   int total = 0, run = incl - local, total_n = 0, run_n = incl_n - local_n;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
+  for (int w = 0; w < NWAVES; ++w) {
     const int t = s_wave[w];
     const int tn = s_wave_n[w];
     total += t;
@@ -354,10 +360,11 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 
   // ---- append: write the step's new K/V rows before any tile is read ------
   // A row lies in one tile of its request; the slice holding that tile (the
-  // cut above) writes it, each wave its own KV head's part, so the wave that
-  // later loads those bytes is the one that stored them, and it waits for
-  // its stores before going on. Rows of positions no slice reads (past the
-  // walked tiles) and the slot mapping itself are written by workgroup 0.
+  // cut above) writes it, each head's first wave its own KV head's part, so
+  // the wave that later loads those bytes is the one that stored them, and it
+  // waits for its stores before going on (with two waves per head, the other
+  // one waits at a workgroup barrier). Rows of positions no slice reads (past
+  // the walked tiles) and the slot mapping itself are written by workgroup 0.
   if constexpr (APP) {
     constexpr int PR = D * ES / 16;  // 16-byte pieces of one head's row
     const int64_t T = p.app_tokens;
@@ -392,7 +399,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     }
     __syncthreads();
     const int n_own = s_app_n;
-    for (int k0 = 0; k0 < n_own; k0 += 64 / PR) {
+    for (int k0 = 0; k0 < n_own && wave < NW; k0 += 64 / PR) {
       const int kk = k0 + lane / PR;
       if (kk < n_own) {
         const int pc = lane % PR;
@@ -403,6 +410,9 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       }
     }
     if (n_own > 0) __builtin_amdgcn_s_waitcnt(0);  // this wave's stores land before its loads
+    if constexpr (RH > 1) {
+      if (n_own > 0) __syncthreads();  // and before the other waves of its head load them
+    }
   }
 
   uint32_t sink = 0;
@@ -508,7 +518,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     u32x4 qp[NC][NP];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int row = 16 * c + rho;
+      const int row = row0 + 16 * c + rho;
       jrow[c] = row / G;
       hh[c] = row - jrow[c] * G;
       qpos[c] = row < nrows ? L - Sq + jrow[c] : -1;
@@ -664,7 +674,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, off, (t_lo + t0) * kTile,
                   (t_lo + t1) * kTile, consume);
 
-    // acc[c][n][i] holds dimension (4*jg + i) * NT + n of query row 16c + rho.
+    // acc[c][n][i] holds dimension (4*jg + i) * NT + n of query row row0 + 16c + rho.
     const int d_base = 4 * jg * NT;
     const bool whole = t0 == 0 && t1 == nr;
     if (t0 == 0 && hg == 0 && threadIdx.x == 0) {
@@ -679,7 +689,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const float l_tot = l_sum[c];
-      const int row = 16 * c + rho;
+      const int row = row0 + 16 * c + rho;
       if (row >= nrows) continue;
       if (whole) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
@@ -804,12 +814,12 @@ inline hipError_t resident_of(const void* kernel, int threads, size_t lds,
 
 // Pass-1 workgroups at the largest LDS the kernel asks for. The context
 // walk's figure serves every mode, so all modes cut the batch the same way.
-template <bool BF16, int D, int NW, int NC>
+template <bool BF16, int D, int NW, int NC, int RH>
 hipError_t resident_workgroups(int* out) {
   static std::atomic<int> cache[kMaxDevices];
   return resident_of(
-      reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, kContextWalk, NC>), NW * 64,
-      decode_lds_bytes(kDecodeMaxSeqs), cache, out);
+      reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, kContextWalk, NC, RH>),
+      NW * RH * 64, decode_lds_bytes(kDecodeMaxSeqs), cache, out);
 }
 
 // Compute units of the current device, queried once per device.
@@ -834,15 +844,15 @@ inline hipError_t device_cus(int* out) {
 // workgroup (4 waves: measured 4-6% faster than two such workgroups per
 // unit, while two-head workgroups are fastest at four per unit), never more
 // than the workspace holds partials for.
-template <bool BF16, int D, int NW, int NC>
+template <bool BF16, int D, int NW, int NC, int RH>
 hipError_t slices_typed(const DecodeParams& p, int* slices) {
   const int HG = p.num_kv_heads / NW;
   int resident = 0, cus = 0;
-  hipError_t e = resident_workgroups<BF16, D, NW, NC>(&resident);
+  hipError_t e = resident_workgroups<BF16, D, NW, NC, RH>(&resident);
   if (e != hipSuccess) return e;
   e = device_cus(&cus);
   if (e != hipSuccess) return e;
-  const int cap = cus * (NW == 4 ? 1 : 8 / NW);
+  const int cap = cus * (RH == 1 && NW == 4 ? 1 : (NW * RH >= 8 ? 1 : 8 / (NW * RH)));
   const int wgs = resident < cap ? resident : cap;
   int s = wgs / HG > 1 ? wgs / HG : 1;
   if (s > p.max_slices) s = p.max_slices;
@@ -853,7 +863,7 @@ hipError_t slices_typed(const DecodeParams& p, int* slices) {
 // Pass 1 over p.slices slices (the caller's cut): the step's writes first
 // when they do not qualify for the append mode, then the kernel of the
 // walk mode.
-template <bool BF16, int D, int NW, int NC>
+template <bool BF16, int D, int NW, int NC, int RH>
 hipError_t pass1_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) {
   const int HG = p.num_kv_heads / NW;
   const dim3 grid((unsigned)p.slices * (unsigned)HG);
@@ -864,9 +874,9 @@ hipError_t pass1_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) 
     // workgroup's threads and the walk is the context walk; otherwise by
     // the fused slot-map + write kernel first.
     if (!(p.flags & kFlagWalkTable) && p.window == 0 && !p.kv_pos_offset && p.cp_world == 1 &&
-        p.app_max_tokens <= NW * 64) {
-      paged_decode_kernel<BF16, D, NW, kAppend, NC>
-          <<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+        p.app_max_tokens <= NW * RH * 64) {
+      paged_decode_kernel<BF16, D, NW, kAppend, NC, RH>
+          <<<grid, dim3(NW * RH * 64), lds, stream>>>(p, bs_shift);
       return hipGetLastError();
     }
     e = launch_slot_write(p.app_req, p.app_pos, p.app_tokens, p.app_max_tokens, p.block_table,
@@ -876,66 +886,68 @@ hipError_t pass1_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) 
     if (e != hipSuccess) return e;
   }
   if (p.flags & kFlagWalkTable)
-    paged_decode_kernel<BF16, D, NW, kTableWalk, NC>
-        <<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+    paged_decode_kernel<BF16, D, NW, kTableWalk, NC, RH>
+        <<<grid, dim3(NW * RH * 64), lds, stream>>>(p, bs_shift);
   else if (p.window > 0 || p.kv_pos_offset || p.cp_world > 1)
-    paged_decode_kernel<BF16, D, NW, kGeneral, NC>
-        <<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+    paged_decode_kernel<BF16, D, NW, kGeneral, NC, RH>
+        <<<grid, dim3(NW * RH * 64), lds, stream>>>(p, bs_shift);
   else
-    paged_decode_kernel<BF16, D, NW, kContextWalk, NC>
-        <<<grid, dim3(NW * 64), lds, stream>>>(p, bs_shift);
+    paged_decode_kernel<BF16, D, NW, kContextWalk, NC, RH>
+        <<<grid, dim3(NW * RH * 64), lds, stream>>>(p, bs_shift);
   return hipGetLastError();
 }
 
-// KV heads per workgroup: the largest of 8, 4, 2, 1 dividing Hkv (at most 4
-// at NC 4, whose waves run one per SIMD).
-template <bool BF16, int D, int NC>
+// KV heads per workgroup: the largest of 8, 4, 2, 1 dividing Hkv, at most
+// eight waves per workgroup.
+template <bool BF16, int D, int NC, int RH>
 hipError_t pass1_heads(const DecodeParams& p, int bs_shift, hipStream_t stream) {
   const int h = p.num_kv_heads;
-  if constexpr (NC < 4) {
-    if (h % 8 == 0) return pass1_typed<BF16, D, 8, NC>(p, bs_shift, stream);
+  if constexpr (RH == 1) {
+    if (h % 8 == 0) return pass1_typed<BF16, D, 8, NC, RH>(p, bs_shift, stream);
   }
-  if (h % 4 == 0) return pass1_typed<BF16, D, 4, NC>(p, bs_shift, stream);
-  if (h % 2 == 0) return pass1_typed<BF16, D, 2, NC>(p, bs_shift, stream);
-  return pass1_typed<BF16, D, 1, NC>(p, bs_shift, stream);
+  if (h % 4 == 0) return pass1_typed<BF16, D, 4, NC, RH>(p, bs_shift, stream);
+  if (h % 2 == 0) return pass1_typed<BF16, D, 2, NC, RH>(p, bs_shift, stream);
+  return pass1_typed<BF16, D, 1, NC, RH>(p, bs_shift, stream);
 }
 
-template <bool BF16, int D, int NC>
+template <bool BF16, int D, int NC, int RH>
 hipError_t slices_heads(const DecodeParams& p, int* slices) {
   const int h = p.num_kv_heads;
-  if constexpr (NC < 4) {
-    if (h % 8 == 0) return slices_typed<BF16, D, 8, NC>(p, slices);
+  if constexpr (RH == 1) {
+    if (h % 8 == 0) return slices_typed<BF16, D, 8, NC, RH>(p, slices);
   }
-  if (h % 4 == 0) return slices_typed<BF16, D, 4, NC>(p, slices);
-  if (h % 2 == 0) return slices_typed<BF16, D, 2, NC>(p, slices);
-  return slices_typed<BF16, D, 1, NC>(p, slices);
+  if (h % 4 == 0) return slices_typed<BF16, D, 4, NC, RH>(p, slices);
+  if (h % 2 == 0) return slices_typed<BF16, D, 2, NC, RH>(p, slices);
+  return slices_typed<BF16, D, 1, NC, RH>(p, slices);
 }
 
-template <int NC>
+// NC column tiles per wave, RH waves per KV head (16 NC RH query rows).
+template <int NC, int RH>
 hipError_t pass1_for(const DecodeParams& p, hipStream_t stream) {
   const int bs_shift = __builtin_ctz((unsigned)p.block_size);
   if (p.is_bf16) {
-    if (p.head_dim == 128) return pass1_heads<true, 128, NC>(p, bs_shift, stream);
-    return pass1_heads<true, 64, NC>(p, bs_shift, stream);
+    if (p.head_dim == 128) return pass1_heads<true, 128, NC, RH>(p, bs_shift, stream);
+    return pass1_heads<true, 64, NC, RH>(p, bs_shift, stream);
   }
-  if (p.head_dim == 128) return pass1_heads<false, 128, NC>(p, bs_shift, stream);
-  return pass1_heads<false, 64, NC>(p, bs_shift, stream);
+  if (p.head_dim == 128) return pass1_heads<false, 128, NC, RH>(p, bs_shift, stream);
+  return pass1_heads<false, 64, NC, RH>(p, bs_shift, stream);
 }
 
-template <int NC>
+template <int NC, int RH>
 hipError_t slices_for(const DecodeParams& p, int* slices) {
   if (p.is_bf16) {
-    if (p.head_dim == 128) return slices_heads<true, 128, NC>(p, slices);
-    return slices_heads<true, 64, NC>(p, slices);
+    if (p.head_dim == 128) return slices_heads<true, 128, NC, RH>(p, slices);
+    return slices_heads<true, 64, NC, RH>(p, slices);
   }
-  if (p.head_dim == 128) return slices_heads<false, 128, NC>(p, slices);
-  return slices_heads<false, 64, NC>(p, slices);
+  if (p.head_dim == 128) return slices_heads<false, 128, NC, RH>(p, slices);
+  return slices_heads<false, 64, NC, RH>(p, slices);
 }
 
 }  // namespace
 
-// Pass 1 (and the slices it cuts the batch into) at 16, 32 and 64 query
-// rows per KV head, one translation unit each (paged_decode.hip,
+// Pass 1 (and the slices it cuts the batch into) at up to 16, 32 and 64
+// query rows per KV head (one wave of one column tile, one wave of two, two
+// waves of two), one translation unit each (paged_decode.hip,
 // paged_decode_nc2.hip, paged_decode_nc4.hip).
 hipError_t decode_pass1_nc1(const DecodeParams& p, hipStream_t stream);
 hipError_t decode_pass1_nc2(const DecodeParams& p, hipStream_t stream);

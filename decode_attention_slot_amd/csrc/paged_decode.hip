@@ -265,10 +265,10 @@ hipError_t launch_merge_for(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t decode_pass1_nc1(const DecodeParams& p, hipStream_t stream) {
-  return pass1_for<1>(p, stream);
+  return pass1_for<1, 1>(p, stream);
 }
 
-hipError_t decode_slices_nc1(const DecodeParams& p, int* slices) { return slices_for<1>(p, slices); }
+hipError_t decode_slices_nc1(const DecodeParams& p, int* slices) { return slices_for<1, 1>(p, slices); }
 
 int32_t decode_max_slices(int32_t num_kv_heads) {
   // Partial storage for up to 8192 waves' worth of slices (a 256-CU part

@@ -6,11 +6,11 @@
 namespace kvs {
 
 hipError_t decode_pass1_nc2(const DecodeParams& p, hipStream_t stream) {
-  return pass1_for<2>(p, stream);
+  return pass1_for<2, 1>(p, stream);
 }
 
 hipError_t decode_slices_nc2(const DecodeParams& p, int* slices) {
-  return slices_for<2>(p, slices);
+  return slices_for<2, 1>(p, slices);
 }
 
 }  // namespace kvs

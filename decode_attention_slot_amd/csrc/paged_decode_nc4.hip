@@ -1,16 +1,17 @@
-// Pass 1 of the decode attention at 33-64 query rows per KV head (4 column
-// tiles of 16 rows per wave), in a translation unit of its own so that the
-// library's sources compile side by side. The kernel is in paged_decode.h.
+// Pass 1 of the decode attention at 33-64 query rows per KV head (two waves
+// per KV head, each with 2 column tiles of 16 rows), in a translation unit of
+// its own so that the library's sources compile side by side. The kernel is
+// in paged_decode.h.
 #include "paged_decode.h"
 
 namespace kvs {
 
 hipError_t decode_pass1_nc4(const DecodeParams& p, hipStream_t stream) {
-  return pass1_for<4>(p, stream);
+  return pass1_for<2, 2>(p, stream);
 }
 
 hipError_t decode_slices_nc4(const DecodeParams& p, int* slices) {
-  return slices_for<4>(p, slices);
+  return slices_for<2, 2>(p, slices);
 }
 
 }  // namespace kvs
