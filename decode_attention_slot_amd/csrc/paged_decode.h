@@ -52,11 +52,13 @@
 // * O^T = V^T P^T, per column tile. Lane l reads a 16-byte slice of the
 //   head rows of tokens 4 * (l / 16) .. + 3 (each 16-lane group reads whole
 //   256-byte head rows: V stays in its natural layout), and dimension column
-//   l % 16 of n-tile n is dimension (l % 16) * NT + n. bf16 KV: one
-//   v_mfma_f32_16x16x16_bf16 per n-tile takes the 16 tokens at once, its A
-//   operand packed from those slices with v_perm, its B operand P^T in bf16;
-//   P is split exactly into three bf16 terms (each the truncation of what
-//   the previous left), so the products equal those of fp32 P. fp32 KV:
+//   l % 16 of n-tile n is dimension (l % 16) * NT + n. bf16 KV: two
+//   v_mfma_f32_16x16x32_bf16 per n-tile take the 16 tokens at once, the A
+//   operand packed from those slices with v_perm (each token's value twice
+//   along the contraction), the B operand P^T in bf16: P is split exactly
+//   into three bf16 terms (each the truncation of what the previous left),
+//   (hi, mid) in the first and (lo, 0) in the second, so the products equal
+//   those of fp32 P. fp32 KV:
 //   v_mfma_f32_16x16x4f32, four tokens per step. The accumulator lands with
 //   query row 16 c + l % 16, matching the softmax state.
 // * A segment that holds a whole request writes its output. Otherwise its
@@ -624,38 +626,47 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 
       // O^T += V^T P^T
       if constexpr (BF16) {
-        // On v_mfma_f32_16x16x16_bf16, the whole tile at once: lane (jg, rho)
-        // gives A = V^T[dim column][tokens 4 jg .. 4 jg + 3] and B =
-        // P^T[those tokens][row 16 c + rho]. P is split into three bf16
-        // terms, each the top 8 significant bits of what the previous ones
-        // left (a truncation, so the remainder is exact): hi + mid + lo == p
-        // bit for bit, and the three products accumulate in fp32.
-        u32x2 pt[NC][3];
+        // The whole tile at once: lane (jg, rho) gives A = V^T[dim column]
+        // [tokens 4 jg .. 4 jg + 3] and B = P^T[those tokens][row 16 c + rho].
+        // P is split into three bf16 terms, each the top 8 significant bits of
+        // what the previous ones left (a truncation, so the remainder is
+        // exact): hi + mid + lo == p bit for bit. Two v_mfma_f32_16x16x32_bf16
+        // take them, each contraction running over the lane's four tokens
+        // twice (A repeats the four values): B = (hi, mid), then (lo, 0); the
+        // products accumulate in fp32. (Only this one MFMA kind touches the
+        // accumulator: a 16x16x16 step chained to a 16x16x32 one on the same
+        // accumulator got too few wait states from the compiler and read a
+        // stale accumulator.)
+        u32x4 pt_hm[NC], pt_l0[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           float rem[4] = {pr4[c][0], pr4[c][1], pr4[c][2], pr4[c][3]};
+          u32x2 pt[3];
 #pragma unroll
           for (int term = 0; term < 3; ++term) {
-            pt[c][term] = (u32x2){bf16_pair_hi(rem[0], rem[1]), bf16_pair_hi(rem[2], rem[3])};
+            pt[term] = (u32x2){bf16_pair_hi(rem[0], rem[1]), bf16_pair_hi(rem[2], rem[3])};
 #pragma unroll
             for (int t = 0; t < 4; ++t)
               rem[t] -= __uint_as_float(__float_as_uint(rem[t]) & 0xffff0000u);
           }
+          pt_hm[c] = (u32x4){pt[0][0], pt[0][1], pt[1][0], pt[1][1]};
+          pt_l0[c] = (u32x4){pt[2][0], pt[2][1], 0u, 0u};
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           // dimension column rho of n-tile n is dimension rho * NT + n: the
           // low or high half of dword n / 2 of each token's 16-byte slice
           const uint32_t sel = (n & 1) ? kPermHi : kPermLo;
-          const u32x2 a = {__builtin_amdgcn_perm(bf.v[1][n >> 1], bf.v[0][n >> 1], sel),
-                           __builtin_amdgcn_perm(bf.v[3][n >> 1], bf.v[2][n >> 1], sel)};
+          const uint32_t a01 = __builtin_amdgcn_perm(bf.v[1][n >> 1], bf.v[0][n >> 1], sel);
+          const uint32_t a23 = __builtin_amdgcn_perm(bf.v[3][n >> 1], bf.v[2][n >> 1], sel);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, (u32x4){a01, a23, a01, a23});
 #pragma unroll
-          for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int term = 0; term < 3; ++term)
-              acc[c][n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                  __builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, pt[c][term]),
-                  acc[c][n], 0, 0, 0);
+          for (int c = 0; c < NC; ++c) {
+            acc[c][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, __builtin_bit_cast(bf16x8, pt_hm[c]), acc[c][n], 0, 0, 0);
+            acc[c][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, __builtin_bit_cast(bf16x8, pt_l0[c]), acc[c][n], 0, 0, 0);
+          }
         }
       } else {
         // fp32 values on v_mfma_f32_16x16x4f32, four tokens per step: lane
