@@ -541,8 +541,10 @@ def main(argv=None) -> int:
                  "tokens_per_s": round(nt / t_big, 1),
                  "gbps": round(slot_map_bytes(nt) / t_big / 1e9, 2),
                  "frac_of_peak": round(slot_map_bytes(nt) / t_big / 1e9 / HBM_PEAK_GBPS, 4),
-                 "note": "24 B per token counted; the table entries (4 of them) are mostly "
-                         "cache hits, the token and slot arrays stream from HBM"}
+                 "note": "24 B per token counted; requests and positions drawn at random, so "
+                         "every table read is a scattered cache-line fetch (the worst case; a "
+                         "step's tokens are grouped by request); the token and slot arrays "
+                         "stream from HBM"}
         del sets
 
     if args.copy_probe_mib:
