@@ -135,7 +135,7 @@ int decode_common(const void* q, const void* k_cache, const void* v_cache,
   p.cp_ishift = __builtin_ctz((unsigned)cp_interleave);
   p.max_slices = kvs::decode_max_slices(num_kv_heads);
   p.min_tiles = 8;  // 128 tokens: partial traffic stays a few percent of the KV a slice reads
-  p.start_tiles = 2;  // a segment start costs about two tiles' streaming time
+  p.start_tiles = 2;  // a segment start costs about two tile steps of streaming
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
   p.flags = flags;
   p.is_bf16 = dtype == KVS_BF16;

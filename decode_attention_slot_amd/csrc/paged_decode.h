@@ -22,9 +22,14 @@
 //   workgroup streams the same number of bytes and all finish together (no
 //   rounds, no tail of short units). A
 //   range may start or end inside a request and may span requests; each
-//   (slice, request) piece is a segment. One wavefront per KV head; a
-//   workgroup holds the waves of NW KV heads, so the [block][token][head]
-//   rows it reads are contiguous in HBM.
+//   (slice, request) piece is a segment. A workgroup holds the waves of NW
+//   KV heads (their [block][token][head] rows are adjacent in HBM); a head
+//   has one wave, or (up to 16 query rows, bf16) WS waves that split its
+//   tiles round robin by absolute tile index, each with a softmax state of
+//   its own, pooled through LDS and merged in wave order at the segment's
+//   end. Two heads of four waves each stream faster than eight heads of one
+//   (the workgroup has four tiles in flight per head instead of one) and cut
+//   the batch into a quarter as many slices, so fewer partial states.
 // * The cut is made on the device from seq_lens (no host synchronisation):
 //   every workgroup scans the batch's tile counts into an LDS prefix. It
 //   depends only on the visible context lengths and the device, so a
@@ -209,9 +214,13 @@ __device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
 // holding 16 NC consecutive rows of the head's (Hq / Hkv) * q_len rows (at
 // most 16 NC RH). The waves of one head read the same K and V tiles (the
 // second read hits in cache); the head's accumulators are split between
-// them. Waves of a workgroup: NW KV heads times RH, head-major in each half.
-template <bool BF16, int D, int NW, int MODE, int NC, int RH>
-__global__ void __launch_bounds__(NW * RH * 64, 2)
+// them. WS: waves per KV head that split the tiles instead (wave s of the
+// head takes the tiles whose absolute index is s mod WS, each keeping its own
+// softmax state for all the head's rows; at the end of a segment the WS
+// states are merged through LDS in a fixed tree). RH and WS are not combined.
+// Waves of a workgroup: NW KV heads times RH (or WS), head-major.
+template <bool BF16, int D, int NW, int MODE, int NC, int RH, int WS>
+__global__ void __launch_bounds__(NW * RH * WS * 64, 2)
 paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int ES = BF16 ? 2 : 4;       // bytes per element
   constexpr int EP = 16 / ES;            // elements per 16-byte piece
@@ -219,13 +228,15 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr int NT = D / 16;             // P.V n-tiles (dimension columns of 16)
   constexpr int NVW = NT * ES / 4;       // V dwords per lane per token
   constexpr int PSTRIDE = D + 4;         // floats per partial row (acc, m, l, pad)
-  constexpr int NTHR = NW * RH * 64;
-  constexpr int NWAVES = NW * RH;
+  constexpr int NTHR = NW * RH * WS * 64;
+  constexpr int NWAVES = NW * RH * WS;
   constexpr bool TW = MODE == kTableWalk;
   constexpr bool GEN = MODE == kGeneral;
   constexpr bool APP = MODE == kAppend;
   constexpr uint32_t kNegZero = BF16 ? 0x80008000u : 0x80000000u;
   static_assert(NP >= 1 && NVW >= 2, "unsupported head_dim");
+  static_assert(RH == 1 || WS == 1, "row split and tile split are not combined");
+  static_assert(WS == 1 || WS == 2 || WS == 4 || WS == 8, "WS: a power of two up to 8");
   struct TileBuf {
     u32x4 k[NP];         // K pieces of token rho of the tile
     uint32_t v[4][NVW];  // V slices of tokens 4*jg .. 4*jg+3
@@ -241,6 +252,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // request holding this slice's first unit (context), first padding tile,
   // and the context tiles of the requests before the latter
   __shared__ int s_first[3];
+  // the tile split's pool: every wave's state at a segment's end, per lane
+  constexpr int NPOOL = WS > 1 ? NWAVES * NC * 64 : 1;
+  __shared__ f32x4 s_pool[WS > 1 ? NPOOL * NT : 1];
+  __shared__ float s_pm[NPOOL], s_pl[NPOOL];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -261,7 +276,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   const int slice = blockIdx.x / HG;
   const int hg = blockIdx.x - slice * HG;
   const int g = hg * NW + wave % NW;  // this wave's KV head
-  const int row0 = 16 * NC * (wave / NW);  // its first query row of that head
+  const int row0 = RH > 1 ? 16 * NC * (wave / NW) : 0;  // its first query row of that head
+  const int ws = WS > 1 ? wave / NW : 0;  // its share of the head's tiles
   const int64_t block_bytes = ((int64_t)Hkv * D * ES) << bs_shift;
   const uint32_t row_bytes = (uint32_t)(Hkv * D * ES);
 
@@ -269,10 +285,12 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // The context tiles of all requests, laid end to end, are cut into S equal
   // ranges, one per slice; a slice's range may start or end inside a
   // request and may cover several requests. Its pieces are the segments.
-  // Each request with context also counts start_tiles units ahead of its
+  // Each request with context also counts X units ahead of its
   // tiles (the cost of starting a segment), so a slice that starts a
   // request carries that many fewer tiles. s_pref holds these units.
-  const int X = p.start_tiles;
+  // (start_tiles is the cost in steps of a wave; a workgroup whose waves split
+  // each head's tiles takes WS tiles per step)
+  const int X = p.start_tiles * WS;
   // The first request of this thread's share is loaded here, before the
   // append's token loads, so that waiting for it does not wait for them.
   const int len0 = (int)threadIdx.x < B ? p.seq_lens[threadIdx.x] : 0;
@@ -412,7 +430,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       }
     }
     if (n_own > 0) __builtin_amdgcn_s_waitcnt(0);  // this wave's stores land before its loads
-    if constexpr (RH > 1) {
+    if constexpr (RH > 1 || WS > 1) {
       if (n_own > 0) __syncthreads();  // and before the other waves of its head load them
     }
   }
@@ -432,7 +450,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     const int blk_end = ((tok_b - 1 - off) >> bs_shift) + 1;
     for (int pb = blk_first; pb < blk_end; pb += kStage) {
       const int pn = min(kStage, blk_end - pb);
-      __syncthreads();  // the previous piece is consumed by every wave
+      __syncthreads();  // the previous piece (and segment's pooled states) is consumed
       for (int i = threadIdx.x; i < pn; i += NTHR) {
         const int col = pb + i;
         s_blk[i] = col < p.table_stride ? trow[col] : 0;
@@ -481,11 +499,21 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
           }
         }
       };
+      // This wave's tiles of the piece: those whose absolute tile index is ws
+      // mod WS (all of them when WS = 1), t_first, t_first + WS, ..., nw of
+      // them. Every wave of the workgroup runs the same number of steps (the
+      // barrier below), loading past its last tile (or the piece's first tile
+      // when it has none) where it has no tile.
+      const int t_first = WS > 1 ? (ws - (t_begin >> 4)) & (WS - 1) : 0;
+      const int nw = WS > 1 ? (nt > t_first ? (nt - t_first + WS - 1) / WS : 0) : nt;
+      const int steps = WS > 1 ? (nt + WS - 1) / WS : nt;
       TileBuf bufs[kDepth];
-      auto tile_at = [&](int t) { return t_begin + min(t, nt - 1) * kTile; };
+      auto tile_at = [&](int u) {
+        return t_begin + (nw > 0 ? t_first + min(u, nw - 1) * WS : 0) * kTile;
+      };
 #pragma unroll
-      for (int s = 0; s < kDepth - 1; ++s) load(tile_at(s), bufs[s], s >= nt);
-      for (int t = 0; t < nt; t += kDepth) {
+      for (int s = 0; s < kDepth - 1; ++s) load(tile_at(s), bufs[s], s >= nw);
+      for (int t = 0; t < steps; t += kDepth) {
         // Keep the workgroup's waves in step (every wave walks the same
         // tiles, for its own KV head). Two waves share each SIMD, and the
         // older one wins issue arbitration; left alone it runs ahead and the
@@ -496,8 +524,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 #pragma unroll
         for (int s = 0; s < kDepth; ++s) {
           load(tile_at(t + s + kDepth - 1), bufs[(s + kDepth - 1) % kDepth],
-               t + s + kDepth - 1 >= nt);
-          if (t + s < nt) fn(t_begin + (t + s) * kTile, bufs[s]);
+               t + s + kDepth - 1 >= nw);
+          if (t + s < nw) fn(t_begin + (t_first + (t + s) * WS) * kTile, bufs[s]);
         }
       }
     }
@@ -686,6 +714,63 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
                   (t_lo + t1) * kTile, consume);
 
     // acc[c][n][i] holds dimension (4*jg + i) * NT + n of query row row0 + 16c + rho.
+    // Its float4 k = i * NT / 4 + n0 / 4 gathers n-tiles n0 .. n0 + 3 of
+    // component i: dimensions d_base + i * NT + n0 .. + 3 of the row.
+    auto own_vec = [&](int c, int k) -> f32x4 {
+      const int i = k / (NT / 4), n0 = (k % (NT / 4)) * 4;
+      return (f32x4){acc[c][n0][i], acc[c][n0 + 1][i], acc[c][n0 + 2][i], acc[c][n0 + 3][i]};
+    };
+    // Tile split: the WS waves of a head pool their states in LDS. The merged
+    // state has the largest of their maxima; each wave's state enters it
+    // scaled by 2^(its max - that max), summed in wave order 0 .. WS-1. Every
+    // wave computes the merged (m, l) and the float4s k with k mod WS == ws.
+    const int hw = wave % NW;
+    float sc[NC][WS];
+    if constexpr (WS > 1) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int at = (hw * WS + ws) * NC + c;
+        s_pm[at * 64 + lane] = m_run[c];
+        s_pl[at * 64 + lane] = l_run[c];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) s_pool[(at * NT + k) * 64 + lane] = own_vec(c, k);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float ms[WS], mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WS; ++w) {
+          ms[w] = s_pm[((hw * WS + w) * NC + c) * 64 + lane];
+          mx = fmaxf(mx, ms[w]);
+        }
+        const float mu = mx == -INFINITY ? 0.0f : mx;  // no wave saw a key
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WS; ++w) {
+          sc[c][w] = __builtin_amdgcn_exp2f(ms[w] - mu);
+          l = __builtin_fmaf(s_pl[((hw * WS + w) * NC + c) * 64 + lane], sc[c][w], l);
+        }
+        m_run[c] = mx;
+        l_run[c] = l;
+      }
+    }
+    auto vec = [&](int c, int k) -> f32x4 {
+      if constexpr (WS == 1) {
+        return own_vec(c, k);
+      } else {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < WS; ++w) {
+          const f32x4 o = s_pool[(((hw * WS + w) * NC + c) * NT + k) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(o[e], sc[c][w], v[e]);
+        }
+        return v;
+      }
+    };
+    auto mine = [&](int k) { return WS == 1 || k % WS == ws; };
+
     const int d_base = 4 * jg * NT;
     const bool whole = t0 == 0 && t1 == nr;
     if (t0 == 0 && hg == 0 && threadIdx.x == 0) {
@@ -707,35 +792,27 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         float* o =
             p.out + (((int64_t)r * Sq + jrow[c]) * Hq + (int64_t)g * G + hh[c]) * D + d_base;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int n0 = 0; n0 < NT; n0 += 4) {
-            f32x4 v = {acc[c][n0][i] * inv, acc[c][n0 + 1][i] * inv, acc[c][n0 + 2][i] * inv,
-                       acc[c][n0 + 3][i] * inv};
-            *(f32x4*)(o + i * NT + n0) = v;
-          }
+        for (int k = 0; k < NT; ++k) {
+          if (!mine(k)) continue;
+          const int i = k / (NT / 4), n0 = (k % (NT / 4)) * 4;
+          *(f32x4*)(o + i * NT + n0) = vec(c, k) * inv;
         }
-        if (p.lse_out && jg == 0)
+        if (p.lse_out && jg == 0 && ws == 0)
           p.lse_out[((int64_t)r * Sq + jrow[c]) * Hq + (int64_t)g * G + hh[c]] =
               row_lse(m_run[c], l_tot);
         continue;
       }
       // split: publish this segment's partial state, in store order: float4
-      // k = i * NT / 4 + n0 / 4 of lane (jg, row) sits at float4 index
-      // (k * 4 + jg) * nrows + row of the slot, so each store writes
-      // contiguous runs of 16 rows (a row-major layout would put each lane's
-      // 16 bytes in a different cache line); (m, l) of the rows follow all
-      // the float4s.
+      // k of lane (jg, row) sits at float4 index (k * 4 + jg) * nrows + row of
+      // the slot, so each store writes contiguous runs of 16 rows (a row-major
+      // layout would put each lane's 16 bytes in a different cache line);
+      // (m, l) of the rows follow all the float4s.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int n0 = 0; n0 < NT; n0 += 4) {
-          const int k = i * (NT / 4) + n0 / 4;
-          f32x4 v = {acc[c][n0][i], acc[c][n0 + 1][i], acc[c][n0 + 2][i], acc[c][n0 + 3][i]};
-          *(f32x4*)(pslot + ((k * 4 + jg) * nrows + row) * 4) = v;
-        }
+      for (int k = 0; k < NT; ++k) {
+        if (!mine(k)) continue;
+        *(f32x4*)(pslot + ((k * 4 + jg) * nrows + row) * 4) = vec(c, k);
       }
-      if (jg == 0) *(f32x2*)(pslot + nrows * D + 2 * row) = (f32x2){m_run[c], l_tot};
+      if (jg == 0 && ws == 0) *(f32x2*)(pslot + nrows * D + 2 * row) = (f32x2){m_run[c], l_tot};
     }
   };
 
@@ -825,12 +902,12 @@ inline hipError_t resident_of(const void* kernel, int threads, size_t lds,
 
 // Pass-1 workgroups at the largest LDS the kernel asks for. The context
 // walk's figure serves every mode, so all modes cut the batch the same way.
-template <bool BF16, int D, int NW, int NC, int RH>
+template <bool BF16, int D, int NW, int NC, int RH, int WS>
 hipError_t resident_workgroups(int* out) {
   static std::atomic<int> cache[kMaxDevices];
   return resident_of(
-      reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, kContextWalk, NC, RH>),
-      NW * RH * 64, decode_lds_bytes(kDecodeMaxSeqs), cache, out);
+      reinterpret_cast<const void*>(&paged_decode_kernel<BF16, D, NW, kContextWalk, NC, RH, WS>),
+      NW * RH * WS * 64, decode_lds_bytes(kDecodeMaxSeqs), cache, out);
 }
 
 // Compute units of the current device, queried once per device.
@@ -855,15 +932,16 @@ inline hipError_t device_cus(int* out) {
 // workgroup (4 waves: measured 4-6% faster than two such workgroups per
 // unit, while two-head workgroups are fastest at four per unit), never more
 // than the workspace holds partials for.
-template <bool BF16, int D, int NW, int NC, int RH>
+template <bool BF16, int D, int NW, int NC, int RH, int WS>
 hipError_t slices_typed(const DecodeParams& p, int* slices) {
+  constexpr int waves = NW * RH * WS;
   const int HG = p.num_kv_heads / NW;
   int resident = 0, cus = 0;
-  hipError_t e = resident_workgroups<BF16, D, NW, NC, RH>(&resident);
+  hipError_t e = resident_workgroups<BF16, D, NW, NC, RH, WS>(&resident);
   if (e != hipSuccess) return e;
   e = device_cus(&cus);
   if (e != hipSuccess) return e;
-  const int cap = cus * (RH == 1 && NW == 4 ? 1 : (NW * RH >= 8 ? 1 : 8 / (NW * RH)));
+  const int cap = cus * (NW == 4 && RH == 1 && WS == 1 ? 1 : (waves >= 8 ? 1 : 8 / waves));
   const int wgs = resident < cap ? resident : cap;
   int s = wgs / HG > 1 ? wgs / HG : 1;
   if (s > p.max_slices) s = p.max_slices;
@@ -874,8 +952,9 @@ hipError_t slices_typed(const DecodeParams& p, int* slices) {
 // Pass 1 over p.slices slices (the caller's cut): the step's writes first
 // when they do not qualify for the append mode, then the kernel of the
 // walk mode.
-template <bool BF16, int D, int NW, int NC, int RH>
+template <bool BF16, int D, int NW, int NC, int RH, int WS>
 hipError_t pass1_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) {
+  constexpr int NTHR = NW * RH * WS * 64;
   const int HG = p.num_kv_heads / NW;
   const dim3 grid((unsigned)p.slices * (unsigned)HG);
   const size_t lds = decode_lds_bytes(p.num_seqs);
@@ -885,9 +964,9 @@ hipError_t pass1_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) 
     // workgroup's threads and the walk is the context walk; otherwise by
     // the fused slot-map + write kernel first.
     if (!(p.flags & kFlagWalkTable) && p.window == 0 && !p.kv_pos_offset && p.cp_world == 1 &&
-        p.app_max_tokens <= NW * RH * 64) {
-      paged_decode_kernel<BF16, D, NW, kAppend, NC, RH>
-          <<<grid, dim3(NW * RH * 64), lds, stream>>>(p, bs_shift);
+        p.app_max_tokens <= NTHR) {
+      paged_decode_kernel<BF16, D, NW, kAppend, NC, RH, WS>
+          <<<grid, dim3(NTHR), lds, stream>>>(p, bs_shift);
       return hipGetLastError();
     }
     e = launch_slot_write(p.app_req, p.app_pos, p.app_tokens, p.app_max_tokens, p.block_table,
@@ -897,39 +976,61 @@ hipError_t pass1_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) 
     if (e != hipSuccess) return e;
   }
   if (p.flags & kFlagWalkTable)
-    paged_decode_kernel<BF16, D, NW, kTableWalk, NC, RH>
-        <<<grid, dim3(NW * RH * 64), lds, stream>>>(p, bs_shift);
+    paged_decode_kernel<BF16, D, NW, kTableWalk, NC, RH, WS>
+        <<<grid, dim3(NTHR), lds, stream>>>(p, bs_shift);
   else if (p.window > 0 || p.kv_pos_offset || p.cp_world > 1)
-    paged_decode_kernel<BF16, D, NW, kGeneral, NC, RH>
-        <<<grid, dim3(NW * RH * 64), lds, stream>>>(p, bs_shift);
+    paged_decode_kernel<BF16, D, NW, kGeneral, NC, RH, WS>
+        <<<grid, dim3(NTHR), lds, stream>>>(p, bs_shift);
   else
-    paged_decode_kernel<BF16, D, NW, kContextWalk, NC, RH>
-        <<<grid, dim3(NW * RH * 64), lds, stream>>>(p, bs_shift);
+    paged_decode_kernel<BF16, D, NW, kContextWalk, NC, RH, WS>
+        <<<grid, dim3(NTHR), lds, stream>>>(p, bs_shift);
   return hipGetLastError();
 }
 
-// KV heads per workgroup: the largest of 8, 4, 2, 1 dividing Hkv, at most
-// eight waves per workgroup.
+// Up to 16 rows per KV head (one column tile) of a bf16 cache: workgroups of
+// eight waves, two KV heads with four waves each splitting the tiles (one
+// head with eight when Hkv is odd). Measured against one wave per head and
+// eight heads per workgroup: the 256-request batch 656 vs 682 us, the 64
+// ragged requests 352 vs 371 us, bucketing 63.9 vs 66.1 us, the 4-rank
+// context-parallel share 197 vs 205 us, the 12-request batch 31.9 vs 30.9 us;
+// four heads of two waves each were no faster than eight of one.
+// Otherwise: one wave per head for the rows of up to 32 (RH = 1) and the
+// largest of 8, 4, 2, 1 heads dividing Hkv; two per head for up to 64 rows
+// (RH = 2, at most four heads). (At two column tiles, and with fp32 values,
+// the pooled merge's registers would spill.)
+template <bool BF16, int NC, int RH>
+constexpr bool tile_split = BF16 && RH == 1 && NC == 1;
+
 template <bool BF16, int D, int NC, int RH>
 hipError_t pass1_heads(const DecodeParams& p, int bs_shift, hipStream_t stream) {
   const int h = p.num_kv_heads;
-  if constexpr (RH == 1) {
-    if (h % 8 == 0) return pass1_typed<BF16, D, 8, NC, RH>(p, bs_shift, stream);
+  if constexpr (tile_split<BF16, NC, RH>) {
+    if (h % 2 == 0) return pass1_typed<BF16, D, 2, NC, RH, 4>(p, bs_shift, stream);
+    return pass1_typed<BF16, D, 1, NC, RH, 8>(p, bs_shift, stream);
+  } else {
+    if constexpr (RH == 1) {
+      if (h % 8 == 0) return pass1_typed<BF16, D, 8, NC, RH, 1>(p, bs_shift, stream);
+    }
+    if (h % 4 == 0) return pass1_typed<BF16, D, 4, NC, RH, 1>(p, bs_shift, stream);
+    if (h % 2 == 0) return pass1_typed<BF16, D, 2, NC, RH, 1>(p, bs_shift, stream);
+    return pass1_typed<BF16, D, 1, NC, RH, 1>(p, bs_shift, stream);
   }
-  if (h % 4 == 0) return pass1_typed<BF16, D, 4, NC, RH>(p, bs_shift, stream);
-  if (h % 2 == 0) return pass1_typed<BF16, D, 2, NC, RH>(p, bs_shift, stream);
-  return pass1_typed<BF16, D, 1, NC, RH>(p, bs_shift, stream);
 }
 
 template <bool BF16, int D, int NC, int RH>
 hipError_t slices_heads(const DecodeParams& p, int* slices) {
   const int h = p.num_kv_heads;
-  if constexpr (RH == 1) {
-    if (h % 8 == 0) return slices_typed<BF16, D, 8, NC, RH>(p, slices);
+  if constexpr (tile_split<BF16, NC, RH>) {
+    if (h % 2 == 0) return slices_typed<BF16, D, 2, NC, RH, 4>(p, slices);
+    return slices_typed<BF16, D, 1, NC, RH, 8>(p, slices);
+  } else {
+    if constexpr (RH == 1) {
+      if (h % 8 == 0) return slices_typed<BF16, D, 8, NC, RH, 1>(p, slices);
+    }
+    if (h % 4 == 0) return slices_typed<BF16, D, 4, NC, RH, 1>(p, slices);
+    if (h % 2 == 0) return slices_typed<BF16, D, 2, NC, RH, 1>(p, slices);
+    return slices_typed<BF16, D, 1, NC, RH, 1>(p, slices);
   }
-  if (h % 4 == 0) return slices_typed<BF16, D, 4, NC, RH>(p, slices);
-  if (h % 2 == 0) return slices_typed<BF16, D, 2, NC, RH>(p, slices);
-  return slices_typed<BF16, D, 1, NC, RH>(p, slices);
 }
 
 // NC column tiles per wave, RH waves per KV head (16 NC RH query rows).
