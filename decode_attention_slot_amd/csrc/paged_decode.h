@@ -214,11 +214,11 @@ __device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
 // holding 16 NC consecutive rows of the head's (Hq / Hkv) * q_len rows (at
 // most 16 NC RH). The waves of one head read the same K and V tiles (the
 // second read hits in cache); the head's accumulators are split between
-// them. WS: waves per KV head that split the tiles instead (wave s of the
-// head takes the tiles whose absolute index is s mod WS, each keeping its own
-// softmax state for all the head's rows; at the end of a segment the WS
-// states are merged through LDS in a fixed tree). RH and WS are not combined.
-// Waves of a workgroup: NW KV heads times RH (or WS), head-major.
+// them. WS: waves that split the tiles of a head (and row group): wave s
+// takes the tiles whose absolute index is s mod WS, keeping its own softmax
+// state for its rows; at the end of a segment the WS states are pooled in LDS
+// and merged in wave order. Waves of a workgroup: NW KV heads times RH times
+// WS, the head fastest.
 template <bool BF16, int D, int NW, int MODE, int NC, int RH, int WS>
 __global__ void __launch_bounds__(NW * RH * WS * 64, 2)
 paged_decode_kernel(const DecodeParams p, int bs_shift) {
@@ -235,7 +235,6 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr bool APP = MODE == kAppend;
   constexpr uint32_t kNegZero = BF16 ? 0x80008000u : 0x80000000u;
   static_assert(NP >= 1 && NVW >= 2, "unsupported head_dim");
-  static_assert(RH == 1 || WS == 1, "row split and tile split are not combined");
   static_assert(WS == 1 || WS == 2 || WS == 4 || WS == 8, "WS: a power of two up to 8");
   struct TileBuf {
     u32x4 k[NP];         // K pieces of token rho of the tile
@@ -252,8 +251,9 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // request holding this slice's first unit (context), first padding tile,
   // and the context tiles of the requests before the latter
   __shared__ int s_first[3];
-  // the tile split's pool: every wave's state at a segment's end, per lane
-  constexpr int NPOOL = WS > 1 ? NWAVES * NC * 64 : 1;
+  // the tile split's pool: every wave's state of one column tile at a
+  // segment's end, per lane
+  constexpr int NPOOL = WS > 1 ? NWAVES * 64 : 1;
   __shared__ f32x4 s_pool[WS > 1 ? NPOOL * NT : 1];
   __shared__ float s_pm[NPOOL], s_pl[NPOOL];
 
@@ -276,8 +276,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   const int slice = blockIdx.x / HG;
   const int hg = blockIdx.x - slice * HG;
   const int g = hg * NW + wave % NW;  // this wave's KV head
-  const int row0 = RH > 1 ? 16 * NC * (wave / NW) : 0;  // its first query row of that head
-  const int ws = WS > 1 ? wave / NW : 0;  // its share of the head's tiles
+  // waves: head in group fastest, then row group, then tile share
+  const int rh = RH > 1 ? (wave / NW) % RH : 0;
+  const int row0 = 16 * NC * rh;                // its first query row of that head
+  const int ws = WS > 1 ? wave / (NW * RH) : 0;  // its share of the head's tiles
   const int64_t block_bytes = ((int64_t)Hkv * D * ES) << bs_shift;
   const uint32_t row_bytes = (uint32_t)(Hkv * D * ES);
 
@@ -720,57 +722,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       const int i = k / (NT / 4), n0 = (k % (NT / 4)) * 4;
       return (f32x4){acc[c][n0][i], acc[c][n0 + 1][i], acc[c][n0 + 2][i], acc[c][n0 + 3][i]};
     };
-    // Tile split: the WS waves of a head pool their states in LDS. The merged
-    // state has the largest of their maxima; each wave's state enters it
-    // scaled by 2^(its max - that max), summed in wave order 0 .. WS-1. Every
-    // wave computes the merged (m, l) and the float4s k with k mod WS == ws.
-    const int hw = wave % NW;
-    float sc[NC][WS];
-    if constexpr (WS > 1) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int at = (hw * WS + ws) * NC + c;
-        s_pm[at * 64 + lane] = m_run[c];
-        s_pl[at * 64 + lane] = l_run[c];
-#pragma unroll
-        for (int k = 0; k < NT; ++k) s_pool[(at * NT + k) * 64 + lane] = own_vec(c, k);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        float ms[WS], mx = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < WS; ++w) {
-          ms[w] = s_pm[((hw * WS + w) * NC + c) * 64 + lane];
-          mx = fmaxf(mx, ms[w]);
-        }
-        const float mu = mx == -INFINITY ? 0.0f : mx;  // no wave saw a key
-        float l = 0.0f;
-#pragma unroll
-        for (int w = 0; w < WS; ++w) {
-          sc[c][w] = __builtin_amdgcn_exp2f(ms[w] - mu);
-          l = __builtin_fmaf(s_pl[((hw * WS + w) * NC + c) * 64 + lane], sc[c][w], l);
-        }
-        m_run[c] = mx;
-        l_run[c] = l;
-      }
-    }
-    auto vec = [&](int c, int k) -> f32x4 {
-      if constexpr (WS == 1) {
-        return own_vec(c, k);
-      } else {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < WS; ++w) {
-          const f32x4 o = s_pool[(((hw * WS + w) * NC + c) * NT + k) * 64 + lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(o[e], sc[c][w], v[e]);
-        }
-        return v;
-      }
-    };
+    const int grp = (wave % NW) * RH + rh;  // the WS waves holding these rows
     auto mine = [&](int k) { return WS == 1 || k % WS == ws; };
-
     const int d_base = 4 * jg * NT;
     const bool whole = t0 == 0 && t1 == nr;
     if (t0 == 0 && hg == 0 && threadIdx.x == 0) {
@@ -779,15 +732,55 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       p.chunk_meta[2 * r + 1] = whole ? 1 : (pr + nr - 1) / Q - slice + 1;
     }
     float* pslot = p.partials + (((int64_t)slice + r) * Hkv + g) * nrows * PSTRIDE;
-    float l_sum[NC];  // whole-wave sums first: the stores below are per lane
-#pragma unroll
-    for (int c = 0; c < NC; ++c) l_sum[c] = sum_over_groups(l_run[c]);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const float l_tot = l_sum[c];
+      // Tile split: the WS waves of a head pool their states of column tile c
+      // in LDS. The merged state has the largest of their maxima; each wave's
+      // state enters it scaled by 2^(its max - that max), summed in wave order
+      // 0 .. WS-1. Every wave computes the merged (m, l) and the float4s k
+      // with k mod WS == ws.
+      float sc[WS];
+      if constexpr (WS > 1) {
+        if (c > 0) __syncthreads();  // the previous column tile's pool is read
+        const int at = grp * WS + ws;
+        s_pm[at * 64 + lane] = m_run[c];
+        s_pl[at * 64 + lane] = l_run[c];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) s_pool[(at * NT + k) * 64 + lane] = own_vec(c, k);
+        __syncthreads();
+        float ms[WS], mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WS; ++w) {
+          ms[w] = s_pm[(grp * WS + w) * 64 + lane];
+          mx = fmaxf(mx, ms[w]);
+        }
+        const float mu = mx == -INFINITY ? 0.0f : mx;  // no wave saw a key
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WS; ++w) {
+          sc[w] = __builtin_amdgcn_exp2f(ms[w] - mu);
+          l = __builtin_fmaf(s_pl[(grp * WS + w) * 64 + lane], sc[w], l);
+        }
+        m_run[c] = mx;
+        l_run[c] = l;
+      }
+      auto vec = [&](int k) -> f32x4 {
+        if constexpr (WS == 1) {
+          return own_vec(c, k);
+        } else {
+          f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int w = 0; w < WS; ++w) {
+            const f32x4 o = s_pool[((grp * WS + w) * NT + k) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(o[e], sc[w], v[e]);
+          }
+          return v;
+        }
+      };
+      const float l_tot = sum_over_groups(l_run[c]);  // whole-wave sum: every lane takes part
       const int row = row0 + 16 * c + rho;
-      if (row >= nrows) continue;
-      if (whole) {
+      if (row < nrows && whole) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         float* o =
             p.out + (((int64_t)r * Sq + jrow[c]) * Hq + (int64_t)g * G + hh[c]) * D + d_base;
@@ -795,24 +788,24 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         for (int k = 0; k < NT; ++k) {
           if (!mine(k)) continue;
           const int i = k / (NT / 4), n0 = (k % (NT / 4)) * 4;
-          *(f32x4*)(o + i * NT + n0) = vec(c, k) * inv;
+          *(f32x4*)(o + i * NT + n0) = vec(k) * inv;
         }
         if (p.lse_out && jg == 0 && ws == 0)
           p.lse_out[((int64_t)r * Sq + jrow[c]) * Hq + (int64_t)g * G + hh[c]] =
               row_lse(m_run[c], l_tot);
-        continue;
-      }
-      // split: publish this segment's partial state, in store order: float4
-      // k of lane (jg, row) sits at float4 index (k * 4 + jg) * nrows + row of
-      // the slot, so each store writes contiguous runs of 16 rows (a row-major
-      // layout would put each lane's 16 bytes in a different cache line);
-      // (m, l) of the rows follow all the float4s.
+      } else if (row < nrows) {
+        // split: publish this segment's partial state, in store order: float4
+        // k of lane (jg, row) sits at float4 index (k * 4 + jg) * nrows + row of
+        // the slot, so each store writes contiguous runs of 16 rows (a row-major
+        // layout would put each lane's 16 bytes in a different cache line);
+        // (m, l) of the rows follow all the float4s.
 #pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        if (!mine(k)) continue;
-        *(f32x4*)(pslot + ((k * 4 + jg) * nrows + row) * 4) = vec(c, k);
+        for (int k = 0; k < NT; ++k) {
+          if (!mine(k)) continue;
+          *(f32x4*)(pslot + ((k * 4 + jg) * nrows + row) * 4) = vec(k);
+        }
+        if (jg == 0 && ws == 0) *(f32x2*)(pslot + nrows * D + 2 * row) = (f32x2){m_run[c], l_tot};
       }
-      if (jg == 0 && ws == 0) *(f32x2*)(pslot + nrows * D + 2 * row) = (f32x2){m_run[c], l_tot};
     }
   };
 
@@ -999,14 +992,14 @@ hipError_t pass1_typed(const DecodeParams& p, int bs_shift, hipStream_t stream) 
 // (RH = 2, at most four heads). (At two column tiles, and with fp32 values,
 // the pooled merge's registers would spill.)
 template <bool BF16, int NC, int RH>
-constexpr bool tile_split = BF16 && RH == 1 && NC == 1;
+constexpr bool tile_split = BF16;
 
 template <bool BF16, int D, int NC, int RH>
 hipError_t pass1_heads(const DecodeParams& p, int bs_shift, hipStream_t stream) {
   const int h = p.num_kv_heads;
   if constexpr (tile_split<BF16, NC, RH>) {
-    if (h % 2 == 0) return pass1_typed<BF16, D, 2, NC, RH, 4>(p, bs_shift, stream);
-    return pass1_typed<BF16, D, 1, NC, RH, 8>(p, bs_shift, stream);
+    if (h % 2 == 0) return pass1_typed<BF16, D, 2, NC, RH, 4 / RH>(p, bs_shift, stream);
+    return pass1_typed<BF16, D, 1, NC, RH, 8 / RH>(p, bs_shift, stream);
   } else {
     if constexpr (RH == 1) {
       if (h % 8 == 0) return pass1_typed<BF16, D, 8, NC, RH, 1>(p, bs_shift, stream);
@@ -1021,8 +1014,8 @@ template <bool BF16, int D, int NC, int RH>
 hipError_t slices_heads(const DecodeParams& p, int* slices) {
   const int h = p.num_kv_heads;
   if constexpr (tile_split<BF16, NC, RH>) {
-    if (h % 2 == 0) return slices_typed<BF16, D, 2, NC, RH, 4>(p, slices);
-    return slices_typed<BF16, D, 1, NC, RH, 8>(p, slices);
+    if (h % 2 == 0) return slices_typed<BF16, D, 2, NC, RH, 4 / RH>(p, slices);
+    return slices_typed<BF16, D, 1, NC, RH, 8 / RH>(p, slices);
   } else {
     if constexpr (RH == 1) {
       if (h % 8 == 0) return slices_typed<BF16, D, 8, NC, RH, 1>(p, slices);
