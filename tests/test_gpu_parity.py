@@ -174,8 +174,9 @@ def test_large_batch_block_split(cuda, large_batch):
 @pytest.mark.parametrize("tp", [2, 8])
 def test_tensor_parallel_share_at_scale(cuda, tp):
     """One tensor-parallel rank's share of the 256-request batch (Hkv / tp KV
-    heads: 4, or 1 with 3072 one-wave slices): the step through the library,
-    whole images, every row against the oracle, padded rows zero."""
+    heads: 4, or 1, whose eight waves per workgroup all split one head's
+    tiles): the step through the library, whole images, every row against
+    the oracle, padded rows zero."""
     full_parity(W.tp_share(W.make_workload(3), tp), cuda)
 
 
@@ -267,8 +268,9 @@ SHAPES = [
     ("bf16", 128, 32, 4, 1, 16, [16, 40, 2100]),
     ("bf16", 128, 16, 2, 3, 5, [5, 6, 49, 5000]),  # G*Sq = 15, long split-K
     ("f32", 128, 16, 8, 1, 1, [9000, 9000]),        # many chunks per request
-    # KV-head counts that are not 1, 2, 4 or 8: one-wave groups of 3, two-wave
-    # groups of 6, and several 8-wave head groups per slice (12, 16, 32)
+    # KV-head counts that are not 1, 2, 4 or 8: odd counts (bf16: one head of
+    # eight tile-splitting waves per workgroup), and several head groups per
+    # slice (6, 12, 16; fp32 32: four of eight one-wave heads)
     ("bf16", 128, 64, 3, 2, 1, [7, 700, 3000]),
     ("bf16", 64, 16, 6, 2, 2, [2, 33, 1800]),
     ("bf16", 128, 32, 12, 1, 4, [4, 500, 2500]),
@@ -281,8 +283,8 @@ SHAPES = [
     ("bf16", 64, 64, 2, 12, 2, [2, 64, 65, 2200]),       # 24 rows, head_dim 64
     ("bf16", 128, 64, 2, 16, 4, [4, 64, 65, 2000]),      # 64 rows
     ("bf16", 64, 32, 4, 8, 8, [8, 9, 100, 1500]),        # 64 rows, head_dim 64
-    ("bf16", 128, 32, 3, 20, 3, [3, 90, 2500]),          # 60 rows, one-wave groups of 3
-    ("bf16", 128, 16, 8, 5, 7, [7, 8, 300, 6000]),       # 35 rows, eight heads in two groups
+    ("bf16", 128, 32, 3, 20, 3, [3, 90, 2500]),          # 60 rows, odd head count
+    ("bf16", 128, 16, 8, 5, 7, [7, 8, 300, 6000]),       # 35 rows, two row groups per head
     ("f32", 128, 16, 2, 12, 2, [2, 33, 700]),            # fp32, 24 rows
     ("f32", 64, 64, 1, 8, 5, [5, 6, 400]),               # fp32, 40 rows
     ("f32", 128, 32, 8, 4, 16, [16, 17, 300]),           # fp32, 64 rows
