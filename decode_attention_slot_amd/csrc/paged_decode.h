@@ -42,7 +42,7 @@
 //   tile t is computed and are never under a data-dependent branch (an
 //   inactive table entry reads null block 0 and is masked; the loop tail
 //   re-loads its last tile, which hits in cache), so one tile stays in
-//   flight behind the one being computed. A barrier every two tiles keeps
+//   flight behind the one being computed. A barrier every tile step keeps
 //   the waves of a workgroup in step.
 // * Tile of 16 tokens. The query rows of a KV head ((query token, head in
 //   group) pairs, up to 64) form column tiles of 16: NC of them per wave, and
@@ -516,15 +516,15 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 #pragma unroll
       for (int s = 0; s < kDepth - 1; ++s) load(tile_at(s), bufs[s], s >= nw);
       for (int t = 0; t < steps; t += kDepth) {
-        // Keep the workgroup's waves in step (every wave walks the same
-        // tiles, for its own KV head). Two waves share each SIMD, and the
-        // older one wins issue arbitration; left alone it runs ahead and the
-        // other finishes its last tiles with half the loads in flight. A
-        // bare s_barrier waits for no memory access, so the tiles already
-        // requested stay in flight across it.
-        __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int s = 0; s < kDepth; ++s) {
+          // Keep the workgroup's waves in step, every step (they walk the
+          // same tiles, or the same tiles' neighbours). Two waves share each
+          // SIMD, and the older one wins issue arbitration; left alone it
+          // runs ahead and the other finishes its last tiles with half the
+          // loads in flight. A bare s_barrier waits for no memory access, so
+          // the tiles already requested stay in flight across it.
+          __builtin_amdgcn_s_barrier();
           load(tile_at(t + s + kDepth - 1), bufs[(s + kDepth - 1) % kDepth],
                t + s + kDepth - 1 >= nw);
           if (t + s < nw) fn(t_begin + (t_first + (t + s) * WS) * kTile, bufs[s]);
