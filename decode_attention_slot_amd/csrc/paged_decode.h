@@ -42,7 +42,8 @@
 //   tile t is computed and are never under a data-dependent branch (an
 //   inactive table entry reads null block 0 and is masked; the loop tail
 //   re-loads its last tile, which hits in cache), so one tile stays in
-//   flight behind the one being computed. A barrier every tile step keeps
+//   flight behind the one being computed. A barrier every tile step (two with
+//   two row groups per head) keeps
 //   the waves of a workgroup in step.
 // * Tile of 16 tokens. The query rows of a KV head ((query token, head in
 //   group) pairs, up to 64) form column tiles of 16: NC of them per wave, and
@@ -258,7 +259,9 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   __shared__ float s_pm[NPOOL], s_pl[NPOOL];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform (in a scalar register): the wave's head, rows, tile share and
+  // every tile's address base follow from it without per-lane arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int rho = lane & 15;  // query row owned by this lane (MFMA column)
   const int jg = lane >> 4;   // lane group: tokens 4*jg .. 4*jg+3 of a tile
 
@@ -518,13 +521,15 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       for (int t = 0; t < steps; t += kDepth) {
 #pragma unroll
         for (int s = 0; s < kDepth; ++s) {
-          // Keep the workgroup's waves in step, every step (they walk the
-          // same tiles, or the same tiles' neighbours). Two waves share each
-          // SIMD, and the older one wins issue arbitration; left alone it
-          // runs ahead and the other finishes its last tiles with half the
-          // loads in flight. A bare s_barrier waits for no memory access, so
-          // the tiles already requested stay in flight across it.
-          __builtin_amdgcn_s_barrier();
+          // Keep the workgroup's waves in step (they walk the same tiles, or
+          // the same tiles' neighbours): every step, or every kDepth steps
+          // with two row groups per head (each measured the faster there). Two
+          // waves share each SIMD, and the older one wins issue arbitration;
+          // left alone it runs ahead and the other finishes its last tiles
+          // with half the loads in flight. A bare s_barrier waits for no
+          // memory access, so the tiles already requested stay in flight
+          // across it.
+          if (RH == 1 || s == 0) __builtin_amdgcn_s_barrier();
           load(tile_at(t + s + kDepth - 1), bufs[(s + kDepth - 1) % kDepth],
                t + s + kDepth - 1 >= nw);
           if (t + s < nw) fn(t_begin + (t_first + (t + s) * WS) * kTile, bufs[s]);
