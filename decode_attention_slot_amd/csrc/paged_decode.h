@@ -17,8 +17,8 @@
 // How, on CDNA4:
 // * Work split: the 16-token tiles of every request's context, laid end to
 //   end over the batch, are cut into `slices` equal ranges, one per
-//   resident workgroup slot (at most eight waves per compute unit, four
-//   with four KV heads per workgroup), so every
+//   resident workgroup slot (eight waves per compute unit; four for the fp32
+//   kernels of four KV heads per workgroup), so every
 //   workgroup streams the same number of bytes and all finish together (no
 //   rounds, no tail of short units). A
 //   range may start or end inside a request and may span requests; each
