@@ -85,6 +85,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "kvslot_internal.h"
 #include "slot_formula.h"
@@ -242,6 +243,19 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     uint32_t v[4][NVW];  // V slices of tokens 4*jg .. 4*jg+3
     int bid;             // block id the tile was read from (0: inactive entry)
   };
+  // Two row groups per head (bf16): the two waves that hold a head's rows
+  // for the same tiles each load half of every tile, row group 0 the K
+  // pieces and row group 1 the V slices, and trade halves through LDS, so no
+  // tile is read twice and a wave's ring holds halves, not whole tiles.
+  // (One more tile in flight measured no faster.)
+  constexpr bool SH = BF16 && RH == 2;
+  constexpr int DEPTH = kDepth;
+  static_assert(!SH || NVW == NP, "a V half packs into NP 16-byte pieces");
+  struct HalfBuf {
+    u32x4 h[NP];  // the K pieces, or the V slices of tokens 4*jg .. 4*jg+3, 16 bytes at a time
+    int bid;
+  };
+  using RingBuf = typename std::conditional<SH, HalfBuf, TileBuf>::type;
   extern __shared__ int s_pref[];  // [num_seqs + 1]: first tile of each request
   __shared__ int s_blk[kStage];
   __shared__ int s_wave[NWAVES], s_wave_n[NWAVES];
@@ -255,7 +269,11 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // the tile split's pool: every wave's state of one column tile at a
   // segment's end, per lane
   constexpr int NPOOL = WS > 1 ? NWAVES * 64 : 1;
-  __shared__ f32x4 s_pool[WS > 1 ? NPOOL * NT : 1];
+  // (with two row groups per head it also carries the traded tile halves:
+  // two steps' worth, per (head, tile share), K then V, per lane)
+  constexpr int NXCH = SH ? 2 * NW * WS * 2 * NP * 64 : 1;
+  constexpr int NBIG = (WS > 1 ? NPOOL * NT : 1) > NXCH ? (WS > 1 ? NPOOL * NT : 1) : NXCH;
+  __shared__ f32x4 s_pool[NBIG];
   __shared__ float s_pm[NPOOL], s_pl[NPOOL];
 
   const int lane = threadIdx.x & 63;
@@ -474,7 +492,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       // used; its V part then reads the same rows of the K cache, lines the
       // tile's K loads just brought in, instead of missing again on V (whose
       // nontemporal loads are not kept in cache).
-      auto load = [&](int tt, TileBuf& bf, bool tail) {
+      auto load = [&](int tt, RingBuf& bf, bool tail) {
         const int bid = uniform(s_blk[((tt - off) >> bs_shift) - pb]);
         const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
         const int64_t base = (int64_t)(active ? bid : 0) * block_bytes;
@@ -482,6 +500,26 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         const char* vb = (const char*)(tail ? p.k_cache : p.v_cache) + base;
         const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
         bf.bid = active ? bid : 0;
+        if constexpr (SH) {
+          if (rh == 0) {
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp)
+              bf.h[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const char* src = vb + in_blk + v_lane_off + i * row_bytes;
+              if constexpr (NVW == 2) {
+                const u32x2 x = __builtin_nontemporal_load((const u32x2*)src);
+                bf.h[i >> 1][(i & 1) * 2] = x[0];
+                bf.h[i >> 1][(i & 1) * 2 + 1] = x[1];
+              } else {
+                bf.h[i] = __builtin_nontemporal_load((const u32x4*)src);
+              }
+            }
+          }
+          return;
+        } else {
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp)
           bf.k[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
@@ -503,6 +541,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
             }
           }
         }
+        }
       };
       // This wave's tiles of the piece: those whose absolute tile index is ws
       // mod WS (all of them when WS = 1), t_first, t_first + WS, ..., nw of
@@ -512,15 +551,53 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       const int t_first = WS > 1 ? (ws - (t_begin >> 4)) & (WS - 1) : 0;
       const int nw = WS > 1 ? (nt > t_first ? (nt - t_first + WS - 1) / WS : 0) : nt;
       const int steps = WS > 1 ? (nt + WS - 1) / WS : nt;
-      TileBuf bufs[kDepth];
+      RingBuf bufs[DEPTH];
       auto tile_at = [&](int u) {
         return t_begin + (nw > 0 ? t_first + min(u, nw - 1) * WS : 0) * kTile;
       };
 #pragma unroll
-      for (int s = 0; s < kDepth - 1; ++s) load(tile_at(s), bufs[s], s >= nw);
-      for (int t = 0; t < steps; t += kDepth) {
+      for (int s = 0; s < DEPTH - 1; ++s) load(tile_at(s), bufs[s], s >= nw);
+      // this wave's (head, tile share): the pair of row groups that trade halves
+      const int stream = wave % NW + NW * ws;
+      for (int t = 0; t < steps; t += DEPTH) {
 #pragma unroll
-        for (int s = 0; s < kDepth; ++s) {
+        for (int s = 0; s < DEPTH; ++s) {
+          if constexpr (SH) {
+            // Put this wave's half of tile t + s into LDS (two steps' buffers
+            // alternate), wait for the partner's, then read both halves.
+            // The barrier also keeps the waves in step, and it is passed by
+            // every wave at every step, with a tile or not.
+            const int x0 = (((t + s) & 1) * NW * WS + stream) * 2 * NP;
+            if (t + s < nw) {
+#pragma unroll
+              for (int j = 0; j < NP; ++j)
+                s_pool[(x0 + rh * NP + j) * 64 + lane] = __builtin_bit_cast(f32x4, bufs[s].h[j]);
+            }
+            __syncthreads();
+            load(tile_at(t + s + DEPTH - 1), bufs[(s + DEPTH - 1) % DEPTH],
+                 t + s + DEPTH - 1 >= nw);
+            if (t + s < nw) {
+              TileBuf tb;
+              tb.bid = bufs[s].bid;
+#pragma unroll
+              for (int j = 0; j < NP; ++j) {
+                tb.k[j] = __builtin_bit_cast(u32x4, s_pool[(x0 + j) * 64 + lane]);
+                const u32x4 vv = __builtin_bit_cast(u32x4, s_pool[(x0 + NP + j) * 64 + lane]);
+                if constexpr (NVW == 2) {
+                  tb.v[2 * j][0] = vv[0];
+                  tb.v[2 * j][1] = vv[1];
+                  tb.v[2 * j + 1][0] = vv[2];
+                  tb.v[2 * j + 1][1] = vv[3];
+                } else {
+                  tb.v[j][0] = vv[0];
+                  tb.v[j][1] = vv[1];
+                  tb.v[j][2] = vv[2];
+                  tb.v[j][3] = vv[3];
+                }
+              }
+              fn(t_begin + (t_first + (t + s) * WS) * kTile, tb);
+            }
+          } else {
           // Keep the workgroup's waves in step (they walk the same tiles, or
           // the same tiles' neighbours): every step, or every kDepth steps
           // with two row groups per head (each measured the faster there). Two
@@ -530,9 +607,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
           // memory access, so the tiles already requested stay in flight
           // across it.
           if (RH == 1 || s == 0) __builtin_amdgcn_s_barrier();
-          load(tile_at(t + s + kDepth - 1), bufs[(s + kDepth - 1) % kDepth],
-               t + s + kDepth - 1 >= nw);
+          load(tile_at(t + s + DEPTH - 1), bufs[(s + DEPTH - 1) % DEPTH],
+               t + s + DEPTH - 1 >= nw);
           if (t + s < nw) fn(t_begin + (t_first + (t + s) * WS) * kTile, bufs[s]);
+          }
         }
       }
     }
@@ -746,7 +824,9 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       // with k mod WS == ws.
       float sc[WS];
       if constexpr (WS > 1) {
-        if (c > 0) __syncthreads();  // the previous column tile's pool is read
+        // the previous column tile's pool is read (and, with traded halves,
+        // the walk's last halves, which share its LDS)
+        if (c > 0 || SH) __syncthreads();
         const int at = grp * WS + ws;
         s_pm[at * 64 + lane] = m_run[c];
         s_pl[at * 64 + lane] = l_run[c];
