@@ -43,12 +43,13 @@
 //   inactive table entry reads null block 0 and is masked; the loop tail
 //   re-loads its last tile, which hits in cache), so one tile stays in
 //   flight behind the one being computed. A barrier every tile step (two with
-//   two row groups per head) keeps
-//   the waves of a workgroup in step.
+//   two row groups per head) keeps the waves of a workgroup in step.
 // * Tile of 16 tokens. The query rows of a KV head ((query token, head in
 //   group) pairs, up to 64) form column tiles of 16: NC of them per wave, and
-//   above 32 rows two waves per KV head share the rows (both read the same
-//   tiles; the second read hits in cache). S^T = K Q^T on
+//   above 32 rows two row groups per KV head share the rows. Both need every
+//   tile: with bf16 KV the wave of row group 0 loads its K pieces and the wave
+//   of row group 1 its V slices, and they trade halves through LDS (fp32 KV:
+//   both load the whole tile, the second read hitting in cache). S^T = K Q^T on
 //   v_mfma_f32_16x16x32_bf16 (fp32 KV: v_mfma_f32_16x16x4f32), once per
 //   column tile: K is the A operand (lane l holds token l % 16, 16 bytes of
 //   its head row per piece), Q^T the B operand (lane l holds query row
