@@ -213,11 +213,12 @@ __device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
 // MODE: kContextWalk, kTableWalk (the fixed-shape walk) or kGeneral (a
 // sliding window over a possibly tail-trimmed table, or one rank's share
 // under context parallelism).
-// NC: column tiles of 16 query rows per wave; RH: waves per KV head, each
-// holding 16 NC consecutive rows of the head's (Hq / Hkv) * q_len rows (at
-// most 16 NC RH). The waves of one head read the same K and V tiles (the
-// second read hits in cache); the head's accumulators are split between
-// them. WS: waves that split the tiles of a head (and row group): wave s
+// NC: column tiles of 16 query rows per wave; RH: row groups per KV head,
+// each holding 16 NC consecutive rows of the head's (Hq / Hkv) * q_len rows
+// (at most 16 NC RH). The row groups of one head need the same K and V tiles
+// (bf16: they trade halves, below; fp32: each reads the whole tile, the
+// second read hitting in cache). WS: waves that split the tiles of a head
+// (and row group): wave s
 // takes the tiles whose absolute index is s mod WS, keeping its own softmax
 // state for its rows; at the end of a segment the WS states are pooled in LDS
 // and merged in wave order. Waves of a workgroup: NW KV heads times RH times
@@ -248,7 +249,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // for the same tiles each load half of every tile, row group 0 the K
   // pieces and row group 1 the V slices, and trade halves through LDS, so no
   // tile is read twice and a wave's ring holds halves, not whole tiles.
-  // (One more tile in flight measured no faster.)
+  // (One more half in flight measured no faster; DEPTH is the ring's
+  // length, the same for every kernel.)
   constexpr bool SH = BF16 && RH == 2;
   constexpr int DEPTH = kDepth;
   static_assert(!SH || NVW == NP, "a V half packs into NP 16-byte pieces");
