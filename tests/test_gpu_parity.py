@@ -356,7 +356,7 @@ def random_case_params(seed):
     return dtype, d, bs, hkv, g, sq, [int(x) for x in lens], trim, table_walk, holes, rng
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(192))
 def test_random_batches_vs_oracle(cuda, seed):
     """Seeded random batches (shape, lengths, head trim, fixed-shape walk,
     inactive entries inside a context) against the oracle."""
