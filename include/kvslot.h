@@ -294,10 +294,10 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
  * 256-rounded 8 * num_seqs bytes plus (S + num_seqs) partial slots of
  * num_q_heads * q_len * (head_dim + 4) * 4 bytes, S being the number of
  * slices the launch cuts the batch into (at most the device's resident
- * pass-1 workgroups per head group: 256 on MI355X at 8 KV heads); a call
- * that needs more than KVS_NOALLOC_WORKSPACE_BYTES returns KVS_ENOSPACE
- * before anything is enqueued (the 256-request, 64-query-head batch needs
- * about 18 MB).
+ * pass-1 workgroups per head group: 64 on MI355X at 8 KV heads of bf16, two
+ * heads per workgroup); a call that needs more than
+ * KVS_NOALLOC_WORKSPACE_BYTES returns KVS_ENOSPACE before anything is
+ * enqueued (the 256-request, 64-query-head batch needs about 11 MB).
  * Errors: those of paged_decode_attention, KVS_ENOSPACE as above, KVS_EHIP
  * when the array's address cannot be obtained.
  */
