@@ -491,6 +491,11 @@ SWA_SHAPES = [
     ("bf16", 128, 64, 8, 4, 4, 333, [4, 5, 336, 337, 2000, 6000]),
     ("bf16", 64, 256, 2, 2, 2, 600, [2, 255, 600, 601, 3000]),
     ("bf16", 128, 32, 4, 1, 16, 50, [16, 40, 66, 2100]),
+    # more than 16 rows per KV head in the window path: two column tiles per
+    # wave (32 rows), two row groups trading tile halves (64 and 60 rows)
+    ("bf16", 128, 16, 8, 8, 4, 500, [4, 5, 600, 3000]),
+    ("bf16", 128, 64, 2, 16, 4, 300, [4, 64, 65, 2000]),
+    ("bf16", 64, 32, 3, 20, 3, 100, [3, 90, 2500]),
 ]
 
 
@@ -659,6 +664,8 @@ def dcp_gpu_case(cuda, seed, lens, bs, world, interleave, hkv, g, sq, d, dtype):
     (4, 8, 64, "bf16", 1, 4, [1, 5, 64, 700, 3000, 9000]),
     (3, 64, 64, "bf16", 2, 8, [2, 191, 192, 193, 4000]),
     (8, 16, 16, "bf16", 1, 8, [7, 128, 2049, 6000]),
+    (2, 16, 64, "bf16", 4, 8, [4, 20, 129, 1500, 5000]),  # 32 rows per KV head
+    (4, 8, 64, "bf16", 4, 16, [4, 100, 3000]),            # 64 rows: traded tile halves
 ])
 def test_dcp_ranks_and_merge_vs_oracle(cuda, world, interleave, bs, dtype, sq, g, lens):
     hkv, d = 2, 128
