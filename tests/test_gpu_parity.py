@@ -404,6 +404,23 @@ def test_invariants_bitwise(cuda):
     assert max_err(base, ref_attn(c)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("hkv,g,sq", [(8, 8, 4), (2, 16, 4), (3, 12, 5)])
+def test_walks_bitwise_many_rows(cuda, hkv, g, sq):
+    """32, 64 and 60 query rows per KV head (two column tiles per wave; two
+    row groups trading tile halves): the fixed-shape walk and a head trim give
+    the context walk's output bit for bit, and it matches the oracle."""
+    c = small_case(cuda, 11 + g, [sq, 70, 700, 3000], 64, hkv, g, sq, 128, "bf16", width=64)
+    base = gpu_attn(c)
+    walk = -(-3000 // 64)
+    trim = gpu_attn(c, walk_blocks=walk)
+    trim_tw = gpu_attn(c, walk_blocks=walk, flags=K.KVS_WALK_TABLE)
+    full_tw = gpu_attn(c, flags=K.KVS_WALK_TABLE)
+    torch.cuda.synchronize()
+    for o in (trim, trim_tw, full_tw):
+        assert torch.equal(o.view(torch.int32), base.view(torch.int32))
+    assert max_err(base, ref_attn(c)) <= TOL["bf16"]
+
+
 def test_edge_lengths_and_trim(cuda):
     # L < q_len (no visible key for early queries), L = 0 rows, narrow trim
     c = small_case(cuda, 5, [2, 9, 200], 16, 2, 2, 4, 64, "bf16", width=16)
