@@ -54,7 +54,8 @@
 //   column tile: K is the A operand (lane l holds token l % 16, 16 bytes of
 //   its head row per piece), Q^T the B operand (lane l holds query row
 //   16 c + l % 16). The result gives each lane four tokens of one row.
-// * Online softmax per query row, in exp2 units, entirely inside the lane
+// * Online softmax per query row, in exp2 units, with a lazily moved
+//   exponent reference (at most 8 below the running max), entirely inside the lane
 //   except one max over the four lane groups (two permlane swaps).
 // * O^T = V^T P^T, per column tile. Lane l reads a 16-byte slice of the
 //   head rows of tokens 4 * (l / 16) .. + 3 (each 16-lane group reads whole
@@ -716,7 +717,13 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         }
       }
 
-      // online softmax, per row
+      // online softmax, per row. The row's exponent reference m_run moves only
+      // when a tile's max passes it by more than 8 (log2 units), to that max:
+      // the weights exp2(s - m_run) stay below 2^8, exact in the three-term
+      // split and far from fp32 overflow in l and acc, and the accumulator
+      // rescale (NT * 4 * NC multiplies) runs a few times per segment instead
+      // of at most tiles. (m_run is a reference, not the running max; the
+      // partial state and the merges use it as such.)
       float pr4[NC][4];
       bool moved = false;
       float alpha[NC];
@@ -724,7 +731,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       for (int c = 0; c < NC; ++c) {
         float mx = fmaxf(fmaxf(sx[c][0], sx[c][1]), fmaxf(sx[c][2], sx[c][3]));
         mx = max_over_groups(mx);
-        const float m_new = fmaxf(m_run[c], mx);
+        const float m_new = mx > m_run[c] + 8.0f ? mx : m_run[c];
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         alpha[c] = __builtin_amdgcn_exp2f(m_run[c] - m_use);
 #pragma unroll
