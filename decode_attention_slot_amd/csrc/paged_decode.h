@@ -54,6 +54,11 @@
 //   column tile: K is the A operand (lane l holds token l % 16, 16 bytes of
 //   its head row per piece), Q^T the B operand (lane l holds query row
 //   16 c + l % 16). The result gives each lane four tokens of one row.
+//   bf16 K with one row group per head does not load in that layout (each
+//   instruction would read a 64-byte piece of sixteen rows 2 KB apart):
+//   direct-to-LDS loads read whole head rows into a per-wave LDS ring,
+//   stored with the chunk index XORed by the token, and each lane reads its
+//   operand pieces back (conflict-free) just before the score MFMA.
 // * Online softmax per query row, in exp2 units, with a lazily moved
 //   exponent reference (at most 8 below the running max), entirely inside the lane
 //   except one max over the four lane groups (two permlane swaps).
@@ -112,6 +117,11 @@ constexpr int kContextWalk = 0, kTableWalk = 1, kGeneral = 2, kAppend = 3;
 constexpr int kTile = 16;
 constexpr int kStage = 256;  // block ids staged in LDS at a time
 constexpr int kDepth = 2;    // tiles in flight per wave
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector memory
+// operations of this wave are outstanding; lgkmcnt and expcnt not waited on.
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+constexpr int kVmcnt0 = vmcnt_imm(0);
 
 // Wavefront scans on DPP: four row shifts build the prefix inside each row
 // of 16 lanes, two row broadcasts carry it across rows. Values move lane to
@@ -276,7 +286,22 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // (with two row groups per head it also carries the traded tile halves:
   // two steps' worth, per (head, tile share), K then V, per lane)
   constexpr int NXCH = SH ? 2 * NW * WS * 2 * NP * 64 : 1;
-  constexpr int NBIG = (WS > 1 ? NPOOL * NT : 1) > NXCH ? (WS > 1 ? NPOOL * NT : 1) : NXCH;
+  // bf16 K (one row group per head) reaches the MFMA through LDS: each tile's
+  // K is read as whole head rows by direct-to-LDS loads into a ring of DEPTH
+  // slots per wave, which shares its LDS with the pool (a segment's walk and
+  // its pooling never overlap). A head row is CH 16-byte chunks; one load
+  // instruction covers TPI whole rows, NI of them a tile. Chunk c of token t
+  // sits at 16-byte slot CH t + (c ^ (t mod CH)) of the slot: the XOR keeps
+  // the operand reads below free of bank conflicts.
+  constexpr bool KL = BF16 && !SH;
+  constexpr int CH = D * ES / 16;
+  constexpr int TPI = 64 / CH;
+  constexpr int NI = kTile / TPI;
+  constexpr int KSLOT = kTile * CH;  // f32x4 per ring slot
+  constexpr int NRING = KL ? NWAVES * DEPTH * KSLOT : 1;
+  constexpr int NPL = WS > 1 ? NPOOL * NT : 1;
+  constexpr int NBIG0 = NPL > NXCH ? NPL : NXCH;
+  constexpr int NBIG = NBIG0 > NRING ? NBIG0 : NRING;
   __shared__ f32x4 s_pool[NBIG];
   __shared__ float s_pm[NPOOL], s_pl[NPOOL];
 
@@ -465,6 +490,50 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   uint32_t sink = 0;
   const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
   const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
+  // K through LDS: this lane's byte offset in the tile for load instruction
+  // i (token TPI i + lane / CH, chunk (lane mod CH) ^ token), and its f32x4
+  // index in a ring slot for operand piece pp (token rho, chunk 4 pp + jg,
+  // the chunk the query's piece pp holds in this lane).
+  uint32_t k_dma_off[KL ? NI : 1];
+  int k_rd[KL ? NP : 1];
+  if constexpr (KL) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t = TPI * i + lane / CH;
+      const int c = (lane % CH) ^ (t % CH);
+      k_dma_off[i] = (uint32_t)t * row_bytes + (uint32_t)g * (D * ES) + 16u * (uint32_t)c;
+    }
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+      k_rd[pp] = (int)(16 * ((uint32_t)(CH * rho + ((4 * pp + jg) ^ (rho % CH)))));
+  }
+  // The operand pieces of the tile in ring slot `base` (an f32x4 index),
+  // read in one asm block that also waits for them: the compiler then adds no
+  // wait of its own for the direct-to-LDS loads in flight to the other slot.
+  auto read_k_slot = [&](u32x4 (&k)[NP], int base) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) f32x4*)
+                           (&s_pool[base]);
+    if constexpr (NP == 4) {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %5\n\t"
+          "ds_read_b128 %2, %6\n\t"
+          "ds_read_b128 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(k[0]), "=v"(k[1]), "=v"(k[2]), "=v"(k[3])
+          : "v"(a + k_rd[0]), "v"(a + k_rd[1]), "v"(a + k_rd[2]), "v"(a + k_rd[3])
+          : "memory");
+    } else {
+      static_assert(!KL || NP == 2, "head_dim 64 or 128");
+      asm volatile(
+          "ds_read_b128 %0, %2\n\t"
+          "ds_read_b128 %1, %3\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=v"(k[0]), "=v"(k[1])
+          : "v"(a + k_rd[0]), "v"(a + k_rd[1])
+          : "memory");
+    }
+  };
 
   // Tiles [tok_a, tok_b) (absolute positions, multiples of kTile) of table
   // row trow, whose column 0 holds position off, through fn(position of the
@@ -477,6 +546,9 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     const int blk_end = ((tok_b - 1 - off) >> bs_shift) + 1;
     for (int pb = blk_first; pb < blk_end; pb += kStage) {
       const int pn = min(kStage, blk_end - pb);
+      // K through LDS: the previous piece's last loads into the ring land
+      // before this piece's first ones are issued
+      if constexpr (KL) __builtin_amdgcn_s_waitcnt(kVmcnt0);
       __syncthreads();  // the previous piece (and segment's pooled states) is consumed
       for (int i = threadIdx.x; i < pn; i += NTHR) {
         const int col = pb + i;
@@ -490,13 +562,17 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       // K as the score MFMA's A operand, V in row layout. An inactive
       // entry reads null block 0 and is masked by the caller. V rows are
       // read with the nontemporal hint (streamed past the caches): on
-      // MI355X that lifts long streams of reads from ~6.4 to ~7 TB/s; K
-      // stays a plain load, its latency heads the per-tile dependency chain.
+      // MI355X that lifts long streams of reads from ~6.4 to ~7 TB/s. bf16 K
+      // (one row group per head) goes to ring slot sl in LDS as whole head
+      // rows (each load instruction reads TPI complete 256-byte rows: about
+      // 7.1 TB/s for the K and V stream, against 6.7 TB/s when every
+      // instruction reads a 64-byte piece of sixteen rows, the operand layout
+      // in registers); otherwise K is a plain load into registers.
       // A load past the last tile (`tail`) re-loads the last tile and is never
       // used; its V part then reads the same rows of the K cache, lines the
       // tile's K loads just brought in, instead of missing again on V (whose
       // nontemporal loads are not kept in cache).
-      auto load = [&](int tt, RingBuf& bf, bool tail) {
+      auto load = [&](int tt, RingBuf& bf, int sl, bool tail) {
         const int bid = uniform(s_blk[((tt - off) >> bs_shift) - pb]);
         const bool active = bid > 0 && (int64_t)bid < p.total_blocks;
         const int64_t base = (int64_t)(active ? bid : 0) * block_bytes;
@@ -524,9 +600,19 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
           }
           return;
         } else {
+        if constexpr (KL) {
+          f32x4* slot = &s_pool[(wave * DEPTH + sl) * KSLOT];
+          asm volatile("" ::: "memory");  // after the slot's last operand reads
 #pragma unroll
-        for (int pp = 0; pp < NP; ++pp)
-          bf.k[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
+          for (int i = 0; i < NI; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const void*)(kb + in_blk + k_dma_off[i]),
+                (__attribute__((address_space(3))) void*)(slot + i * 64), 16, 0, 0);
+        } else {
+#pragma unroll
+          for (int pp = 0; pp < NP; ++pp)
+            bf.k[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const char* src = vb + in_blk + v_lane_off + i * row_bytes;
@@ -560,7 +646,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         return t_begin + (nw > 0 ? t_first + min(u, nw - 1) * WS : 0) * kTile;
       };
 #pragma unroll
-      for (int s = 0; s < DEPTH - 1; ++s) load(tile_at(s), bufs[s], s >= nw);
+      for (int s = 0; s < DEPTH - 1; ++s) load(tile_at(s), bufs[s], s, s >= nw);
       // this wave's (head, tile share): the pair of row groups that trade halves
       const int stream = wave % NW + NW * ws;
       for (int t = 0; t < steps; t += DEPTH) {
@@ -578,7 +664,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
                 s_pool[(x0 + rh * NP + j) * 64 + lane] = __builtin_bit_cast(f32x4, bufs[s].h[j]);
             }
             __syncthreads();
-            load(tile_at(t + s + DEPTH - 1), bufs[(s + DEPTH - 1) % DEPTH],
+            load(tile_at(t + s + DEPTH - 1), bufs[(s + DEPTH - 1) % DEPTH], (s + DEPTH - 1) % DEPTH,
                  t + s + DEPTH - 1 >= nw);
             if (t + s < nw) {
               TileBuf tb;
@@ -611,9 +697,23 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
           // memory access, so the tiles already requested stay in flight
           // across it.
           if (RH == 1 || s == 0) __builtin_amdgcn_s_barrier();
-          load(tile_at(t + s + DEPTH - 1), bufs[(s + DEPTH - 1) % DEPTH],
+          load(tile_at(t + s + DEPTH - 1), bufs[(s + DEPTH - 1) % DEPTH], (s + DEPTH - 1) % DEPTH,
                t + s + DEPTH - 1 >= nw);
-          if (t + s < nw) fn(t_begin + (t_first + (t + s) * WS) * kTile, bufs[s]);
+          if constexpr (KL) {
+            // Tile t + s is in (its K in slot s) once at most the loads just
+            // issued (one tile's: NI to LDS, four V) are outstanding. Waited
+            // for at every step, with a tile or not, so that the compiler
+            // finds the older loads done on every path and adds no wait of
+            // its own. The empty asm statements keep it from moving memory
+            // accesses across the wait.
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI + 4));
+            asm volatile("" ::: "memory");
+          }
+          if (t + s < nw) {
+            if constexpr (KL) read_k_slot(bufs[s].k, (wave * DEPTH + s) * KSLOT);
+            fn(t_begin + (t_first + (t + s) * WS) * kTile, bufs[s]);
+          }
           }
         }
       }
@@ -836,7 +936,10 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       if constexpr (WS > 1) {
         // the previous column tile's pool is read (and, with traded halves,
         // the walk's last halves, which share its LDS)
-        if (c > 0 || SH) __syncthreads();
+        // (K through LDS: every wave's last loads into its ring, which the
+        // pool overlays, have landed)
+        if (KL && c == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        if (c > 0 || SH || KL) __syncthreads();
         const int at = grp * WS + ws;
         s_pm[at * 64 + lane] = m_run[c];
         s_pl[at * 64 + lane] = l_run[c];
@@ -964,6 +1067,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     }
     if (p.flags & kFlagSink) p.out[0] = __uint_as_float(sink);
   }
+  // no load into this workgroup's LDS outlives it
+  if constexpr (KL) __builtin_amdgcn_s_waitcnt(kVmcnt0);
 }
 
 // Workgroups of a kernel the device holds at once (compute units times
