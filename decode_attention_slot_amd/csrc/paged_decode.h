@@ -42,14 +42,17 @@
 //   tile t is computed and are never under a data-dependent branch (an
 //   inactive table entry reads null block 0 and is masked; the loop tail
 //   re-loads its last tile, which hits in cache), so one tile stays in
-//   flight behind the one being computed. A barrier every tile step (two with
-//   two row groups per head) keeps the waves of a workgroup in step.
+//   flight behind the one being computed. A bare barrier every tile step
+//   keeps the waves of a workgroup in step (every two steps for fp32 with two
+//   row groups per head); it waits for no load in flight, where
+//   __syncthreads() would wait for all of them.
 // * Tile of 16 tokens. The query rows of a KV head ((query token, head in
 //   group) pairs, up to 64) form column tiles of 16: NC of them per wave, and
 //   above 32 rows two row groups per KV head share the rows. Both need every
-//   tile: with bf16 KV the wave of row group 0 loads its K pieces and the wave
-//   of row group 1 its V slices, and they trade halves through LDS (fp32 KV:
-//   both load the whole tile, the second read hitting in cache). S^T = K Q^T on
+//   tile: with bf16 KV the wave of row group 0 loads its K rows and the wave
+//   of row group 1 its V rows, by direct-to-LDS loads into a ring the two
+//   share, and both read their operands from there (fp32 KV: both load the
+//   whole tile into registers, the second read hitting in cache). S^T = K Q^T on
 //   v_mfma_f32_16x16x32_bf16 (fp32 KV: v_mfma_f32_16x16x4f32), once per
 //   column tile: K is the A operand (lane l holds token l % 16, 16 bytes of
 //   its head row per piece), Q^T the B operand (lane l holds query row
@@ -257,19 +260,13 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     int bid;             // block id the tile was read from (0: inactive entry)
   };
   // Two row groups per head (bf16): the two waves that hold a head's rows
-  // for the same tiles each load half of every tile, row group 0 the K
-  // pieces and row group 1 the V slices, and trade halves through LDS, so no
-  // tile is read twice and a wave's ring holds halves, not whole tiles.
-  // (One more half in flight measured no faster; DEPTH is the ring's
-  // length, the same for every kernel.)
+  // for the same tiles each load half of every tile, row group 0 the K rows
+  // and row group 1 the V rows, by direct-to-LDS loads into a ring of DL
+  // slots that the pair shares, so no tile is read twice and no register
+  // holds a tile in flight.
   constexpr bool SH = BF16 && RH == 2;
   constexpr int DEPTH = kDepth;
-  static_assert(!SH || NVW == NP, "a V half packs into NP 16-byte pieces");
-  struct HalfBuf {
-    u32x4 h[NP];  // the K pieces, or the V slices of tokens 4*jg .. 4*jg+3, 16 bytes at a time
-    int bid;
-  };
-  using RingBuf = typename std::conditional<SH, HalfBuf, TileBuf>::type;
+  using RingBuf = TileBuf;
   extern __shared__ int s_pref[];  // [num_seqs + 1]: first tile of each request
   __shared__ int s_blk[kStage];
   __shared__ int s_wave[NWAVES], s_wave_n[NWAVES];
@@ -283,25 +280,27 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // the tile split's pool: every wave's state of one column tile at a
   // segment's end, per lane
   constexpr int NPOOL = WS > 1 ? NWAVES * 64 : 1;
-  // (with two row groups per head it also carries the traded tile halves:
-  // two steps' worth, per (head, tile share), K then V, per lane)
-  constexpr int NXCH = SH ? 2 * NW * WS * 2 * NP * 64 : 1;
-  // bf16 K (one row group per head) reaches the MFMA through LDS: each tile's
-  // K is read as whole head rows by direct-to-LDS loads into a ring of DEPTH
-  // slots per wave, which shares its LDS with the pool (a segment's walk and
-  // its pooling never overlap). A head row is CH 16-byte chunks; one load
-  // instruction covers TPI whole rows, NI of them a tile. Chunk c of token t
-  // sits at 16-byte slot CH t + (c ^ (t mod CH)) of the slot: the XOR keeps
-  // the operand reads below free of bank conflicts.
+  // bf16 K reaches the MFMA through LDS: each tile's K is read as whole head
+  // rows by direct-to-LDS loads into a ring, which shares its LDS with the
+  // pool (a segment's walk and its pooling never overlap). One row group per
+  // head: DEPTH slots of K per wave (V in registers). Two row groups: DL
+  // slots of K and V per (head, tile share). A head row is CH 16-byte
+  // chunks; one load instruction covers TPI whole rows, NI of them a tile.
+  // Chunk c of K token t sits at 16-byte slot CH t + (c ^ (t mod CH)) of
+  // its slot: the XOR keeps the operand reads below free of bank conflicts.
+  // V rows are stored as they are (chunk c of token t at slot CH t + c).
   constexpr bool KL = BF16 && !SH;
+  constexpr bool LR = KL || SH;  // a ring in LDS
   constexpr int CH = D * ES / 16;
   constexpr int TPI = 64 / CH;
   constexpr int NI = kTile / TPI;
-  constexpr int KSLOT = kTile * CH;  // f32x4 per ring slot
-  constexpr int NRING = KL ? NWAVES * DEPTH * KSLOT : 1;
+  constexpr int KSLOT = kTile * CH;  // f32x4 per tile's K (or V)
+  // Two row groups: two slots per pair (a third measured no faster at 64
+  // rows: 985 vs 983 us for the 256-request batch with 1 + 7 tokens).
+  constexpr int DL = 2;
+  constexpr int NRING = KL ? NWAVES * DEPTH * KSLOT : SH ? NW * WS * DL * 2 * KSLOT : 1;
   constexpr int NPL = WS > 1 ? NPOOL * NT : 1;
-  constexpr int NBIG0 = NPL > NXCH ? NPL : NXCH;
-  constexpr int NBIG = NBIG0 > NRING ? NBIG0 : NRING;
+  constexpr int NBIG = NPL > NRING ? NPL : NRING;
   __shared__ f32x4 s_pool[NBIG];
   __shared__ float s_pm[NPOOL], s_pl[NPOOL];
 
@@ -488,15 +487,17 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   }
 
   uint32_t sink = 0;
+  // this wave's (head, tile share): with two row groups, the pair that shares a ring
+  const int stream = wave % NW + NW * ws;
   const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
   const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
   // K through LDS: this lane's byte offset in the tile for load instruction
   // i (token TPI i + lane / CH, chunk (lane mod CH) ^ token), and its f32x4
   // index in a ring slot for operand piece pp (token rho, chunk 4 pp + jg,
   // the chunk the query's piece pp holds in this lane).
-  uint32_t k_dma_off[KL ? NI : 1];
-  int k_rd[KL ? NP : 1];
-  if constexpr (KL) {
+  uint32_t k_dma_off[LR ? NI : 1];
+  int k_rd[LR ? NP : 1];
+  if constexpr (LR) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = TPI * i + lane / CH;
@@ -507,9 +508,25 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     for (int pp = 0; pp < NP; ++pp)
       k_rd[pp] = (int)(16 * ((uint32_t)(CH * rho + ((4 * pp + jg) ^ (rho % CH)))));
   }
+  // Two row groups: V rows as stored (token TPI i + lane / CH, chunk
+  // lane mod CH for load instruction i), and the byte offset in a V slot of
+  // this lane's slice of token 4 jg + i (NT bf16 values at dimension
+  // column rho * NT).
+  uint32_t v_dma_off[SH ? NI : 1];
+  int v_rd[SH ? 4 : 1];
+  if constexpr (SH) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      v_dma_off[i] = (uint32_t)(TPI * i + lane / CH) * row_bytes + (uint32_t)g * (D * ES) +
+                     16u * (uint32_t)(lane % CH);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v_rd[i] = 16 * CH * (4 * jg + i) + rho * (NT * ES);
+  }
   // The operand pieces of the tile in ring slot `base` (an f32x4 index),
   // read in one asm block that also waits for them: the compiler then adds no
   // wait of its own for the direct-to-LDS loads in flight to the other slot.
+  // The outputs are early-clobber: a read's destination must not be the
+  // address register of a later read in the block (its data may land first).
   auto read_k_slot = [&](u32x4 (&k)[NP], int base) {
     const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) f32x4*)
                            (&s_pool[base]);
@@ -520,18 +537,59 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
           "ds_read_b128 %2, %6\n\t"
           "ds_read_b128 %3, %7\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(k[0]), "=v"(k[1]), "=v"(k[2]), "=v"(k[3])
+          : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
           : "v"(a + k_rd[0]), "v"(a + k_rd[1]), "v"(a + k_rd[2]), "v"(a + k_rd[3])
           : "memory");
     } else {
-      static_assert(!KL || NP == 2, "head_dim 64 or 128");
+      static_assert(!LR || NP == 2, "head_dim 64 or 128");
       asm volatile(
           "ds_read_b128 %0, %2\n\t"
           "ds_read_b128 %1, %3\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(k[0]), "=v"(k[1])
+          : "=&v"(k[0]), "=&v"(k[1])
           : "v"(a + k_rd[0]), "v"(a + k_rd[1])
           : "memory");
+    }
+  };
+  // Two row groups: the V slices of the tile in the V part of ring slot
+  // `base` (this lane's NT values of tokens 4 jg .. 4 jg + 3), read the same
+  // way.
+  auto read_v_slot = [&](TileBuf& tb, int base) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) f32x4*)
+                           (&s_pool[base]);
+    if constexpr (NVW == 4) {
+      u32x4 v0, v1, v2, v3;
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %5\n\t"
+          "ds_read_b128 %2, %6\n\t"
+          "ds_read_b128 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+          : "v"(a + v_rd[0]), "v"(a + v_rd[1]), "v"(a + v_rd[2]), "v"(a + v_rd[3])
+          : "memory");
+      const u32x4 vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) tb.v[i][w] = vv[i][w];
+    } else {
+      static_assert(!SH || NVW == 2, "head_dim 64 or 128");
+      u32x2 v0, v1, v2, v3;
+      asm volatile(
+          "ds_read_b64 %0, %4\n\t"
+          "ds_read_b64 %1, %5\n\t"
+          "ds_read_b64 %2, %6\n\t"
+          "ds_read_b64 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+          : "v"(a + v_rd[0]), "v"(a + v_rd[1]), "v"(a + v_rd[2]), "v"(a + v_rd[3])
+          : "memory");
+      const u32x2 vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) tb.v[i][w] = vv[i][w];
     }
   };
 
@@ -548,7 +606,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       const int pn = min(kStage, blk_end - pb);
       // K through LDS: the previous piece's last loads into the ring land
       // before this piece's first ones are issued
-      if constexpr (KL) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      if constexpr (LR) __builtin_amdgcn_s_waitcnt(kVmcnt0);
       __syncthreads();  // the previous piece (and segment's pooled states) is consumed
       for (int i = threadIdx.x; i < pn; i += NTHR) {
         const int col = pb + i;
@@ -581,22 +639,23 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
         bf.bid = active ? bid : 0;
         if constexpr (SH) {
+          // this wave's half of the tile, K rows (row group 0) or V rows (1),
+          // into the K or V part of the pair's ring slot sl
+          f32x4* slot = &s_pool[(stream * DL + sl) * 2 * KSLOT + (rh ? KSLOT : 0)];
+          asm volatile("" ::: "memory");  // after the slot's last operand reads
           if (rh == 0) {
 #pragma unroll
-            for (int pp = 0; pp < NP; ++pp)
-              bf.h[pp] = *(const u32x4*)(kb + in_blk + k_lane_off + pp * 64);
+            for (int i = 0; i < NI; ++i)
+              __builtin_amdgcn_global_load_lds(
+                  (const void*)(kb + in_blk + k_dma_off[i]),
+                  (__attribute__((address_space(3))) void*)(slot + i * 64), 16, 0, 0);
           } else {
+            // V with the nontemporal hint, as in registers
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const char* src = vb + in_blk + v_lane_off + i * row_bytes;
-              if constexpr (NVW == 2) {
-                const u32x2 x = __builtin_nontemporal_load((const u32x2*)src);
-                bf.h[i >> 1][(i & 1) * 2] = x[0];
-                bf.h[i >> 1][(i & 1) * 2 + 1] = x[1];
-              } else {
-                bf.h[i] = __builtin_nontemporal_load((const u32x4*)src);
-              }
-            }
+            for (int i = 0; i < NI; ++i)
+              __builtin_amdgcn_global_load_lds(
+                  (const void*)(vb + in_blk + v_dma_off[i]),
+                  (__attribute__((address_space(3))) void*)(slot + i * 64), 16, 0, 2);
           }
           return;
         } else {
@@ -641,53 +700,53 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       const int t_first = WS > 1 ? (ws - (t_begin >> 4)) & (WS - 1) : 0;
       const int nw = WS > 1 ? (nt > t_first ? (nt - t_first + WS - 1) / WS : 0) : nt;
       const int steps = WS > 1 ? (nt + WS - 1) / WS : nt;
-      RingBuf bufs[DEPTH];
       auto tile_at = [&](int u) {
         return t_begin + (nw > 0 ? t_first + min(u, nw - 1) * WS : 0) * kTile;
       };
+      if constexpr (SH) {
+        // Two row groups: the pair's ring of DL slots in LDS. Step t reads
+        // slot t mod DL and first issues this wave's half of tile t + DL - 1
+        // into the slot read at step t - 1, so DL - 1 tiles are on their way
+        // while one is used.
+        TileBuf idle;  // load() only records the block id here
+#pragma unroll
+        for (int u = 0; u < DL - 1; ++u) load(tile_at(u), idle, u, u >= nw);
+        int sl = 0;
+        for (int t = 0; t < steps; ++t) {
+          // This wave's half of tile t has landed once at most the halves
+          // issued after it are outstanding; the barrier then has the
+          // partner's half landed too, and every wave done with the slot
+          // loaded next (its reads wait for their data before the wave goes
+          // on). Passed by every wave at every step, with a tile or not. A
+          // bare s_barrier: __syncthreads() would also wait for every load
+          // in flight, the next tiles' included. (The empty asm statements
+          // keep the compiler from moving memory accesses across the wait
+          // and the barrier.)
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((DL - 2) * NI));
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          load(tile_at(t + DL - 1), idle, sl == 0 ? DL - 1 : sl - 1, t + DL - 1 >= nw);
+          if (t < nw) {
+            const int tt = tile_at(t);
+            const int bid = uniform(s_blk[((tt - off) >> bs_shift) - pb]);
+            TileBuf tb;
+            tb.bid = bid > 0 && (int64_t)bid < p.total_blocks ? bid : 0;
+            const int base = (stream * DL + sl) * 2 * KSLOT;
+            read_k_slot(tb.k, base);
+            read_v_slot(tb, base + KSLOT);
+            fn(tt, tb);
+          }
+          sl = sl == DL - 1 ? 0 : sl + 1;
+        }
+      } else {
+      RingBuf bufs[DEPTH];
 #pragma unroll
       for (int s = 0; s < DEPTH - 1; ++s) load(tile_at(s), bufs[s], s, s >= nw);
-      // this wave's (head, tile share): the pair of row groups that trade halves
-      const int stream = wave % NW + NW * ws;
       for (int t = 0; t < steps; t += DEPTH) {
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
-          if constexpr (SH) {
-            // Put this wave's half of tile t + s into LDS (two steps' buffers
-            // alternate), wait for the partner's, then read both halves.
-            // The barrier also keeps the waves in step, and it is passed by
-            // every wave at every step, with a tile or not.
-            const int x0 = (((t + s) & 1) * NW * WS + stream) * 2 * NP;
-            if (t + s < nw) {
-#pragma unroll
-              for (int j = 0; j < NP; ++j)
-                s_pool[(x0 + rh * NP + j) * 64 + lane] = __builtin_bit_cast(f32x4, bufs[s].h[j]);
-            }
-            __syncthreads();
-            load(tile_at(t + s + DEPTH - 1), bufs[(s + DEPTH - 1) % DEPTH], (s + DEPTH - 1) % DEPTH,
-                 t + s + DEPTH - 1 >= nw);
-            if (t + s < nw) {
-              TileBuf tb;
-              tb.bid = bufs[s].bid;
-#pragma unroll
-              for (int j = 0; j < NP; ++j) {
-                tb.k[j] = __builtin_bit_cast(u32x4, s_pool[(x0 + j) * 64 + lane]);
-                const u32x4 vv = __builtin_bit_cast(u32x4, s_pool[(x0 + NP + j) * 64 + lane]);
-                if constexpr (NVW == 2) {
-                  tb.v[2 * j][0] = vv[0];
-                  tb.v[2 * j][1] = vv[1];
-                  tb.v[2 * j + 1][0] = vv[2];
-                  tb.v[2 * j + 1][1] = vv[3];
-                } else {
-                  tb.v[j][0] = vv[0];
-                  tb.v[j][1] = vv[1];
-                  tb.v[j][2] = vv[2];
-                  tb.v[j][3] = vv[3];
-                }
-              }
-              fn(t_begin + (t_first + (t + s) * WS) * kTile, tb);
-            }
-          } else {
           // Keep the workgroup's waves in step (they walk the same tiles, or
           // the same tiles' neighbours): every step, or every kDepth steps
           // with two row groups per head (each measured the faster there). Two
@@ -714,8 +773,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
             if constexpr (KL) read_k_slot(bufs[s].k, (wave * DEPTH + s) * KSLOT);
             fn(t_begin + (t_first + (t + s) * WS) * kTile, bufs[s]);
           }
-          }
         }
+      }
       }
     }
   };
@@ -938,8 +997,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         // the walk's last halves, which share its LDS)
         // (K through LDS: every wave's last loads into its ring, which the
         // pool overlays, have landed)
-        if (KL && c == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        if (c > 0 || SH || KL) __syncthreads();
+        if (LR && c == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        if (c > 0 || LR) __syncthreads();
         const int at = grp * WS + ws;
         s_pm[at * 64 + lane] = m_run[c];
         s_pl[at * 64 + lane] = l_run[c];
@@ -1068,7 +1127,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     if (p.flags & kFlagSink) p.out[0] = __uint_as_float(sink);
   }
   // no load into this workgroup's LDS outlives it
-  if constexpr (KL) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  if constexpr (LR) __builtin_amdgcn_s_waitcnt(kVmcnt0);
 }
 
 // Workgroups of a kernel the device holds at once (compute units times
