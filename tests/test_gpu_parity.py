@@ -407,7 +407,7 @@ def test_invariants_bitwise(cuda):
 @pytest.mark.parametrize("hkv,g,sq", [(8, 8, 4), (2, 16, 4), (3, 12, 5)])
 def test_walks_bitwise_many_rows(cuda, hkv, g, sq):
     """32, 64 and 60 query rows per KV head (two column tiles per wave; two
-    row groups trading tile halves): the fixed-shape walk and a head trim give
+    row groups sharing one LDS ring of tiles): the fixed-shape walk and a head trim give
     the context walk's output bit for bit, and it matches the oracle."""
     c = small_case(cuda, 11 + g, [sq, 70, 700, 3000], 64, hkv, g, sq, 128, "bf16", width=64)
     base = gpu_attn(c)
