@@ -599,7 +599,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // of kStage; a ring of kDepth tile buffers keeps tiles t+1 .. t+kDepth-1
   // in flight while tile t is used. Loads past the last tile re-load the
   // last tile (a cache hit), so no load depends on a branch.
-  auto walk_tiles_of = [&](const int32_t* trow, int off, int tok_a, int tok_b, auto&& fn) {
+  auto walk_tiles_of = [&](const int32_t* trow, int off, int tok_a, int tok_b, auto&& fn,
+                           auto&& after_first_prologue) {
     const int blk_first = (tok_a - off) >> bs_shift;
     const int blk_end = ((tok_b - 1 - off) >> bs_shift) + 1;
     for (int pb = blk_first; pb < blk_end; pb += kStage) {
@@ -711,6 +712,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         TileBuf idle;  // load() only records the block id here
 #pragma unroll
         for (int u = 0; u < DL - 1; ++u) load(tile_at(u), idle, u, u >= nw);
+        if (pb == blk_first) after_first_prologue();
         int sl = 0;
         for (int t = 0; t < steps; ++t) {
           // This wave's half of tile t has landed once at most the halves
@@ -744,6 +746,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       RingBuf bufs[DEPTH];
 #pragma unroll
       for (int s = 0; s < DEPTH - 1; ++s) load(tile_at(s), bufs[s], s, s >= nw);
+      if (pb == blk_first) after_first_prologue();
       for (int t = 0; t < steps; t += DEPTH) {
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
@@ -805,14 +808,23 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       qlo[c] = GEN && p.window > 0
                    ? (int)max((int64_t)qpos[c] - p.window + 1, (int64_t)INT32_MIN)
                    : INT32_MIN;
-      const char* qrow = (const char*)p.q +
-                         ((((int64_t)r * Sq + jrow[c]) * Hq + (int64_t)g * G + hh[c]) * D) * ES;
-#pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        qp[c][pp] = (u32x4){0u, 0u, 0u, 0u};
-        if (row < nrows) qp[c][pp] = *(const u32x4*)(qrow + pp * 64 + jg * 16);
-      }
     }
+    // The query pieces, loaded once the segment's first tiles are requested
+    // (walk_tiles_of calls this after its first prologue), so that their round
+    // trip overlaps the tiles' instead of preceding the table staging.
+    auto load_q = [&]() {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int row = row0 + 16 * c + rho;
+        const char* qrow = (const char*)p.q +
+                           ((((int64_t)r * Sq + jrow[c]) * Hq + (int64_t)g * G + hh[c]) * D) * ES;
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          qp[c][pp] = (u32x4){0u, 0u, 0u, 0u};
+          if (row < nrows) qp[c][pp] = *(const u32x4*)(qrow + pp * 64 + jg * 16);
+        }
+      }
+    };
     // Global position of a walked position: itself, except under context
     // parallelism, where the walk runs over this rank's local positions.
     auto gpos = [&](int lp) -> int64_t {
@@ -965,7 +977,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       }
     };
     walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, off, (t_lo + t0) * kTile,
-                  (t_lo + t1) * kTile, consume);
+                  (t_lo + t1) * kTile, consume, load_q);
 
     // acc[c][n][i] holds dimension (4*jg + i) * NT + n of query row row0 + 16c + rho.
     // Its float4 k = i * NT / 4 + n0 / 4 gathers n-tiles n0 .. n0 + 3 of
@@ -1118,7 +1130,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       if (pn > pos) {
         const int e = min(pbnd, pn);
         walk_tiles_of(p.block_table + (int64_t)r * p.table_stride, 0, (n + pos - pr) * kTile,
-                      (n + e - pr) * kTile, drain);
+                      (n + e - pr) * kTile, drain, [] {});
         pos = e;
       }
       tp += n;
