@@ -267,7 +267,9 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   constexpr bool SH = BF16 && RH == 2;
   constexpr int DEPTH = kDepth;
   using RingBuf = TileBuf;
-  extern __shared__ int s_pref[];  // [num_seqs + 1]: first tile of each request
+  // [num_seqs + 1]: first tile of each request; then [num_seqs]: its length
+  extern __shared__ int s_pref[];
+  int* const s_len = s_pref + p.num_seqs + 1;
   __shared__ int s_blk[kStage];
   __shared__ int s_wave[NWAVES], s_wave_n[NWAVES];
   // append: the step tokens whose rows this slice reads, and their slots
@@ -357,15 +359,21 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       app_p = p.app_pos[threadIdx.x];
     }
   }
-  if ((int)threadIdx.x < B) s_pref[threadIdx.x] = request_span<GEN>(p, threadIdx.x, len0, walk_tok, bs, Sq).n;
+  if ((int)threadIdx.x < B) {
+    s_pref[threadIdx.x] = request_span<GEN>(p, threadIdx.x, len0, walk_tok, bs, Sq).n;
+    s_len[threadIdx.x] = len0;
+  }
   if constexpr (APP) {
     if (app_r >= 0 && app_r < B && app_p >= 0 && (app_p >> bs_shift) < p.table_stride) {
       app_lb = app_p >> bs_shift;
       app_blk = p.block_table[(int64_t)app_r * p.table_stride + app_lb];
     }
   }
-  for (int rr = threadIdx.x + NTHR; rr < B; rr += NTHR)
-    s_pref[rr] = request_span<GEN>(p, rr, p.seq_lens[rr], walk_tok, bs, Sq).n;
+  for (int rr = threadIdx.x + NTHR; rr < B; rr += NTHR) {
+    const int len = p.seq_lens[rr];
+    s_pref[rr] = request_span<GEN>(p, rr, len, walk_tok, bs, Sq).n;
+    s_len[rr] = len;
+  }
   if (threadIdx.x == 0) {
     s_first[0] = 0;
     s_first[1] = 0;
@@ -784,7 +792,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 
   // ---- one segment: tiles [t0, t1) of request r (nr tiles, tile 0 at unit pr) --
   auto segment = [&](int r, int t0, int t1, int nr, int pr) {
-    const int L = uniform(p.seq_lens[r]);
+    const int L = uniform(s_len[r]);  // from LDS: no memory round trip at a segment start
     const ReqSpan sp = request_span<GEN>(p, r, L, walk_tok, bs, Sq);
     const int E = uniform(sp.E);
     const int off = uniform(sp.off);

@@ -278,7 +278,8 @@ int32_t decode_max_slices(int32_t num_kv_heads) {
 }
 
 size_t decode_lds_bytes(int32_t num_seqs) {
-  return ((size_t)num_seqs + 1) * sizeof(int32_t);
+  // pass 1's prefix of the requests' tiles (num_seqs + 1) and their lengths
+  return (2 * (size_t)num_seqs + 1) * sizeof(int32_t);
 }
 
 size_t decode_meta_bytes(int32_t num_seqs) {
