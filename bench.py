@@ -54,6 +54,7 @@ HBM_PEAK_GBPS = 8000.0
 MIN_CALLS = 50  # event-timed attention calls, at least
 SLOT_SWEEP_TOKENS = 1 << 22  # slot mapping measured at this many tokens per launch as well
 SLOT_SWEEP_SETS = 11  # distinct token sets rotated (11 x 100 MB: past the 256 MB MALL)
+SLOT_SWEEP_RUN = 128  # consecutive positions per request in the chunked sweep
 WORKLOADS = {
     "block_config_bf16": 1,
     "ctx_bucketing": 2,
@@ -517,7 +518,7 @@ def main(argv=None) -> int:
     # launches rotate over SLOT_SWEEP_SETS distinct token sets (about 1.1 GB of
     # token and slot arrays), so their bytes come from HBM and not from the
     # 256 MB last-level cache; only the table (a few hundred KB) stays cached.
-    sweep = None
+    sweep = sweep_chunked = None
     if w.num_reqs:
         nt = SLOT_SWEEP_TOKENS
         gen = torch.Generator(device=cuda)
@@ -545,6 +546,36 @@ def main(argv=None) -> int:
                          "every table read is a scattered cache-line fetch (the worst case; a "
                          "step's tokens are grouped by request); the token and slot arrays "
                          "stream from HBM"}
+        del sets
+        # The same sweep with the tokens of a prefill chunk: runs of
+        # SLOT_SWEEP_RUN consecutive positions of one request (a random real
+        # request, from a random start below its length), as a chunked step
+        # hands them over; neighbouring tokens then share their table entry.
+        runs = nt // SLOT_SWEEP_RUN
+        step = torch.arange(SLOT_SWEEP_RUN, device=cuda, dtype=torch.int64)
+        sets = []
+        for _ in range(SLOT_SWEEP_SETS):
+            r_req = torch.randint(0, w.num_reqs, (runs,), generator=gen, device=cuda,
+                                  dtype=torch.int64)
+            r_len = lens[r_req]
+            r_start = (torch.rand(runs, generator=gen, device=cuda, dtype=torch.float64)
+                       * torch.clamp(r_len - SLOT_SWEEP_RUN, min=1)).to(torch.int64)
+            d_pos = torch.minimum(r_start[:, None] + step[None, :], r_len[:, None] - 1).reshape(-1)
+            d_req = r_req.to(torch.int32).repeat_interleave(SLOT_SWEEP_RUN)
+            d_slots = torch.empty(nt, dtype=torch.int64, device=cuda)
+            sets.append((d_req.contiguous(), d_pos.contiguous(), d_slots))
+        big = [(a.data_ptr(), b.data_ptr(), nt, nt, s.block_table.data_ptr(), int(rows),
+                int(stride), w.block_size, c.data_ptr(), sp) for a, b, c in sets]
+        t_chunk = back_to_back(f_slot, big, 5 * SLOT_SWEEP_SETS)
+        sweep_chunked = {"tokens": nt, "token_sets_rotated": SLOT_SWEEP_SETS,
+                         "run": SLOT_SWEEP_RUN, "us": round(t_chunk * 1e6, 3),
+                         "tokens_per_s": round(nt / t_chunk, 1),
+                         "gbps": round(slot_map_bytes(nt) / t_chunk / 1e9, 2),
+                         "frac_of_peak": round(slot_map_bytes(nt) / t_chunk / 1e9 / HBM_PEAK_GBPS, 4),
+                         "note": f"24 B per token counted; runs of {SLOT_SWEEP_RUN} consecutive "
+                                 "positions of one request (a prefill chunk), so neighbouring "
+                                 "tokens share their table entry; the token and slot arrays "
+                                 "stream from HBM"}
         del sets
 
     if args.copy_probe_mib:
@@ -606,6 +637,7 @@ def main(argv=None) -> int:
         "decode_tokens_per_s": round(decode_tokens / (ms_per_step * 1e-3), 1),
         "slot_map_tokens_per_s": round(T / t_slot, 1),
         "slot_map_sweep": sweep,
+        "slot_map_sweep_chunked": sweep_chunked,
         "lse_merge": lse_merge,
         "kernel_us": {"kv_slot_mapping": round(t_slot * 1e6, 3),
                       "kv_cache_write": round(t_write * 1e6, 3),

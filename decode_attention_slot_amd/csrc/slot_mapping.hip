@@ -8,8 +8,12 @@
 // Sentinel -1"), and the tail of a fixed-size slot buffer is padded with -1
 // (the vLLM block-table notes, data-flow listing).
 //
-// One thread per output entry. The vLLM kernel runs one program per request;
-// a flat grid over tokens keeps every lane busy whatever the length mix.
+// One thread per output entry, or per four consecutive entries when the
+// three arrays are 16-byte aligned (one 16-byte load of request indices, two
+// of positions and two 16-byte stores: a step's tokens come in runs of one
+// request, so most of a launch's bytes are these streams, not the table).
+// The vLLM kernel runs one program per request; a flat grid over tokens keeps
+// every lane busy whatever the length mix.
 #include "kvslot_internal.h"
 #include "slot_formula.h"
 
@@ -28,6 +32,44 @@ slot_mapping_kernel(const int32_t* __restrict__ req_indices, const int64_t* __re
                                                   table_rows, table_stride, block_size,
                                                   block_shift)
                                      : -1;
+  }
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
+
+__global__ void __launch_bounds__(256)
+slot_mapping_x4_kernel(const int32_t* __restrict__ req_indices,
+                       const int64_t* __restrict__ positions, int64_t num_tokens,
+                       int64_t max_num_tokens, const int32_t* __restrict__ block_table,
+                       int32_t table_rows, int32_t table_stride, int32_t block_size,
+                       int32_t block_shift, int64_t* __restrict__ slot_mapping) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t quads = (max_num_tokens + 3) / 4;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += stride) {
+    const int64_t t = 4 * q;
+    if (t + 4 <= num_tokens) {
+      const i32x4 r = *(const i32x4*)(req_indices + t);
+      const i64x2 p01 = *(const i64x2*)(positions + t);
+      const i64x2 p23 = *(const i64x2*)(positions + t + 2);
+      const i64x2 s01 = {token_slot(r[0], p01[0], block_table, table_rows, table_stride,
+                                    block_size, block_shift),
+                         token_slot(r[1], p01[1], block_table, table_rows, table_stride,
+                                    block_size, block_shift)};
+      const i64x2 s23 = {token_slot(r[2], p23[0], block_table, table_rows, table_stride,
+                                    block_size, block_shift),
+                         token_slot(r[3], p23[1], block_table, table_rows, table_stride,
+                                    block_size, block_shift)};
+      *(i64x2*)(slot_mapping + t) = s01;
+      *(i64x2*)(slot_mapping + t + 2) = s23;
+    } else {
+      // the quad holding the step's last tokens, or only padding
+      for (int64_t u = t; u < t + 4 && u < max_num_tokens; ++u)
+        slot_mapping[u] = u < num_tokens ? token_slot(req_indices[u], positions[u], block_table,
+                                                      table_rows, table_stride, block_size,
+                                                      block_shift)
+                                         : -1;
+    }
   }
 }
 
@@ -74,11 +116,19 @@ hipError_t launch_slot_mapping(const int32_t* req_indices, const int64_t* positi
   if (max_num_tokens == 0) return hipSuccess;
   const int shift =
       (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
-  int64_t blocks = (max_num_tokens + 255) / 256;
+  const bool x4 = (((uintptr_t)req_indices | (uintptr_t)positions | (uintptr_t)slot_mapping) &
+                   15) == 0;
+  const int64_t units = x4 ? (max_num_tokens + 3) / 4 : max_num_tokens;
+  int64_t blocks = (units + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  slot_mapping_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-      req_indices, positions, num_tokens, max_num_tokens, block_table, table_rows, table_stride,
-      block_size, shift, slot_mapping);
+  if (x4)
+    slot_mapping_x4_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        req_indices, positions, num_tokens, max_num_tokens, block_table, table_rows,
+        table_stride, block_size, shift, slot_mapping);
+  else
+    slot_mapping_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        req_indices, positions, num_tokens, max_num_tokens, block_table, table_rows,
+        table_stride, block_size, shift, slot_mapping);
   return hipGetLastError();
 }
 

@@ -463,16 +463,24 @@ def test_empty_inputs(cuda):
 
 
 @pytest.mark.parametrize("bs", [1, 3, 16, 64, 100])
-def test_slot_mapping_edges_vs_oracle(cuda, bs):
+@pytest.mark.parametrize("shift", [0, 1])
+def test_slot_mapping_edges_vs_oracle(cuda, bs, shift):
+    """Edge inputs against the oracle. shift 0: 16-byte aligned arrays (four
+    tokens per thread), 3001 tokens, so the last quad holds one token and
+    three padding slots; shift 1: views one element into their allocations,
+    aligned to their element size only (one token per thread)."""
     rng = np.random.default_rng(bs)
-    rows, width, T = 6, 7, 3000
+    rows, width, T = 6, 7, 3001
     table = rng.permutation(np.arange(1, rows * width + 1)).reshape(rows, width).astype(np.int32)
     kill = rng.random((rows, width))
     table = np.where(kill < 0.2, -1, np.where(kill < 0.3, 0, table)).astype(np.int32)
     req = rng.integers(-1, rows + 2, size=T).astype(np.int32)
     pos = rng.integers(-3, (width + 2) * bs, size=T).astype(np.int64)
-    got = K.kv_slot_mapping(torch.from_numpy(req).to(cuda), torch.from_numpy(pos).to(cuda),
-                            torch.from_numpy(table).to(cuda), bs, max_num_tokens=T + 77)
+    d_req = torch.from_numpy(np.concatenate([np.zeros(shift, np.int32), req])).to(cuda)[shift:]
+    d_pos = torch.from_numpy(np.concatenate([np.zeros(shift, np.int64), pos])).to(cuda)[shift:]
+    out = torch.empty(T + 77 + shift, dtype=torch.int64, device=cuda)[shift:]
+    assert (d_req.data_ptr() % 16 == 0) == (shift == 0) and (out.data_ptr() % 16 == 0) == (shift == 0)
+    got = K.kv_slot_mapping(d_req, d_pos, torch.from_numpy(table).to(cuda), bs, slot_mapping=out)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), O.compute_slot_mapping(req, pos, table, bs, T + 77))
 
