@@ -230,7 +230,7 @@ __device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
 // NC: column tiles of 16 query rows per wave; RH: row groups per KV head,
 // each holding 16 NC consecutive rows of the head's (Hq / Hkv) * q_len rows
 // (at most 16 NC RH). The row groups of one head need the same K and V tiles
-// (bf16: they trade halves, below; fp32: each reads the whole tile, the
+// (bf16: they share one LDS ring, below; fp32: each reads the whole tile, the
 // second read hitting in cache). WS: waves that split the tiles of a head
 // (and row group): wave s
 // takes the tiles whose absolute index is s mod WS, keeping its own softmax
@@ -500,8 +500,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
   const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
   // K through LDS: this lane's byte offset in the tile for load instruction
-  // i (token TPI i + lane / CH, chunk (lane mod CH) ^ token), and its f32x4
-  // index in a ring slot for operand piece pp (token rho, chunk 4 pp + jg,
+  // i (token TPI i + lane / CH, chunk (lane mod CH) ^ token), and its byte
+  // offset in a ring slot for operand piece pp (token rho, chunk 4 pp + jg,
   // the chunk the query's piece pp holds in this lane).
   uint32_t k_dma_off[LR ? NI : 1];
   int k_rd[LR ? NP : 1];
