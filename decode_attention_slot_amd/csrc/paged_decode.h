@@ -43,22 +43,22 @@
 //   inactive table entry reads null block 0 and is masked; the loop tail
 //   re-loads its last tile, which hits in cache), so one tile stays in
 //   flight behind the one being computed. A bare barrier every tile step
-//   keeps the waves of a workgroup in step (every two steps for fp32 with two
-//   row groups per head); it waits for no load in flight, where
-//   __syncthreads() would wait for all of them.
+//   keeps the waves of a workgroup in step (every two steps with two row
+//   groups per head); it waits for no load in flight, where __syncthreads()
+//   would wait for all of them.
 // * Tile of 16 tokens. The query rows of a KV head ((query token, head in
 //   group) pairs, up to 64) form column tiles of 16: NC of them per wave, and
 //   above 32 rows two row groups per KV head share the rows. Both need every
-//   tile: with bf16 KV the wave of row group 0 loads its K rows and the wave
-//   of row group 1 its V rows, by direct-to-LDS loads into a ring the two
-//   share, and both read their operands from there (fp32 KV: both load the
-//   whole tile into registers, the second read hitting in cache). S^T = K Q^T on
+//   tile and each wave loads it, the second read hitting in cache (V then
+//   without the nontemporal hint, so that its lines stay for the partner).
+//   (Sharing one LDS ring, each wave loading half of the tile, was slower:
+//   each step's barrier then waits for both halves to land.) S^T = K Q^T on
 //   v_mfma_f32_16x16x32_bf16 (fp32 KV: v_mfma_f32_16x16x4f32), once per
 //   column tile: K is the A operand (lane l holds token l % 16, 16 bytes of
 //   its head row per piece), Q^T the B operand (lane l holds query row
 //   16 c + l % 16). The result gives each lane four tokens of one row.
-//   bf16 K with one row group per head does not load in that layout (each
-//   instruction would read a 64-byte piece of sixteen rows 2 KB apart):
+//   bf16 K does not load in that layout (each instruction would read a
+//   64-byte piece of sixteen rows 2 KB apart):
 //   direct-to-LDS loads read whole head rows into a per-wave LDS ring,
 //   stored with the chunk index XORed by the token, and each lane reads its
 //   operand pieces back (conflict-free) just before the score MFMA.
@@ -229,9 +229,8 @@ __device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
 // under context parallelism).
 // NC: column tiles of 16 query rows per wave; RH: row groups per KV head,
 // each holding 16 NC consecutive rows of the head's (Hq / Hkv) * q_len rows
-// (at most 16 NC RH). The row groups of one head need the same K and V tiles
-// (bf16: they share one LDS ring, below; fp32: each reads the whole tile, the
-// second read hitting in cache). WS: waves that split the tiles of a head
+// (at most 16 NC RH). The row groups of one head need the same K and V tiles:
+// each reads the whole tile, the second read hitting in cache. WS: waves that split the tiles of a head
 // (and row group): wave s
 // takes the tiles whose absolute index is s mod WS, keeping its own softmax
 // state for its rows; at the end of a segment the WS states are pooled in LDS
@@ -259,12 +258,6 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     uint32_t v[4][NVW];  // V slices of tokens 4*jg .. 4*jg+3
     int bid;             // block id the tile was read from (0: inactive entry)
   };
-  // Two row groups per head (bf16): the two waves that hold a head's rows
-  // for the same tiles each load half of every tile, row group 0 the K rows
-  // and row group 1 the V rows, by direct-to-LDS loads into a ring of DL
-  // slots that the pair shares, so no tile is read twice and no register
-  // holds a tile in flight.
-  constexpr bool SH = BF16 && RH == 2;
   constexpr int DEPTH = kDepth;
   using RingBuf = TileBuf;
   // [num_seqs + 1]: first tile of each request; then [num_seqs]: its length
@@ -283,24 +276,18 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   // segment's end, per lane
   constexpr int NPOOL = WS > 1 ? NWAVES * 64 : 1;
   // bf16 K reaches the MFMA through LDS: each tile's K is read as whole head
-  // rows by direct-to-LDS loads into a ring, which shares its LDS with the
-  // pool (a segment's walk and its pooling never overlap). One row group per
-  // head: DEPTH slots of K per wave (V in registers). Two row groups: DL
-  // slots of K and V per (head, tile share). A head row is CH 16-byte
-  // chunks; one load instruction covers TPI whole rows, NI of them a tile.
-  // Chunk c of K token t sits at 16-byte slot CH t + (c ^ (t mod CH)) of
-  // its slot: the XOR keeps the operand reads below free of bank conflicts.
-  // V rows are stored as they are (chunk c of token t at slot CH t + c).
-  constexpr bool KL = BF16 && !SH;
-  constexpr bool LR = KL || SH;  // a ring in LDS
+  // rows by direct-to-LDS loads into a ring of DEPTH slots per wave (V stays
+  // in registers), which shares its LDS with the pool (a segment's walk and
+  // its pooling never overlap). A head row is CH 16-byte chunks; one load
+  // instruction covers TPI whole rows, NI of them a tile. Chunk c of token t
+  // sits at 16-byte slot CH t + (c ^ (t mod CH)) of its slot: the XOR keeps
+  // the operand reads below free of bank conflicts.
+  constexpr bool KL = BF16;
   constexpr int CH = D * ES / 16;
   constexpr int TPI = 64 / CH;
   constexpr int NI = kTile / TPI;
-  constexpr int KSLOT = kTile * CH;  // f32x4 per tile's K (or V)
-  // Two row groups: two slots per pair (a third measured no faster at 64
-  // rows: 985 vs 983 us for the 256-request batch with 1 + 7 tokens).
-  constexpr int DL = 2;
-  constexpr int NRING = KL ? NWAVES * DEPTH * KSLOT : SH ? NW * WS * DL * 2 * KSLOT : 1;
+  constexpr int KSLOT = kTile * CH;  // f32x4 per tile's K
+  constexpr int NRING = KL ? NWAVES * DEPTH * KSLOT : 1;
   constexpr int NPL = WS > 1 ? NPOOL * NT : 1;
   constexpr int NBIG = NPL > NRING ? NPL : NRING;
   __shared__ f32x4 s_pool[NBIG];
@@ -495,17 +482,15 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
   }
 
   uint32_t sink = 0;
-  // this wave's (head, tile share): with two row groups, the pair that shares a ring
-  const int stream = wave % NW + NW * ws;
   const uint32_t k_lane_off = ((uint32_t)rho * Hkv + g) * (D * ES) + jg * 16;
   const uint32_t v_lane_off = ((uint32_t)(4 * jg) * Hkv + g) * (D * ES) + rho * (NT * ES);
   // K through LDS: this lane's byte offset in the tile for load instruction
   // i (token TPI i + lane / CH, chunk (lane mod CH) ^ token), and its byte
   // offset in a ring slot for operand piece pp (token rho, chunk 4 pp + jg,
   // the chunk the query's piece pp holds in this lane).
-  uint32_t k_dma_off[LR ? NI : 1];
-  int k_rd[LR ? NP : 1];
-  if constexpr (LR) {
+  uint32_t k_dma_off[KL ? NI : 1];
+  int k_rd[KL ? NP : 1];
+  if constexpr (KL) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = TPI * i + lane / CH;
@@ -515,20 +500,6 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp)
       k_rd[pp] = (int)(16 * ((uint32_t)(CH * rho + ((4 * pp + jg) ^ (rho % CH)))));
-  }
-  // Two row groups: V rows as stored (token TPI i + lane / CH, chunk
-  // lane mod CH for load instruction i), and the byte offset in a V slot of
-  // this lane's slice of token 4 jg + i (NT bf16 values at dimension
-  // column rho * NT).
-  uint32_t v_dma_off[SH ? NI : 1];
-  int v_rd[SH ? 4 : 1];
-  if constexpr (SH) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      v_dma_off[i] = (uint32_t)(TPI * i + lane / CH) * row_bytes + (uint32_t)g * (D * ES) +
-                     16u * (uint32_t)(lane % CH);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v_rd[i] = 16 * CH * (4 * jg + i) + rho * (NT * ES);
   }
   // The operand pieces of the tile in ring slot `base` (an f32x4 index),
   // read in one asm block that also waits for them: the compiler then adds no
@@ -549,7 +520,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
           : "v"(a + k_rd[0]), "v"(a + k_rd[1]), "v"(a + k_rd[2]), "v"(a + k_rd[3])
           : "memory");
     } else {
-      static_assert(!LR || NP == 2, "head_dim 64 or 128");
+      static_assert(!KL || NP == 2, "head_dim 64 or 128");
       asm volatile(
           "ds_read_b128 %0, %2\n\t"
           "ds_read_b128 %1, %3\n\t"
@@ -559,48 +530,6 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
           : "memory");
     }
   };
-  // Two row groups: the V slices of the tile in the V part of ring slot
-  // `base` (this lane's NT values of tokens 4 jg .. 4 jg + 3), read the same
-  // way.
-  auto read_v_slot = [&](TileBuf& tb, int base) {
-    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) f32x4*)
-                           (&s_pool[base]);
-    if constexpr (NVW == 4) {
-      u32x4 v0, v1, v2, v3;
-      asm volatile(
-          "ds_read_b128 %0, %4\n\t"
-          "ds_read_b128 %1, %5\n\t"
-          "ds_read_b128 %2, %6\n\t"
-          "ds_read_b128 %3, %7\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
-          : "v"(a + v_rd[0]), "v"(a + v_rd[1]), "v"(a + v_rd[2]), "v"(a + v_rd[3])
-          : "memory");
-      const u32x4 vv[4] = {v0, v1, v2, v3};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) tb.v[i][w] = vv[i][w];
-    } else {
-      static_assert(!SH || NVW == 2, "head_dim 64 or 128");
-      u32x2 v0, v1, v2, v3;
-      asm volatile(
-          "ds_read_b64 %0, %4\n\t"
-          "ds_read_b64 %1, %5\n\t"
-          "ds_read_b64 %2, %6\n\t"
-          "ds_read_b64 %3, %7\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
-          : "v"(a + v_rd[0]), "v"(a + v_rd[1]), "v"(a + v_rd[2]), "v"(a + v_rd[3])
-          : "memory");
-      const u32x2 vv[4] = {v0, v1, v2, v3};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int w = 0; w < 2; ++w) tb.v[i][w] = vv[i][w];
-    }
-  };
-
   // Tiles [tok_a, tok_b) (absolute positions, multiples of kTile) of table
   // row trow, whose column 0 holds position off, through fn(position of the
   // tile, its loads). Block ids are staged in LDS in pieces
@@ -615,7 +544,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       const int pn = min(kStage, blk_end - pb);
       // K through LDS: the previous piece's last loads into the ring land
       // before this piece's first ones are issued
-      if constexpr (LR) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      if constexpr (KL) __builtin_amdgcn_s_waitcnt(kVmcnt0);
       __syncthreads();  // the previous piece (and segment's pooled states) is consumed
       for (int i = threadIdx.x; i < pn; i += NTHR) {
         const int col = pb + i;
@@ -629,12 +558,13 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       // K as the score MFMA's A operand, V in row layout. An inactive
       // entry reads null block 0 and is masked by the caller. V rows are
       // read with the nontemporal hint (streamed past the caches): on
-      // MI355X that lifts long streams of reads from ~6.4 to ~7 TB/s. bf16 K
-      // (one row group per head) goes to ring slot sl in LDS as whole head
-      // rows (each load instruction reads TPI complete 256-byte rows: about
-      // 7.1 TB/s for the K and V stream, against 6.7 TB/s when every
-      // instruction reads a 64-byte piece of sixteen rows, the operand layout
-      // in registers); otherwise K is a plain load into registers.
+      // MI355X that lifts long streams of reads from ~6.4 to ~7 TB/s; with
+      // two row groups per head, whose second read of each tile must hit in
+      // cache, they are plain loads. bf16 K goes to ring slot sl in LDS as
+      // whole head rows (each load instruction reads TPI complete 256-byte
+      // rows: about 7.1 TB/s for the K and V stream, against 6.7 TB/s when
+      // every instruction reads a 64-byte piece of sixteen rows, the operand
+      // layout in registers); fp32 K is a plain load into registers.
       // A load past the last tile (`tail`) re-loads the last tile and is never
       // used; its V part then reads the same rows of the K cache, lines the
       // tile's K loads just brought in, instead of missing again on V (whose
@@ -647,27 +577,6 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         const char* vb = (const char*)(tail ? p.k_cache : p.v_cache) + base;
         const uint32_t in_blk = (uint32_t)(tt & (bs - 1)) * row_bytes;
         bf.bid = active ? bid : 0;
-        if constexpr (SH) {
-          // this wave's half of the tile, K rows (row group 0) or V rows (1),
-          // into the K or V part of the pair's ring slot sl
-          f32x4* slot = &s_pool[(stream * DL + sl) * 2 * KSLOT + (rh ? KSLOT : 0)];
-          asm volatile("" ::: "memory");  // after the slot's last operand reads
-          if (rh == 0) {
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-              __builtin_amdgcn_global_load_lds(
-                  (const void*)(kb + in_blk + k_dma_off[i]),
-                  (__attribute__((address_space(3))) void*)(slot + i * 64), 16, 0, 0);
-          } else {
-            // V with the nontemporal hint, as in registers
-#pragma unroll
-            for (int i = 0; i < NI; ++i)
-              __builtin_amdgcn_global_load_lds(
-                  (const void*)(vb + in_blk + v_dma_off[i]),
-                  (__attribute__((address_space(3))) void*)(slot + i * 64), 16, 0, 2);
-          }
-          return;
-        } else {
         if constexpr (KL) {
           f32x4* slot = &s_pool[(wave * DEPTH + sl) * KSLOT];
           asm volatile("" ::: "memory");  // after the slot's last operand reads
@@ -685,20 +594,21 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         for (int i = 0; i < 4; ++i) {
           const char* src = vb + in_blk + v_lane_off + i * row_bytes;
           if constexpr (NVW == 2) {
-            const u32x2 x = __builtin_nontemporal_load((const u32x2*)src);
+            const u32x2 x = RH == 1 ? __builtin_nontemporal_load((const u32x2*)src)
+                                    : *(const u32x2*)src;
             bf.v[i][0] = x[0];
             bf.v[i][1] = x[1];
           } else {
 #pragma unroll
             for (int w = 0; w < NVW; w += 4) {
-              const u32x4 x = __builtin_nontemporal_load((const u32x4*)(src + w * 4));
+              const u32x4 x = RH == 1 ? __builtin_nontemporal_load((const u32x4*)(src + w * 4))
+                                      : *(const u32x4*)(src + w * 4);
               bf.v[i][w] = x[0];
               bf.v[i][w + 1] = x[1];
               bf.v[i][w + 2] = x[2];
               bf.v[i][w + 3] = x[3];
             }
           }
-        }
         }
       };
       // This wave's tiles of the piece: those whose absolute tile index is ws
@@ -712,45 +622,6 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
       auto tile_at = [&](int u) {
         return t_begin + (nw > 0 ? t_first + min(u, nw - 1) * WS : 0) * kTile;
       };
-      if constexpr (SH) {
-        // Two row groups: the pair's ring of DL slots in LDS. Step t reads
-        // slot t mod DL and first issues this wave's half of tile t + DL - 1
-        // into the slot read at step t - 1, so DL - 1 tiles are on their way
-        // while one is used.
-        TileBuf idle;  // load() only records the block id here
-#pragma unroll
-        for (int u = 0; u < DL - 1; ++u) load(tile_at(u), idle, u, u >= nw);
-        if (pb == blk_first) after_first_prologue();
-        int sl = 0;
-        for (int t = 0; t < steps; ++t) {
-          // This wave's half of tile t has landed once at most the halves
-          // issued after it are outstanding; the barrier then has the
-          // partner's half landed too, and every wave done with the slot
-          // loaded next (its reads wait for their data before the wave goes
-          // on). Passed by every wave at every step, with a tile or not. A
-          // bare s_barrier: __syncthreads() would also wait for every load
-          // in flight, the next tiles' included. (The empty asm statements
-          // keep the compiler from moving memory accesses across the wait
-          // and the barrier.)
-          asm volatile("" ::: "memory");
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm((DL - 2) * NI));
-          asm volatile("" ::: "memory");
-          __builtin_amdgcn_s_barrier();
-          asm volatile("" ::: "memory");
-          load(tile_at(t + DL - 1), idle, sl == 0 ? DL - 1 : sl - 1, t + DL - 1 >= nw);
-          if (t < nw) {
-            const int tt = tile_at(t);
-            const int bid = uniform(s_blk[((tt - off) >> bs_shift) - pb]);
-            TileBuf tb;
-            tb.bid = bid > 0 && (int64_t)bid < p.total_blocks ? bid : 0;
-            const int base = (stream * DL + sl) * 2 * KSLOT;
-            read_k_slot(tb.k, base);
-            read_v_slot(tb, base + KSLOT);
-            fn(tt, tb);
-          }
-          sl = sl == DL - 1 ? 0 : sl + 1;
-        }
-      } else {
       RingBuf bufs[DEPTH];
 #pragma unroll
       for (int s = 0; s < DEPTH - 1; ++s) load(tile_at(s), bufs[s], s, s >= nw);
@@ -785,7 +656,6 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
             fn(t_begin + (t_first + (t + s) * WS) * kTile, bufs[s]);
           }
         }
-      }
       }
     }
   };
@@ -1017,8 +887,8 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
         // the walk's last halves, which share its LDS)
         // (K through LDS: every wave's last loads into its ring, which the
         // pool overlays, have landed)
-        if (LR && c == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0);
-        if (c > 0 || LR) __syncthreads();
+        if (KL && c == 0) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        if (c > 0 || KL) __syncthreads();
         const int at = grp * WS + ws;
         s_pm[at * 64 + lane] = m_run[c];
         s_pl[at * 64 + lane] = l_run[c];
@@ -1147,7 +1017,7 @@ paged_decode_kernel(const DecodeParams p, int bs_shift) {
     if (p.flags & kFlagSink) p.out[0] = __uint_as_float(sink);
   }
   // no load into this workgroup's LDS outlives it
-  if constexpr (LR) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  if constexpr (KL) __builtin_amdgcn_s_waitcnt(kVmcnt0);
 }
 
 // Workgroups of a kernel the device holds at once (compute units times
