@@ -12,6 +12,9 @@
 // three arrays are 16-byte aligned (one 16-byte load of request indices, two
 // of positions and two 16-byte stores: a step's tokens come in runs of one
 // request, so most of a launch's bytes are these streams, not the table).
+// The streams are touched once, so they are read and written with the
+// nontemporal hint; the table reads, which neighbouring tokens share, are
+// plain loads.
 // The vLLM kernel runs one program per request; a flat grid over tokens keeps
 // every lane busy whatever the length mix.
 #include "kvslot_internal.h"
@@ -49,9 +52,9 @@ slot_mapping_x4_kernel(const int32_t* __restrict__ req_indices,
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += stride) {
     const int64_t t = 4 * q;
     if (t + 4 <= num_tokens) {
-      const i32x4 r = *(const i32x4*)(req_indices + t);
-      const i64x2 p01 = *(const i64x2*)(positions + t);
-      const i64x2 p23 = *(const i64x2*)(positions + t + 2);
+      const i32x4 r = __builtin_nontemporal_load((const i32x4*)(req_indices + t));
+      const i64x2 p01 = __builtin_nontemporal_load((const i64x2*)(positions + t));
+      const i64x2 p23 = __builtin_nontemporal_load((const i64x2*)(positions + t + 2));
       const i64x2 s01 = {token_slot(r[0], p01[0], block_table, table_rows, table_stride,
                                     block_size, block_shift),
                          token_slot(r[1], p01[1], block_table, table_rows, table_stride,
@@ -60,8 +63,8 @@ slot_mapping_x4_kernel(const int32_t* __restrict__ req_indices,
                                     block_size, block_shift),
                          token_slot(r[3], p23[1], block_table, table_rows, table_stride,
                                     block_size, block_shift)};
-      *(i64x2*)(slot_mapping + t) = s01;
-      *(i64x2*)(slot_mapping + t + 2) = s23;
+      __builtin_nontemporal_store(s01, (i64x2*)(slot_mapping + t));
+      __builtin_nontemporal_store(s23, (i64x2*)(slot_mapping + t + 2));
     } else {
       // the quad holding the step's last tokens, or only padding
       for (int64_t u = t; u < t + 4 && u < max_num_tokens; ++u)
