@@ -6,7 +6,10 @@ one by one, the distinct (request, block) pairs they fall in are counted, and
 the bytes are summed from the arrays' own sizes. CPU only.
 """
 
+import glob
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -104,3 +107,23 @@ def test_step_write_bytes():
     assert bench.cache_write_bytes(w, live, T) == live * 4 * row + 8 * T
     assert bench.slot_map_bytes(T) == 24 * T
     assert math.isclose(bench.slot_map_bytes(1 << 22) / (1 << 22), 24.0)
+
+
+def test_committed_counter_traffic_is_for_these_kernels():
+    """Every committed pass-1 counter summary was taken with the decode kernels
+    as they are (the hash of their code), so the bench line's traffic for the
+    256-request step resolves instead of being dropped as stale; and there the
+    DRAM bytes are within a few percent of the algorithmic bytes of the call."""
+    paths = sorted(glob.glob(os.path.join(bench.ROOT, "profiles",
+                                          "paged_decode_attention_*_traffic.json")))
+    assert paths
+    for path in paths:
+        with open(path) as f:
+            d = json.load(f)
+        assert d["kernel_source_sha256_16"] == bench.kernel_source_hash(), path
+    t = bench.measured_traffic("large_batch_block_split", "context")
+    assert t is not None
+    with open(os.path.join(bench.ROOT, "profiles",
+                           "paged_decode_attention_large_batch_block_split_context_traffic.json")) as f:
+        d = json.load(f)
+    assert 1.0 <= t / d["algorithmic_bytes_of_the_call"] <= 1.05
