@@ -904,9 +904,10 @@ def test_fused_step_vs_oracle(cuda, index):
 
 def test_grid_stride_at_scale(cuda):
     """Work past one launch's 65536 x 256 threads, so every thread of the
-    slot-map, cache-write and fused kernels takes a second grid stride:
-    2^24 + 1000 slots, and 1.1M tokens x 16 pieces of 16 bytes written,
-    against the oracle, bit-exact."""
+    cache-write and fused kernels takes a second grid stride (1.1M tokens x
+    16 pieces of 16 bytes written), and a slot map of 2^24 + 1000 slots,
+    against the oracle, bit-exact. (The slot map's four-token kernel covers
+    2^26 tokens in one stride: the next test takes it past that.)"""
     rng = np.random.default_rng(11)
     # slot map over 2^24 + 500 tokens (+500 tail): pads, rows and columns past the table
     rows, width, bs = 4096, 64, 64
@@ -952,6 +953,39 @@ def test_grid_stride_at_scale(cuda):
         assert np.array_equal(host_bits(gv), vc.view(np.uint32)), f"fused={fused}"
         del gk, gv
 
+
+
+def test_slot_map_grid_stride_four_tokens_and_context_parallel(cuda):
+    """The other slot-map kernels past their first grid stride, bit-exact
+    against the oracle. With 16-byte aligned arrays kv_slot_mapping takes four
+    tokens per thread, so one launch of 65536 x 256 threads covers 2^26
+    tokens: 2^26 + 500 tokens and a 500-slot tail reach the second stride.
+    The context-parallel slot map takes one token per thread: 2^24 + 500
+    tokens and a 300-slot tail, on two ranks' views."""
+    rng = np.random.default_rng(12)
+    rows, width, bs = 4096, 64, 64
+    table = rng.permutation(np.arange(1, rows * width + 1)).reshape(rows, width).astype(np.int32)
+    d_bt = torch.from_numpy(table).to(cuda)
+    T = (1 << 26) + 500
+    req = rng.integers(-1, rows + 1, T).astype(np.int32)
+    pos = rng.integers(0, width * bs + 64, T).astype(np.int64)
+    d_req, d_pos = torch.from_numpy(req).to(cuda), torch.from_numpy(pos).to(cuda)
+    assert d_req.data_ptr() % 16 == 0 and d_pos.data_ptr() % 16 == 0  # the four-token kernel
+    got = K.kv_slot_mapping(d_req, d_pos, d_bt, bs, max_num_tokens=T + 500)
+    assert got.data_ptr() % 16 == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), O.compute_slot_mapping(req, pos, table, bs, T + 500))
+    del got
+
+    T2 = (1 << 24) + 500
+    for world, rank, interleave in ((4, 1, 1), (2, 0, 16)):
+        got = K.kv_slot_mapping_dcp(d_req[:T2], d_pos[:T2], d_bt, bs, world, rank, interleave,
+                                    max_num_tokens=T2 + 300)
+        torch.cuda.synchronize()
+        want = O.compute_slot_mapping_dcp(req[:T2], pos[:T2], table, bs, world, rank, interleave,
+                                          T2 + 300)
+        assert np.array_equal(got.cpu().numpy(), want), (world, rank, interleave)
+        del got
 
 def test_step_replays_from_a_hip_graph(cuda):
     """The bench step (fused slot map + write, then attention), its buffers
