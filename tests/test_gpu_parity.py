@@ -955,13 +955,15 @@ def test_grid_stride_at_scale(cuda):
 
 
 
-def test_slot_map_grid_stride_four_tokens_and_context_parallel(cuda):
+def test_slot_map_kernels_past_one_grid_stride(cuda):
     """The other slot-map kernels past their first grid stride, bit-exact
     against the oracle. With 16-byte aligned arrays kv_slot_mapping takes four
     tokens per thread, so one launch of 65536 x 256 threads covers 2^26
     tokens: 2^26 + 500 tokens and a 500-slot tail reach the second stride.
     The context-parallel slot map takes one token per thread: 2^24 + 500
-    tokens and a 300-slot tail, on two ranks' views."""
+    tokens and a 300-slot tail, on two ranks' views; and kv_slot_mapping's
+    one-token kernel (arrays not 16-byte aligned: views one element in) over
+    2^24 + 500 tokens."""
     rng = np.random.default_rng(12)
     rows, width, bs = 4096, 64, 64
     table = rng.permutation(np.arange(1, rows * width + 1)).reshape(rows, width).astype(np.int32)
@@ -986,6 +988,13 @@ def test_slot_map_grid_stride_four_tokens_and_context_parallel(cuda):
                                           T2 + 300)
         assert np.array_equal(got.cpu().numpy(), want), (world, rank, interleave)
         del got
+
+    v_req, v_pos = d_req[1:T2 + 1], d_pos[1:T2 + 1]
+    assert v_req.data_ptr() % 16 != 0 and v_pos.data_ptr() % 16 != 0  # the one-token kernel
+    got = K.kv_slot_mapping(v_req, v_pos, d_bt, bs, max_num_tokens=T2 + 200)
+    torch.cuda.synchronize()
+    want = O.compute_slot_mapping(req[1:T2 + 1], pos[1:T2 + 1], table, bs, T2 + 200)
+    assert np.array_equal(got.cpu().numpy(), want)
 
 def test_step_replays_from_a_hip_graph(cuda):
     """The bench step (fused slot map + write, then attention), its buffers
