@@ -375,6 +375,36 @@ def test_random_batches_vs_oracle(cuda, seed):
     assert err <= TOL[dtype], (err, dtype, d, bs, hkv, g, sq, len(lens), walk, table_walk)
 
 
+
+@pytest.mark.parametrize("seed", range(32))
+def test_long_random_batches_vs_oracle(cuda, seed):
+    """Seeded random batches with long requests (4096 to 20000 tokens at block
+    sizes 16 and 32), so that segments cross the 256-block pieces their table
+    entries are staged in, under the tile split and every head count; with
+    inactive entries, head trims and the fixed-shape walk, against the oracle."""
+    rng = np.random.default_rng(70_000 + seed)
+    dtype = ["f32", "bf16"][rng.integers(2)] if rng.random() < 0.3 else "bf16"
+    d = [64, 128][rng.integers(2)]
+    bs = [16, 32][rng.integers(2)]
+    hkv = [1, 2, 4, 8][rng.integers(4)]
+    sq = int(rng.integers(1, 5))
+    g = int(rng.choice([x for x in (1, 2, 4, 8, 16) if x * sq <= 64]))
+    nb = int(rng.integers(1, 7))
+    lens = [int(x) for x in np.where(rng.random(nb) < 0.5, rng.integers(4096, 20000, nb),
+                                     rng.integers(sq, 3000, nb))]
+    c = small_case(cuda, seed, lens, bs, hkv, g, sq, d, dtype)
+    for _ in range(int(rng.integers(0, 3))):
+        r = int(rng.integers(len(lens)))
+        c["table"][r, int(rng.integers(-(-lens[r] // bs)))] = -1
+    c["d_bt"] = torch.from_numpy(c["table"]).to(cuda)
+    width = c["table"].shape[1]
+    walk = max(1, -(-max(lens) // bs) - int(rng.integers(0, 2))) if rng.random() < 0.3 else width
+    table_walk = bool(rng.random() < 0.3)
+    out = gpu_attn(c, walk_blocks=walk, flags=K.KVS_WALK_TABLE if table_walk else 0)
+    torch.cuda.synchronize()
+    err = max_err(out, ref_attn(c, walk=walk))
+    assert err <= TOL[dtype], (err, dtype, d, bs, hkv, g, sq, lens, walk, table_walk)
+
 def test_invariants_bitwise(cuda):
     c = small_case(cuda, 3, [1, 50, 64, 700, 3000], 64, 8, 4, 2, 128, "bf16", width=64)
     base = gpu_attn(c)
