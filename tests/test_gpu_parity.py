@@ -606,6 +606,34 @@ def test_swa_random_vs_oracle(cuda, seed):
     assert err <= TOL[dtype], (dtype, d, bs, hkv, g, sq, window, lens[:8], err)
 
 
+
+@pytest.mark.parametrize("seed", range(16))
+def test_long_swa_random_vs_oracle(cuda, seed):
+    """Seeded sliding-window batches with long requests (4096 to 20000 tokens
+    at block sizes 16 and 32) and windows up to 12000 positions, so that the
+    tail-trimmed walk crosses staging pieces, against the oracle over the
+    whole table."""
+    rng = np.random.default_rng(80_000 + seed)
+    dtype = "bf16" if rng.random() < 0.7 else "f32"
+    d = [64, 128][rng.integers(2)]
+    bs = [16, 32][rng.integers(2)]
+    hkv = [1, 2, 4, 8][rng.integers(4)]
+    sq = int(rng.integers(1, 5))
+    g = int(rng.choice([x for x in (1, 2, 4, 8, 16) if x * sq <= 64]))
+    nb = int(rng.integers(1, 7))
+    lens = [int(x) for x in np.where(rng.random(nb) < 0.5, rng.integers(4096, 20000, nb),
+                                     rng.integers(sq, 3000, nb))]
+    window = int(rng.choice([1, int(rng.integers(2, 600)), int(rng.integers(600, 5000)),
+                             int(rng.integers(5000, 12000)), max(lens) + 100]))
+    c = swa_case(cuda, (dtype, d, bs, hkv, g, sq, window, lens), seed=seed)
+    w = c["w"]
+    out = swa_gpu(c)
+    torch.cuda.synchronize()
+    want = O.paged_decode_attention(c["q"], c["kc"], c["vc"], c["table"], w.seq_lens,
+                                    c["table"].shape[1], w.scale, w.dtype, window=window)
+    err = max_err(out, want)
+    assert err <= TOL[dtype], (dtype, d, bs, hkv, g, sq, window, lens, err)
+
 def test_swa_trimmed_equals_whole_table_bitwise(cuda):
     c = swa_case(cuda, SWA_SHAPES[4])
     trimmed = swa_gpu(c)
