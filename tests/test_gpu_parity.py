@@ -749,6 +749,9 @@ def dcp_gpu_case(cuda, seed, lens, bs, world, interleave, hkv, g, sq, d, dtype):
     (8, 16, 16, "bf16", 1, 8, [7, 128, 2049, 6000]),
     (2, 16, 64, "bf16", 4, 8, [4, 20, 129, 1500, 5000]),  # 32 rows per KV head
     (4, 8, 64, "bf16", 4, 16, [4, 100, 3000]),            # 64 rows: traded tile halves
+    # a rank's local walk past one 256-block staging piece
+    (2, 1, 16, "bf16", 1, 4, [9000, 20000]),
+    (4, 16, 16, "bf16", 2, 4, [100, 33000]),
 ])
 def test_dcp_ranks_and_merge_vs_oracle(cuda, world, interleave, bs, dtype, sq, g, lens):
     hkv, d = 2, 128
